@@ -1,0 +1,342 @@
+"""Benchmark of the FP8 block-scaled hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|decode|backward|moe]
+                    [--no-cpu-baseline]
+
+A step is one pass of the hot path over one batch of synthetic input, inputs resident in
+HBM. The default workload is the dense layer shaped like a ~9B model's MLP
+(X 8192x4096 with 0.1% outlier channels x50, fused gate/up W 24576x4096, down
+W 4096x12288, down input 8192x12288):
+    quantize X 1x128 row-wise + 128x1 column-wise (the copy WGrad consumes),
+    quantize W_gu and W_dn per 128x128 block (re-quantized each optimizer step),
+    Y_gu = X . W_gu^T (FP8 MFMA, fp32 accumulation, bf16 out),
+    quantize the down input 1x128, Y_dn = X2 . W_dn^T.
+`value` = GEMM FLOPs of the step / step time (TFLOP/s, whole step including the
+quantizers). `roofline` reports the dominant kernel (the gate/up GEMM) from HIP events
+recorded on the stream the library launches on, against the 5.0 PFLOP/s dense FP8 MFMA
+peak; `quant_roofline` the X quantizer against 8 TB/s HBM.
+
+Other workloads (--workload) time the decode, backward and MoE paths the same way.
+Prints ONE JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s (% of FP8 MFMA peak); quantizer GB/s (% of HBM)"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense", choices=["dense", "decode", "backward", "moe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class EventTimer:
+    """Pairs of HIP events recorded on the current stream around one kernel's launches."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        ts = [a.elapsed_time(b) for a, b in self.pairs]
+        return float(np.mean(ts)) if ts else float("nan")
+
+
+# ---------------------------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------------------------
+
+def dense_setup(torch, F, W, dev):
+    d = W.dense_forward(with_down=True)
+    t = {k: W.to_bf16_tensor(v).to(dev) for k, v in d.items()}
+    M, K = t["x"].shape
+    N = t["w_gu"].shape[0]
+    N2, K2 = t["w_dn"].shape
+    u8, f32 = torch.uint8, torch.float32
+    b = dict(
+        xq=torch.empty((M, K), dtype=u8, device=dev), sx=torch.empty((M, K // 128), dtype=f32, device=dev),
+        xqt=torch.empty((K, M), dtype=u8, device=dev), sxt=torch.empty((K, M // 128), dtype=f32, device=dev),
+        wq_gu=torch.empty((N, K), dtype=u8, device=dev), sw_gu=torch.empty((N // 128, K // 128), dtype=f32, device=dev),
+        wq_dn=torch.empty((N2, K2), dtype=u8, device=dev),
+        sw_dn=torch.empty((N2 // 128, K2 // 128), dtype=f32, device=dev),
+        x2q=torch.empty((M, K2), dtype=u8, device=dev), sx2=torch.empty((M, K2 // 128), dtype=f32, device=dev),
+        y_gu=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        y_dn=torch.empty((M, N2), dtype=torch.bfloat16, device=dev),
+    )
+    timers = {k: EventTimer(torch) for k in ("quant_x", "quant_w", "gemm_gu", "quant_x2", "gemm_dn")}
+
+    def step(timed):
+        tm = timers if timed else None
+        if tm: tm["quant_x"].start()
+        F.fp8_quant_act_1x128(t["x"], q=b["xq"], s=b["sx"], qt=b["xqt"], st=b["sxt"], rowwise=True, colwise=True)
+        if tm: tm["quant_x"].stop(); tm["quant_w"].start()
+        F.fp8_quant_w_128x128(t["w_gu"], q=b["wq_gu"], s=b["sw_gu"])
+        F.fp8_quant_w_128x128(t["w_dn"], q=b["wq_dn"], s=b["sw_dn"])
+        if tm: tm["quant_w"].stop(); tm["gemm_gu"].start()
+        F.fp8_gemm_blockscaled_fwd(b["xq"], b["sx"], b["wq_gu"], b["sw_gu"], y=b["y_gu"])
+        if tm: tm["gemm_gu"].stop(); tm["quant_x2"].start()
+        F.fp8_quant_act_1x128(t["x2"], q=b["x2q"], s=b["sx2"])
+        if tm: tm["quant_x2"].stop(); tm["gemm_dn"].start()
+        F.fp8_gemm_blockscaled_fwd(b["x2q"], b["sx2"], b["wq_dn"], b["sw_dn"], y=b["y_dn"])
+        if tm: tm["gemm_dn"].stop()
+
+    flops_gu = 2.0 * M * N * K
+    flops_dn = 2.0 * M * N2 * K2
+    info = dict(
+        config={"workload": "dense_layer_forward_9b", "tokens_M": M, "hidden_K": K, "gate_up_N": N,
+                "down_N": N2, "down_K": K2, "recipe": "blockwise 1x128 act / 128x128 weight, E4M3, fp32 scales",
+                "out": "bf16"},
+        flops=flops_gu + flops_dn,
+        dominant=("gemm_gu", "mfma", flops_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
+                  f"2*M*N*K = {flops_gu:.4g} FLOP per launch"),
+        # quant X: 2 B read + 1 B row + 1 B column payload + 4 B per 128 per direction
+        quant=("quant_x", (M * K * (2 + 1 + 1) + 2 * M * K // 128 * 4) / 1e9,
+               "bf16 read 2 B + row and column E4M3 payloads 1 B each + fp32 scales per element"),
+        gemm_keys=("gemm_gu", "gemm_dn"),
+    )
+    return step, timers, info
+
+
+def decode_setup(torch, F, W, dev):
+    d = W.decode_rollout()
+    x = W.to_bf16_tensor(d["x"]).to(dev)
+    M, K = x.shape
+    mats = {}
+    for n in W.DECODE_N:
+        wq, sw, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d[f"w{n}"]).to(dev))
+        # installed (rollout-owned) copies
+        iq, is_ = torch.empty_like(wq), torch.empty_like(sw)
+        F.fp8_weight_install(wq, sw, iq, is_)
+        mats[n] = (iq, is_, torch.empty((M, n), dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(F.fp8rl_fwd_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    timers = {f"decode_n{n}": EventTimer(torch) for n in W.DECODE_N}
+
+    def step(timed):
+        for n, (iq, is_, y) in mats.items():
+            if timed: timers[f"decode_n{n}"].start()
+            F.fp8_gemm_blockscaled_fwd(wq=iq, sw=is_, x_bf16=x, y=y, workspace=ws)
+            if timed: timers[f"decode_n{n}"].stop()
+
+    nmax = max(W.DECODE_N)
+    info = dict(
+        config={"workload": "decode_rollout", "rows_M": M, "K": K, "N": list(W.DECODE_N),
+                "activations": "bf16, quantized 1x128 inside the call", "weights": "installed E4M3 128x128"},
+        flops=sum(2.0 * M * n * K for n in W.DECODE_N),
+        dominant=(f"decode_n{nmax}", "hbm", (nmax * K + nmax * K // 128 // 128 * 4) / 1e9, "GB/s", PEAK_HBM_GBS,
+                  "weight stream: E4M3 payload + fp32 block scales per launch"),
+        quant=None,
+        gemm_keys=tuple(timers),
+    )
+    return step, timers, info
+
+
+def backward_setup(torch, F, W, dev):
+    d = W.dense_forward(with_down=False)
+    dy = W.to_bf16_tensor(W.dense_backward()["dy"]).to(dev)
+    x = W.to_bf16_tensor(d["x"]).to(dev)
+    w = W.to_bf16_tensor(d["w_gu"]).to(dev)
+    M, K = x.shape
+    N = w.shape[0]
+    _, _, xqt, sxt = F.fp8_quant_act_1x128(x, rowwise=False, colwise=True)      # saved from the forward
+    wq, sw, wqt = F.fp8_quant_w_128x128(w, transpose=True)
+    u8, f32 = torch.uint8, torch.float32
+    b = dict(dyq=torch.empty((M, N), dtype=u8, device=dev), sdy=torch.empty((M, N // 128), dtype=f32, device=dev),
+             dyqt=torch.empty((N, M), dtype=u8, device=dev), sdyt=torch.empty((N, M // 128), dtype=f32, device=dev),
+             dx=torch.empty((M, K), dtype=torch.bfloat16, device=dev), dw=torch.empty((N, K), dtype=f32, device=dev))
+    timers = {k: EventTimer(torch) for k in ("quant_dy", "dgrad", "wgrad")}
+
+    def step(timed):
+        if timed: timers["quant_dy"].start()
+        F.fp8_quant_act_1x128(dy, q=b["dyq"], s=b["sdy"], qt=b["dyqt"], st=b["sdyt"], rowwise=True, colwise=True)
+        if timed: timers["quant_dy"].stop(); timers["dgrad"].start()
+        F.fp8_gemm_blockscaled_dgrad(b["dyq"], b["sdy"], wqt, sw, dx=b["dx"])
+        if timed: timers["dgrad"].stop(); timers["wgrad"].start()
+        F.fp8_gemm_blockscaled_wgrad(b["dyqt"], b["sdyt"], xqt, sxt, dw=b["dw"])
+        if timed: timers["wgrad"].stop()
+
+    fl = 2.0 * M * N * K
+    info = dict(
+        config={"workload": "dense_layer_backward_gate_up", "tokens_M": M, "N": N, "K": K,
+                "dgrad_out": "bf16", "wgrad_out": "fp32"},
+        flops=2 * fl,
+        dominant=("dgrad", "mfma", fl / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS, f"2*M*N*K = {fl:.4g} FLOP per launch"),
+        quant=("quant_dy", (M * N * 4 + 2 * M * N // 128 * 4) / 1e9,
+               "bf16 read 2 B + row and column E4M3 payloads + fp32 scales per element"),
+        gemm_keys=("dgrad", "wgrad"),
+    )
+    return step, timers, info
+
+
+def moe_setup(torch, F, W, dev):
+    d = W.moe_mxfp8()
+    xp = W.to_bf16_tensor(d["x_perm"]).to(dev)
+    h = W.to_bf16_tensor(d["h"]).to(dev)
+    wq_gu, sw_gu = F.mxfp8_quant_1x32(W.to_bf16_tensor(d["w_gu"]).to(dev))
+    wq_dn, sw_dn = F.mxfp8_quant_1x32(W.to_bf16_tensor(d["w_dn"]).to(dev))
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    T, K = xp.shape
+    E, N, _ = wq_gu.shape
+    _, N2, K2 = wq_dn.shape
+    u8 = torch.uint8
+    b = dict(xq=torch.empty((T, K), dtype=u8, device=dev), sx=torch.empty((T, K // 32), dtype=u8, device=dev),
+             hq=torch.empty((T, K2), dtype=u8, device=dev), sh=torch.empty((T, K2 // 32), dtype=u8, device=dev),
+             y_gu=torch.empty((T, N), dtype=torch.bfloat16, device=dev),
+             y_dn=torch.empty((T, N2), dtype=torch.bfloat16, device=dev))
+    timers = {k: EventTimer(torch) for k in ("quant_x", "grouped_gu", "quant_h", "grouped_dn")}
+
+    def step(timed):
+        if timed: timers["quant_x"].start()
+        F.mxfp8_quant_1x32(xp, q=b["xq"], e8m0=b["sx"])
+        if timed: timers["quant_x"].stop(); timers["grouped_gu"].start()
+        F.fp8_grouped_gemm(b["xq"], b["sx"], wq_gu, sw_gu, off, y=b["y_gu"])
+        if timed: timers["grouped_gu"].stop(); timers["quant_h"].start()
+        F.mxfp8_quant_1x32(h, q=b["hq"], e8m0=b["sh"])
+        if timed: timers["quant_h"].stop(); timers["grouped_dn"].start()
+        F.fp8_grouped_gemm(b["hq"], b["sh"], wq_dn, sw_dn, off, y=b["y_dn"])
+        if timed: timers["grouped_dn"].stop()
+
+    fl_gu, fl_dn = 2.0 * T * N * K, 2.0 * T * N2 * K2
+    info = dict(
+        config={"workload": "moe_mxfp8_grouped", "routed_rows_T": T, "experts": E, "gate_up": [N, K],
+                "down": [N2, K2], "routing": "Zipf(1.1) top-8"},
+        flops=fl_gu + fl_dn,
+        dominant=("grouped_gu", "mfma", fl_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
+                  f"2*T*N*K = {fl_gu:.4g} FLOP per launch"),
+        quant=("quant_x", T * K * (2 + 1 + 1 / 32) / 1e9, "bf16 read 2 B + E4M3 1 B + E8M0 1/32 B per element"),
+        gemm_keys=("grouped_gu", "grouped_dn"),
+    )
+    return step, timers, info
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample of the same workload
+# ---------------------------------------------------------------------------------------------
+
+def cpu_baseline(workload: str):
+    import workloads as W
+    from oracle import gemm as OG
+    from oracle import quantize as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    if workload in ("dense", "backward", "decode"):
+        # 256 token rows x 2048 output features of the gate/up projection, K = 4096: the
+        # oracle quantizes both operands and forms the fp64 dequantized product.
+        m, n, k = 256, 2048, 4096
+        x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        w = W.bf16_round(rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02))
+        t0 = time.perf_counter()
+        xq, sx = OQ.quant_act_1x128(x)
+        wq, sw = OQ.quant_w_128x128(w)
+        OG.gemm_fwd(xq, sx, wq, sw)
+        dt = time.perf_counter() - t0
+        sample = f"oracle quant 1x128 + 128x128 and fp64 dequantized GEMM on {m}x{n}x{k} of the gate/up layer"
+    else:
+        m, n, k = 512, 1024, 2048
+        x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        w = W.bf16_round(rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02))
+        t0 = time.perf_counter()
+        xq, ex = OQ.quant_mx_1x32(x)
+        wq, ew = OQ.quant_mx_1x32(w)
+        OG.grouped_gemm_mx(xq, ex, wq[None], ew[None], np.array([0, m], np.int64))
+        dt = time.perf_counter() - t0
+        sample = f"oracle MXFP8 quant + fp64 dequantized GEMM on {m}x{n}x{k} (one expert)"
+    return {"value": 2.0 * m * n * k / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on a single MI355X).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fp8_block_scaled_quant_amd as F
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    F.load_library()
+    setup = {"dense": dense_setup, "decode": decode_setup, "backward": backward_setup, "moe": moe_setup}[a.workload]
+    step, timers, info = setup(torch, F, W, dev)
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / a.steps * 1e3
+
+    breakdown = {k: round(v.mean_ms() * 1e3, 2) for k, v in timers.items()}          # microseconds
+    name, bound, per_launch, unit, peak, per_unit = info["dominant"]
+    dom_ms = timers[name].mean_ms()
+    achieved = per_launch / (dom_ms * 1e-3)
+    gemm_ms = sum(timers[k].mean_ms() for k in info["gemm_keys"])
+    out = {
+        "metric": METRIC,
+        "value": round(info["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate",
+        "data": "synthetic",
+        "config": info["config"],
+        "roofline": {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "per_launch": per_unit},
+        "gemm_tflops": round(info["flops"] / (gemm_ms * 1e-3) / 1e12, 2),
+        "kernel_us": breakdown,
+    }
+    if info["quant"] is not None:
+        qname, qgb, qdesc = info["quant"]
+        qms = timers[qname].mean_ms()
+        out["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
+                                 "per_launch": qdesc}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a.workload)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,295 @@
+"""Python binding of libfp8rl (fine-grained FP8 quantization and block-scaled FP8 GEMMs
+for MI355X / gfx950).
+
+The functions here have the names of the C entry points in ``include/fp8rl.h`` and do
+argument marshalling only: they check devices, dtypes and shapes, allocate missing
+outputs with torch, and pass raw device pointers plus torch's current HIP stream to the
+library. Every step of the computation runs in the library's HIP kernels; there is no
+fallback path. Importing this package does not load the library; the first call does,
+and raises if ``libfp8rl.so`` has not been built
+(``python -m fp8_block_scaled_quant_amd.build``).
+
+Tensors: bf16 inputs as ``torch.bfloat16``; FP8 payloads and E8M0 scales as
+``torch.uint8`` (raw bytes); fp32 scales as ``torch.float32``. All on the GPU,
+contiguous.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Fp8rlError", "RECIPE_BLOCK128", "RECIPE_MXFP8", "OUT_BF16", "OUT_F32", "library_path", "load_library",
+    "fp8rl_abi_version", "fp8_quant_act_1x128", "fp8_quant_w_128x128", "mxfp8_quant_1x32",
+    "fp8_gemm_blockscaled_fwd", "fp8rl_fwd_workspace_bytes", "fp8_gemm_blockscaled_dgrad",
+    "fp8_gemm_blockscaled_wgrad", "fp8_grouped_gemm", "fp8_weight_install",
+]
+
+RECIPE_BLOCK128 = 0
+RECIPE_MXFP8 = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8rl.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("recipe", _int), ("rows", _i64), ("cols", _i64), ("q", _vp), ("s", _vp)]
+
+
+_SIGNATURES = {
+    "fp8rl_abi_version": ([], _int),
+    "fp8rl_status_str": ([_int], ctypes.c_char_p),
+    "fp8_quant_act_1x128": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
+    "fp8_quant_w_128x128": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
+    "mxfp8_quant_1x32": ([_vp, _i64, _i64, _vp, _vp, _vp], _int),
+    "fp8_gemm_blockscaled_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp], _int),
+    "fp8rl_fwd_workspace_bytes": ([_i64, _i64], _sz),
+    "fp8_gemm_blockscaled_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_gemm_blockscaled_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_grouped_gemm": ([_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_weight_install": ([ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), _vp], _int),
+}
+
+
+class Fp8rlError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = load_library().fp8rl_status_str(status).decode()
+        super().__init__(f"{call}: status {status} ({msg})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfp8rl.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m fp8_block_scaled_quant_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise Fp8rlError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(t, dtype, shape, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(t, dtype, shape, name)
+
+
+def fp8rl_abi_version() -> int:
+    return load_library().fp8rl_abi_version()
+
+
+def fp8_quant_act_1x128(x, q=None, s=None, qt=None, st=None, *, rowwise=True, colwise=False):
+    """1x128 (row-wise) and/or 128x1 (column-wise, transposed) activation quantization.
+
+    Returns (q [M][K] u8, s [M][K/128] f32, qt [K][M] u8, st [K][M/128] f32); outputs not
+    requested are None."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    dev = x.device
+    if rowwise:
+        q = _out(q, torch.uint8, (M, K), dev, "q")
+        s = _out(s, torch.float32, (M, K // 128), dev, "s")
+    else:
+        q = s = None
+    if colwise:
+        qt = _out(qt, torch.uint8, (K, M), dev, "qt")
+        st = _out(st, torch.float32, (K, M // 128), dev, "st")
+    else:
+        qt = st = None
+    _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(dev)),
+           "fp8_quant_act_1x128")
+    return q, s, qt, st
+
+
+def fp8_quant_w_128x128(w, q=None, s=None, qt=None, *, transpose=False):
+    """128x128-block weight quantization. Returns (q [N][K] u8, s [N/128][K/128] f32,
+    qt [K][N] u8 or None)."""
+    lib = load_library()
+    N, K = w.shape
+    _need(w, torch.bfloat16, (N, K), "w")
+    dev = w.device
+    q = _out(q, torch.uint8, (N, K), dev, "q")
+    s = _out(s, torch.float32, (N // 128, K // 128), dev, "s")
+    qt = _out(qt, torch.uint8, (K, N), dev, "qt") if transpose else None
+    _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, _ptr(q), _ptr(s), _ptr(qt), _stream(dev)), "fp8_quant_w_128x128")
+    return q, s, qt
+
+
+def mxfp8_quant_1x32(x, q=None, e8m0=None):
+    """MXFP8 quantization, one E8M0 scale per 1x32 group. x: [..., K] bf16 (leading dims
+    flattened into rows). Returns (q u8 same shape, e8m0 u8 [..., K/32])."""
+    lib = load_library()
+    K = x.shape[-1]
+    R = x.numel() // K if K else 0
+    _need(x, torch.bfloat16, tuple(x.shape), "x")
+    dev = x.device
+    q = _out(q, torch.uint8, tuple(x.shape), dev, "q")
+    e8m0 = _out(e8m0, torch.uint8, tuple(x.shape[:-1]) + (K // 32,), dev, "e8m0")
+    _check(lib.mxfp8_quant_1x32(_ptr(x), R, K, _ptr(q), _ptr(e8m0), _stream(dev)), "mxfp8_quant_1x32")
+    return q, e8m0
+
+
+def fp8rl_fwd_workspace_bytes(M: int, K: int) -> int:
+    return load_library().fp8rl_fwd_workspace_bytes(M, K)
+
+
+def _odt(out_dtype):
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    if out_dtype == torch.float32:
+        return OUT_F32
+    raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def fp8_gemm_blockscaled_fwd(xq=None, sx=None, wq=None, sw=None, *, x_bf16=None, out_dtype=torch.bfloat16, y=None,
+                             workspace=None):
+    """Y[M][N] = deq(X) deq(W)^T. X as (xq, sx) or, for the fused form, as x_bf16 (then a
+    workspace is allocated unless given)."""
+    lib = load_library()
+    N, K = wq.shape
+    _need(wq, torch.uint8, (N, K), "wq")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    dev = wq.device
+    if x_bf16 is not None:
+        M = x_bf16.shape[0]
+        _need(x_bf16, torch.bfloat16, (M, K), "x_bf16")
+        if xq is not None or sx is not None:
+            raise ValueError("give either (xq, sx) or x_bf16")
+        nbytes = lib.fp8rl_fwd_workspace_bytes(M, K)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        M = xq.shape[0]
+        _need(xq, torch.uint8, (M, K), "xq")
+        _need(sx, torch.float32, (M, K // 128), "sx")
+    y = _out(y, out_dtype, (M, N), dev, "y")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.fp8_gemm_blockscaled_fwd(_ptr(xq), _ptr(sx), _ptr(x_bf16), _ptr(wq), _ptr(sw), M, N, K, _ptr(y),
+                                        _odt(out_dtype), _ptr(workspace), ws_bytes, _stream(dev)),
+           "fp8_gemm_blockscaled_fwd")
+    return y
+
+
+def fp8_gemm_blockscaled_dgrad(dyq, sdy, wqt, sw, *, out_dtype=torch.bfloat16, dx=None):
+    """dX[M][K] = deq(dY) deq(W) with wqt = W's byte transpose [K][N], sw [N/128][K/128]."""
+    lib = load_library()
+    M, N = dyq.shape
+    K = wqt.shape[0]
+    _need(dyq, torch.uint8, (M, N), "dyq")
+    _need(sdy, torch.float32, (M, N // 128), "sdy")
+    _need(wqt, torch.uint8, (K, N), "wqt")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    dx = _out(dx, out_dtype, (M, K), dyq.device, "dx")
+    _check(lib.fp8_gemm_blockscaled_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wqt), _ptr(sw), M, N, K, _ptr(dx),
+                                          _odt(out_dtype), _stream(dyq.device)), "fp8_gemm_blockscaled_dgrad")
+    return dx
+
+
+def fp8_gemm_blockscaled_wgrad(dyqt, sdyt, xqt, sxt, *, dw=None, accumulate=False):
+    """dW[N][K] (fp32) = deq(dY)^T deq(X) from the column-wise copies dyqt [N][M], xqt [K][M]."""
+    lib = load_library()
+    N, M = dyqt.shape
+    K = xqt.shape[0]
+    _need(dyqt, torch.uint8, (N, M), "dyqt")
+    _need(sdyt, torch.float32, (N, M // 128), "sdyt")
+    _need(xqt, torch.uint8, (K, M), "xqt")
+    _need(sxt, torch.float32, (K, M // 128), "sxt")
+    if accumulate and dw is None:
+        raise ValueError("accumulate=True needs dw")
+    dw = _out(dw, torch.float32, (N, K), dyqt.device, "dw")
+    _check(lib.fp8_gemm_blockscaled_wgrad(_ptr(dyqt), _ptr(sdyt), _ptr(xqt), _ptr(sxt), M, N, K, _ptr(dw),
+                                          1 if accumulate else 0, _stream(dyqt.device)), "fp8_gemm_blockscaled_wgrad")
+    return dw
+
+
+def fp8_grouped_gemm(xq, sx, wq, sw, offsets, *, recipe=RECIPE_MXFP8, out_dtype=torch.bfloat16, y=None):
+    """MXFP8 grouped GEMM: xq [T][K] u8, sx [T][K/32] u8, wq [E][N][K] u8, sw [E][N][K/32] u8,
+    offsets int32 [E+1] on the GPU. Returns y [T][N]."""
+    lib = load_library()
+    T, K = xq.shape
+    E, N, _ = wq.shape
+    _need(xq, torch.uint8, (T, K), "xq")
+    _need(sx, torch.uint8, (T, K // 32), "sx")
+    _need(wq, torch.uint8, (E, N, K), "wq")
+    _need(sw, torch.uint8, (E, N, K // 32), "sw")
+    _need(offsets, torch.int32, (E + 1,), "offsets")
+    y = _out(y, out_dtype, (T, N), xq.device, "y")
+    _check(lib.fp8_grouped_gemm(recipe, _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(offsets), T, E, N, K, _ptr(y),
+                                _odt(out_dtype), _stream(xq.device)), "fp8_grouped_gemm")
+    return y
+
+
+def fp8_weight_install(src_q, src_s, dst_q, dst_s, *, recipe=RECIPE_BLOCK128):
+    """Copy a quantized weight's payload and scales verbatim into the destination buffers."""
+    lib = load_library()
+    rows = src_q.shape[0] if src_q.dim() == 2 else src_q.numel() // src_q.shape[-1]
+    cols = src_q.shape[-1]
+    drows = dst_q.shape[0] if dst_q.dim() == 2 else dst_q.numel() // dst_q.shape[-1]
+    for t, name in ((src_q, "src_q"), (src_s, "src_s"), (dst_q, "dst_q"), (dst_s, "dst_s")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    for qt_, st_, r_, name in ((src_q, src_s, rows, "src"), (dst_q, dst_s, drows, "dst")):
+        if qt_.dtype != torch.uint8:
+            raise ValueError(f"{name}_q must be uint8")
+        if recipe == RECIPE_BLOCK128:
+            need = (r_ // 128) * (cols // 128) * 4
+        elif recipe == RECIPE_MXFP8:
+            need = r_ * (cols // 32)
+        else:
+            need = 0
+        if st_.numel() * st_.element_size() < need:
+            raise ValueError(f"{name}_s holds {st_.numel() * st_.element_size()} bytes, the recipe needs {need}")
+    src = _Weight(recipe, rows, cols, src_q.data_ptr(), src_s.data_ptr())
+    dst = _Weight(recipe, drows, dst_q.shape[-1], dst_q.data_ptr(), dst_s.data_ptr())
+    _check(lib.fp8_weight_install(ctypes.byref(src), ctypes.byref(dst), _stream(src_q.device)), "fp8_weight_install")
+    return dst_q, dst_s

@@ -1,0 +1,277 @@
+// C ABI of libfp8rl (declared in include/fp8rl.h). Every entry point validates all of its
+// arguments on the host before making any HIP call, checks once per device that the
+// current device is gfx950, then enqueues its kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8rl.h"
+#include "internal.hpp"
+
+namespace {
+
+using namespace fp8rl;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fp8rl_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8RL_ERR_DEVICE;
+  int state = dev < kMaxDevices ? g_device_state[dev].load(std::memory_order_acquire) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8RL_ERR_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (dev < kMaxDevices) g_device_state[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? FP8RL_OK : FP8RL_ERR_DEVICE;
+}
+
+fp8rl_status launched(hipError_t e) { return e == hipSuccess ? FP8RL_OK : FP8RL_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Grid-size guard: kernels index workgroups with 32-bit ids.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+fp8rl_status check_dims(int64_t a, int64_t b) {
+  if (a < 0 || b < 0) return FP8RL_ERR_SHAPE;
+  if (a > 0 && b > kMaxElems / a) return FP8RL_ERR_SHAPE;
+  return FP8RL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8rl_abi_version(void) { return FP8RL_ABI_VERSION; }
+
+const char* fp8rl_status_str(fp8rl_status s) {
+  switch (s) {
+    case FP8RL_OK: return "ok";
+    case FP8RL_ERR_NULL: return "required pointer is NULL (or an output pair is half given)";
+    case FP8RL_ERR_SHAPE: return "invalid shape for this call's granularity rules";
+    case FP8RL_ERR_ALIGN: return "pointer misaligned (data 16 bytes, fp32 scales 4 bytes)";
+    case FP8RL_ERR_RECIPE: return "unsupported recipe/dtype or install descriptors disagree";
+    case FP8RL_ERR_DEVICE: return "current HIP device is not gfx950";
+    case FP8RL_ERR_LAUNCH: return "kernel launch failed";
+    case FP8RL_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                 float* st, void* stream) {
+  if ((q == nullptr) != (s == nullptr) || (qt == nullptr) != (st == nullptr)) return FP8RL_ERR_NULL;
+  if (q == nullptr && qt == nullptr) return FP8RL_ERR_NULL;
+  if (fp8rl_status e = check_dims(M, K)) return e;
+  if (K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (qt != nullptr && M % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8RL_OK;
+  if (x == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(x, 16) || (q && !aligned(q, 16)) || (qt && !aligned(qt, 16)) || (s && !aligned(s, 4)) ||
+      (st && !aligned(st, 4)))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  if (qt == nullptr) return launched(launch_quant_rows_1x128(x, M, K, q, s, as_stream(stream)));
+  return launched(launch_quant_act_tile(x, M, K, q, s, qt, st, as_stream(stream)));
+}
+
+fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                 void* stream) {
+  if (q == nullptr || s == nullptr) return FP8RL_ERR_NULL;
+  if (fp8rl_status e = check_dims(N, K)) return e;
+  if (N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8RL_OK;
+  if (w == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || (qt && !aligned(qt, 16))) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_quant_w_128x128(w, N, K, q, s, qt, as_stream(stream)));
+}
+
+fp8rl_status mxfp8_quant_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0, void* stream) {
+  if (q == nullptr || e8m0 == nullptr) return FP8RL_ERR_NULL;
+  if (fp8rl_status e = check_dims(R, K)) return e;
+  if (K % 32 != 0) return FP8RL_ERR_SHAPE;
+  if (R == 0 || K == 0) return FP8RL_OK;
+  if (x == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16)) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_quant_mx_1x32(x, R, K, q, e8m0, as_stream(stream)));
+}
+
+size_t fp8rl_fwd_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 128 != 0 || check_dims(M, K) != FP8RL_OK) return 0;
+  const size_t qbytes = (size_t)(M * K);
+  const size_t qpad = (qbytes + 255) & ~(size_t)255;
+  return qpad + (size_t)M * (size_t)(K / 128) * sizeof(float);
+}
+
+fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const uint16_t* x_bf16, const uint8_t* wq,
+                                      const float* sw, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const bool quantized = xq != nullptr || sx != nullptr;
+  if (quantized && (xq == nullptr || sx == nullptr)) return FP8RL_ERR_NULL;
+  if (quantized == (x_bf16 != nullptr)) return FP8RL_ERR_NULL;  // exactly one form of X
+  if (wq == nullptr || sw == nullptr || y == nullptr) return FP8RL_ERR_NULL;
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
+  if (fp8rl_status e = check_dims(M, K)) return e;
+  if (fp8rl_status e = check_dims(N, K)) return e;
+  if (fp8rl_status e = check_dims(M, N)) return e;
+  if (K % 128 != 0 || N % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8RL_OK;
+  if (K == 0) return FP8RL_ERR_SHAPE;  // the product would be all zeros; not a supported call
+  if (!aligned(wq, 16) || !aligned(sw, 4) || !aligned(y, 16)) return FP8RL_ERR_ALIGN;
+  if (quantized && (!aligned(xq, 16) || !aligned(sx, 4))) return FP8RL_ERR_ALIGN;
+  if (!quantized) {
+    if (!aligned(x_bf16, 16)) return FP8RL_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < fp8rl_fwd_workspace_bytes(M, K)) return FP8RL_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+  }
+  if (fp8rl_status e = check_device()) return e;
+  hipStream_t st = as_stream(stream);
+  if (!quantized) {
+    const size_t qpad = ((size_t)(M * K) + 255) & ~(size_t)255;
+    uint8_t* wxq = static_cast<uint8_t*>(workspace);
+    float* wsx = reinterpret_cast<float*>(wxq + qpad);
+    if (launch_quant_rows_1x128(x_bf16, M, K, wxq, wsx, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
+    xq = wxq;
+    sx = wsx;
+  }
+  GemmParams p{};
+  p.A = xq;
+  p.B = wq;
+  p.sA = sx;
+  p.sB = sw;
+  p.C = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.sa_ld = K / 128;
+  p.sb_ld_n = K / 128;
+  p.sb_ld_k = 1;
+  p.ldc = N;
+  p.accumulate = 0;
+  return launched(launch_gemm_blockscaled(p, false, y_dtype == FP8RL_OUT_F32, st));
+}
+
+fp8rl_status fp8_gemm_blockscaled_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wqt, const float* sw,
+                                        int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* stream) {
+  if (dyq == nullptr || sdy == nullptr || wqt == nullptr || sw == nullptr || dx == nullptr) return FP8RL_ERR_NULL;
+  if (dx_dtype != FP8RL_OUT_BF16 && dx_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
+  if (fp8rl_status e = check_dims(M, N)) return e;
+  if (fp8rl_status e = check_dims(N, K)) return e;
+  if (fp8rl_status e = check_dims(M, K)) return e;
+  if (N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8RL_OK;
+  if (N == 0) return FP8RL_ERR_SHAPE;
+  if (!aligned(dyq, 16) || !aligned(wqt, 16) || !aligned(dx, 16) || !aligned(sdy, 4) || !aligned(sw, 4))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  GemmParams p{};
+  p.A = dyq;                 // [M][N]: contraction over N
+  p.B = wqt;                 // [K][N]
+  p.sA = sdy;
+  p.sB = sw;                 // sw[N/128][K/128]: output block j = k/128, contraction block c = n/128
+  p.C = dx;
+  p.M = M;
+  p.N = K;
+  p.K = N;
+  p.sa_ld = N / 128;
+  p.sb_ld_n = 1;
+  p.sb_ld_k = K / 128;
+  p.ldc = K;
+  p.accumulate = 0;
+  return launched(launch_gemm_blockscaled(p, false, dx_dtype == FP8RL_OUT_F32, as_stream(stream)));
+}
+
+fp8rl_status fp8_gemm_blockscaled_wgrad(const uint8_t* dyqt, const float* sdyt, const uint8_t* xqt, const float* sxt,
+                                        int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream) {
+  if (dyqt == nullptr || sdyt == nullptr || xqt == nullptr || sxt == nullptr || dw == nullptr) return FP8RL_ERR_NULL;
+  if (fp8rl_status e = check_dims(M, N)) return e;
+  if (fp8rl_status e = check_dims(M, K)) return e;
+  if (fp8rl_status e = check_dims(N, K)) return e;
+  if (M % 128 != 0 || N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8RL_OK;
+  if (M == 0) return FP8RL_ERR_SHAPE;
+  if (!aligned(dyqt, 16) || !aligned(xqt, 16) || !aligned(dw, 16) || !aligned(sdyt, 4) || !aligned(sxt, 4))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  GemmParams p{};
+  p.A = dyqt;                // [N][M]: contraction over the M tokens
+  p.B = xqt;                 // [K][M]
+  p.sA = sdyt;
+  p.sB = sxt;
+  p.C = dw;
+  p.M = N;
+  p.N = K;
+  p.K = M;
+  p.sa_ld = M / 128;
+  p.sb_ld_n = M / 128;
+  p.sb_ld_k = 1;
+  p.ldc = K;
+  p.accumulate = accumulate ? 1 : 0;
+  return launched(launch_gemm_blockscaled(p, true, true, as_stream(stream)));
+}
+
+fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, const uint8_t* wq, const void* sw,
+                              const int32_t* offsets, int64_t T, int64_t E, int64_t N, int64_t K, void* y,
+                              int y_dtype, void* stream) {
+  if (recipe != FP8RL_RECIPE_MXFP8) return FP8RL_ERR_RECIPE;
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
+  if (xq == nullptr || sx == nullptr || wq == nullptr || sw == nullptr || offsets == nullptr || y == nullptr)
+    return FP8RL_ERR_NULL;
+  if (E < 1) return FP8RL_ERR_SHAPE;
+  if (fp8rl_status e = check_dims(T, K)) return e;
+  if (fp8rl_status e = check_dims(E * N, K)) return e;
+  if (fp8rl_status e = check_dims(T, N)) return e;
+  if (K % 128 != 0 || N % 16 != 0 || E > ((int64_t)1 << 24)) return FP8RL_ERR_SHAPE;
+  if (T == 0 || N == 0) return FP8RL_OK;
+  if (K == 0) return FP8RL_ERR_SHAPE;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(sx, 4) || !aligned(sw, 4) ||
+      !aligned(offsets, 4))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  GroupedParams p{};
+  p.X = xq;
+  p.Xs = static_cast<const uint8_t*>(sx);
+  p.W = wq;
+  p.Ws = static_cast<const uint8_t*>(sw);
+  p.offsets = offsets;
+  p.Y = y;
+  p.T = T;
+  p.E = E;
+  p.N = N;
+  p.K = K;
+  return launched(launch_grouped_mx(p, y_dtype == FP8RL_OUT_F32, as_stream(stream)));
+}
+
+fp8rl_status fp8_weight_install(const fp8rl_weight* src, const fp8rl_weight* dst, void* stream) {
+  if (src == nullptr || dst == nullptr) return FP8RL_ERR_NULL;
+  if (src->recipe != dst->recipe || src->rows != dst->rows || src->cols != dst->cols) return FP8RL_ERR_RECIPE;
+  const int64_t rows = src->rows, cols = src->cols;
+  if (fp8rl_status e = check_dims(rows, cols)) return e;
+  int64_t sbytes;
+  if (src->recipe == FP8RL_RECIPE_BLOCK128) {
+    if (rows % 128 != 0 || cols % 128 != 0) return FP8RL_ERR_SHAPE;
+    sbytes = (rows / 128) * (cols / 128) * 4;
+  } else if (src->recipe == FP8RL_RECIPE_MXFP8) {
+    if (cols % 32 != 0) return FP8RL_ERR_SHAPE;
+    sbytes = rows * (cols / 32);
+  } else {
+    return FP8RL_ERR_RECIPE;
+  }
+  if (rows == 0 || cols == 0) return FP8RL_OK;
+  if (src->q == nullptr || src->s == nullptr || dst->q == nullptr || dst->s == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(src->q, 16) || !aligned(dst->q, 16) || !aligned(src->s, 4) || !aligned(dst->s, 4))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_copy(src->q, dst->q, rows * cols, static_cast<const uint8_t*>(src->s),
+                              static_cast<uint8_t*>(dst->s), sbytes, as_stream(stream)));
+}
+
+}  // extern "C"

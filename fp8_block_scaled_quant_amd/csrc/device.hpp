@@ -1,0 +1,140 @@
+// Device helpers shared by the libfp8rl kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8rl {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round an fp32 value to bf16 bits, nearest-even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Scale of a 1x128 / 128x1 / 128x128 group: s = fl32(amax / 448) (IEEE division; hipcc's
+// default fp32 division is correctly rounded), 1.0 for an all-zero group. `r` is the
+// fp64 reciprocal used to form the scaled values (see scaled()).
+struct BlockScale {
+  float s;
+  double r;
+};
+
+__device__ __forceinline__ BlockScale block_scale(float amax) {
+  BlockScale b;
+  b.s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+  b.r = 1.0 / (double)b.s;
+  return b;
+}
+
+// The fp32 quotient fl32(x / s) for a bf16 value x with |x| <= amax, computed as
+// fl32(x * fl64(1/s)). x has 8 significant bits and s 24, so x/s never lies within a
+// relative 2^-49 of an fp32 rounding midpoint, while the fp64 product is within 2^-52 of
+// x/s: both round to the same fp32 value. (An exhaustive CPU test over every bf16 pair
+// (x, amax) checks this identity, and that |x/s| stays below 449.)
+__device__ __forceinline__ float scaled(float x, double r) { return (float)((double)x * r); }
+
+// Four fp32 values -> four E4M3 bytes, round to nearest even (v_cvt_pk_fp8_f32 under the
+// default round-to-nearest-even mode). The converter does not saturate: it returns the
+// max-magnitude code only for 448 < |v| < 464, which covers every quotient above, and NaN
+// beyond; callers never pass |v| >= 464.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+// Quantize 8 bf16 values held in 4 words (2 per word) with one group scale -> 8 E4M3 bytes.
+__device__ __forceinline__ uint2 quant8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, double r) {
+  uint2 o;
+  o.x = pack4_e4m3(scaled(bf16_lo(w0), r), scaled(bf16_hi(w0), r), scaled(bf16_lo(w1), r), scaled(bf16_hi(w1), r));
+  o.y = pack4_e4m3(scaled(bf16_lo(w2), r), scaled(bf16_hi(w2), r), scaled(bf16_lo(w3), r), scaled(bf16_hi(w3), r));
+  return o;
+}
+
+// max(|lo|, |hi|) of the two bf16 values in a word.
+__device__ __forceinline__ float absmax2(uint32_t w) {
+  return fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w)));
+}
+
+// MXFP8 exponent for a group amax: the smallest integer e with amax <= 448 * 2^e, clamped
+// to [-127, 127]; 0 for amax == 0. For amax = 1.m * 2^F (m the 23-bit field), 448 * 2^(F-8)
+// = 1.75 * 2^F, so e = F - 8 when the mantissa field is <= 0x600000, else F - 7. A
+// subnormal amax (< 2^-126) needs e <= -134, i.e. the clamp value -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t u = __float_as_uint(amax);
+  const int be = (int)((u >> 23) & 0xffu);
+  if (be == 0) return -127;
+  const int F = be - 127;
+  int e = ((u & 0x7fffffu) <= 0x600000u) ? F - 8 : F - 7;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads at byte offsets >= bytes return
+// zero instead of touching memory (the hardware range check of raw buffers, stride 0).
+// The last dword is the gfx9 buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct buffer -> LDS copies (buffer_load_dword{,x4} ... lds): lane i's 16 (or 4) bytes
+// from rsrc + voff land at lds_base + 16 * i (or 4 * i). lds_base must be wave-uniform.
+// The per-lane state is one 32-bit offset; the descriptor lives in SGPRs.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Swizzled LDS layout for 128-byte rows of FP8 (one 128-wide K block per row): the 16-byte
+// chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7). With 64 banks of 4 bytes,
+// 16 consecutive rows reading the same logical chunk then hit 16 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// MFMA operand fragment for v_mfma_*_16x16x128_f8f6f4: lane l holds row (l & 15) of a
+// 16 x 128 FP8 tile; lane group g = l >> 4 holds K bytes [16g, 16g+16) in bytes 0..15 and
+// [64+16g, 64+16g+16) in bytes 16..31. `tile` is the swizzled 128-byte-row LDS tile.
+__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row0, int lane) {
+  const int row = row0 + (lane & 15);
+  const int g = lane >> 4;
+  const uint8_t* base = tile + row * 128;
+  const uint4 lo = *reinterpret_cast<const uint4*>(base + (swz(row, g) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(base + (swz(row, g + 4) << 4));
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+// 16x16x128 FP8 MFMA (E4M3 x E4M3, cbsz = blgp = 0). Scales are E8M0 bytes; lane
+// (i + 16 b) supplies the scale of row i for K block [32b, 32b+32). 127 = 1.0.
+__device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// Logical tile index for workgroup `bid` of `nblocks`: the hardware deals workgroups to
+// the 8 XCDs round-robin (bid % 8); this gives XCD x the contiguous logical range
+// [start_x, start_x + count_x) so that neighbouring tiles, which share operand rows,
+// run under the same L2. A bijection on [0, nblocks).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks >> 3, rem = nblocks & 7;
+  const int x = bid & 7, idx = bid >> 3;
+  return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
+}
+
+}  // namespace fp8rl

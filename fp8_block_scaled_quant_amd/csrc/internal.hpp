@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI layer (abi.hip) and the kernel files.
+// Launchers assume validated arguments: non-empty shapes that satisfy each call's rules.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8rl {
+
+hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                                   hipStream_t stream);
+hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                 float* st, hipStream_t stream);
+hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                  hipStream_t stream);
+hipError_t launch_quant_mx_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0,
+                                hipStream_t stream);
+
+// C[m][n] = sum_kb sA[m * sa_ld + kb] * sB(n, kb) * sum_{k in kb} A[m][k] * B[n][k]
+//   row-scaled B : sB(n, kb) = sB[n * sb_ld_n + kb]
+//   block-scaled B: sB(n, kb) = sB[(n / 128) * sb_ld_n + kb * sb_ld_k]
+struct GemmParams {
+  const uint8_t* A;
+  const uint8_t* B;
+  const float* sA;
+  const float* sB;
+  void* C;
+  int64_t M, N, K;
+  int64_t sa_ld, sb_ld_n, sb_ld_k, ldc;
+  int accumulate;
+};
+hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, hipStream_t stream);
+
+struct GroupedParams {
+  const uint8_t* X;     // [T][K]
+  const uint8_t* Xs;    // E8M0 [T][K/32]
+  const uint8_t* W;     // [E][N][K]
+  const uint8_t* Ws;    // E8M0 [E][N][K/32]
+  const int32_t* offsets;
+  void* Y;              // [T][N]
+  int64_t T, E, N, K;
+};
+hipError_t launch_grouped_mx(const GroupedParams& p, bool f32, hipStream_t stream);
+
+hipError_t launch_copy(const uint8_t* src_q, uint8_t* dst_q, int64_t qbytes, const uint8_t* src_s, uint8_t* dst_s,
+                       int64_t sbytes, hipStream_t stream);
+
+}  // namespace fp8rl

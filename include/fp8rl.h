@@ -1,0 +1,193 @@
+/*
+ * libfp8rl: fine-grained FP8 (E4M3) quantization and block-scaled FP8 GEMMs for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages describing the method), cited by title and section:
+ *   [SkyRL-FP8] "Anyscale、SkyRL で FP8 学習・ロールアウトをサポートし一貫性を維持"
+ *               (news.ainew.jp translation of the Anyscale/SkyRL FP8 article)
+ *   [AIS]       "AIS: Adaptive Importance Sampling for Quantized RL" (kasblo.com explainer)
+ *   [Jet-RL]    "Jet-RL: Enabling On-Policy FP8 Reinforcement Learning with Unified
+ *               Training and Rollout Precision Flow" (gist.science summary)
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library keeps no
+ *     pointer after returning and allocates no memory.
+ *   - Tensors are row-major and contiguous. bf16 tensors are passed as uint16_t bit
+ *     patterns. FP8 payloads are E4M3 "FN" bytes (bias 7, max 448, NaN 0x7F/0xFF).
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the legacy default
+ *     stream). No synchronization, no host<->device copies; group offsets are read on the
+ *     device.
+ *   - All arguments are validated before any HIP call is made. Invalid arguments return a
+ *     status code and enqueue nothing. A call whose work is empty (a zero-sized dimension)
+ *     returns FP8RL_OK without touching the device.
+ *   - Data pointers must be 16-byte aligned (FP8RL_ERR_ALIGN otherwise); scale pointers
+ *     4-byte aligned (fp32) or 1-byte (E8M0).
+ *   - FP8RL_ERR_DEVICE: the current device is not gfx950. FP8RL_ERR_LAUNCH: the kernel
+ *     launch was rejected by the runtime. Faults inside a kernel surface at the caller's
+ *     next synchronization with the stream, as for any HIP kernel.
+ *   - Results are deterministic: no atomics, a fixed reduction order, and the same bytes
+ *     from run to run and across output modes.
+ *   - Calls that share no output buffer may run concurrently on different streams.
+ */
+#ifndef FP8RL_H
+#define FP8RL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8RL_OK = 0,
+  FP8RL_ERR_NULL = 1,      /* a required pointer is NULL, or an optional output pair is half given */
+  FP8RL_ERR_SHAPE = 2,     /* a dimension is negative or breaks the granularity rules of the call */
+  FP8RL_ERR_ALIGN = 3,     /* a pointer is not suitably aligned */
+  FP8RL_ERR_RECIPE = 4,    /* unknown / unsupported recipe or dtype, or install descriptors disagree */
+  FP8RL_ERR_DEVICE = 5,    /* current HIP device is not gfx950, or it could not be queried */
+  FP8RL_ERR_LAUNCH = 6,    /* kernel launch failed */
+  FP8RL_ERR_WORKSPACE = 7  /* workspace missing or smaller than fp8rl_fwd_workspace_bytes() */
+} fp8rl_status;
+
+/* Scaling recipes ([SkyRL-FP8] TL;DR and "Deep dive: FP8 quantization with FP32 and
+ * power-of-two block scales": blockwise FP32 scales on Hopper, MXFP8 power-of-two scales
+ * on Blackwell; the recipe is always chosen explicitly by the caller here). */
+typedef enum {
+  FP8RL_RECIPE_BLOCK128 = 0,   /* fp32 scale per 1x128 (activations) / 128x128 (weights) */
+  FP8RL_RECIPE_MXFP8 = 1       /* E8M0 (power-of-two) scale byte per 1x32 along K */
+} fp8rl_recipe;
+
+typedef enum {
+  FP8RL_OUT_BF16 = 0,          /* round-to-nearest-even of the fp32 accumulator */
+  FP8RL_OUT_F32 = 1
+} fp8rl_out;
+
+/* ABI version of this header. */
+#define FP8RL_ABI_VERSION 1
+int fp8rl_abi_version(void);
+const char* fp8rl_status_str(fp8rl_status status);
+
+/* ---------------------------------------------------------------------------------------
+ * Quantizers. The quantizer is the symmetric one of [AIS] (quantizer equation), with the
+ * E4M3 grid: s = fl32(amax / 448) per group (an IEEE fp32 division), q = E4M3(fl32(x / s))
+ * with round-to-nearest-even and saturation to +-448, the sign of zero kept. A group whose
+ * amax is 0 gets s = 1.0. Bytes and scales are bit-identical to the CPU oracle.
+ * ------------------------------------------------------------------------------------- */
+
+/* Activation quantization, 1x128 groups along K and/or 128x1 groups along M
+ * ([Jet-RL] "Quantization scheme": activations 1x128; WGrad operands 1x128 and 128x1;
+ * [SkyRL-FP8] "Performance analysis": row-wise plus transposed FP8 copies for backward).
+ *   x   : bf16 [M][K]
+ *   q,s : row-wise output, q uint8 [M][K], s fp32 [M][K/128]   (both NULL: not produced)
+ *   qt,st: column-wise output written transposed: qt uint8 [K][M], st fp32 [K][M/128];
+ *          qt[k][m] quantizes x[m][k] within the group of 128 consecutive rows m.
+ *          (both NULL: not produced)
+ * Rules: K % 128 == 0; M % 128 == 0 when qt is requested; at least one output pair. */
+fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K,
+                                 uint8_t* q, float* s, uint8_t* qt, float* st, void* stream);
+
+/* Weight quantization, one fp32 scale per 128x128 block ([SkyRL-FP8] "Why FP8 matters for
+ * RL", "When independent quantization breaks policy consistency"; [Jet-RL]).
+ *   w  : bf16 [N][K];  q uint8 [N][K];  s fp32 [N/128][K/128]
+ *   qt : optional (NULL allowed) byte transpose of q, uint8 [K][N] (the DGrad operand;
+ *        a 128x128 block stays a 128x128 block, so s is reused unchanged).
+ * Rules: N % 128 == 0, K % 128 == 0. */
+fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K,
+                                 uint8_t* q, float* s, uint8_t* qt, void* stream);
+
+/* MXFP8 quantization, one E8M0 scale per 1x32 group along K ([SkyRL-FP8] "When
+ * independent quantization breaks policy consistency": one scale per 1x32 block; "Deep
+ * dive": power-of-two, exponent-only scales). The exponent is the smallest e with
+ * amax <= 448 * 2^e (clamped to [-127, 127]; amax 0 gives e = 0); byte = e + 127;
+ * q = E4M3(x * 2^-e) (exact scaling, never saturates).
+ *   x : bf16 [R][K];  q uint8 [R][K];  e8m0 uint8 [R][K/32].   Rules: K % 32 == 0. */
+fp8rl_status mxfp8_quant_1x32(const uint16_t* x, int64_t R, int64_t K,
+                              uint8_t* q, uint8_t* e8m0, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Block-scaled GEMMs (FP8 operands, fp32 accumulation). Each is the product of the
+ * dequantized operands, dequantized value = E4M3 value * scale of its group/block
+ * ([SkyRL-FP8] TL;DR: FP8 linear-layer GEMMs; [Jet-RL] "Quantization scheme").
+ * ------------------------------------------------------------------------------------- */
+
+/* Forward: Y[M][N] = deq(X) . deq(W)^T.
+ *   X given EITHER quantized (xq uint8 [M][K] + sx fp32 [M][K/128], x_bf16 = NULL)
+ *   OR as bf16 (x_bf16 [M][K], xq = sx = NULL): then X is quantized 1x128 on the device
+ *   inside this call ([SkyRL-FP8] "Performance analysis", generation: activation
+ *   quantization folded into the GEMM path while weights and scales stay fixed), into the
+ *   caller's workspace, with bytes identical to fp8_quant_act_1x128.
+ *   wq uint8 [N][K], sw fp32 [N/128][K/128] (as produced by fp8_quant_w_128x128 or
+ *   installed by fp8_weight_install).
+ *   y: [M][N], bf16 or fp32 per y_dtype.
+ *   workspace/workspace_bytes: only for the bf16-input form; at least
+ *   fp8rl_fwd_workspace_bytes(M, K) bytes, 16-byte aligned. Ignored otherwise (may be NULL).
+ * Rules: K % 128 == 0, N % 128 == 0, M >= 0 (any M). */
+fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const uint16_t* x_bf16,
+                                      const uint8_t* wq, const float* sw,
+                                      int64_t M, int64_t N, int64_t K,
+                                      void* y, int y_dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+size_t fp8rl_fwd_workspace_bytes(int64_t M, int64_t K);
+
+/* DGrad: dX[M][K] = deq(dY) . deq(W)  ([Jet-RL] "Quantization scheme": DGrad in FP8).
+ *   dyq uint8 [M][N], sdy fp32 [M][N/128]  (dY quantized 1x128 along N)
+ *   wqt uint8 [K][N]: byte transpose of W's payload (fp8_quant_w_128x128's qt)
+ *   sw  fp32 [N/128][K/128]: W's block scales, NOT transposed.
+ *   dx: [M][K], bf16 or fp32.   Rules: N % 128 == 0, K % 128 == 0, M >= 0. */
+fp8rl_status fp8_gemm_blockscaled_dgrad(const uint8_t* dyq, const float* sdy,
+                                        const uint8_t* wqt, const float* sw,
+                                        int64_t M, int64_t N, int64_t K,
+                                        void* dx, int dx_dtype, void* stream);
+
+/* WGrad: dW[N][K] = deq(dY)^T . deq(X), both operands grouped 128x1 along the M tokens
+ * ([Jet-RL] "Quantization scheme": WGrad with 1x128 and 128x1 groups), i.e. the
+ * column-wise outputs of fp8_quant_act_1x128:
+ *   dyqt uint8 [N][M], sdyt fp32 [N][M/128];  xqt uint8 [K][M], sxt fp32 [K][M/128].
+ *   dw fp32 [N][K]; accumulate != 0 adds the product to the existing dw contents.
+ * Rules: M % 128 == 0, N % 128 == 0, K % 128 == 0. */
+fp8rl_status fp8_gemm_blockscaled_wgrad(const uint8_t* dyqt, const float* sdyt,
+                                        const uint8_t* xqt, const float* sxt,
+                                        int64_t M, int64_t N, int64_t K,
+                                        float* dw, int accumulate, void* stream);
+
+/* Grouped GEMM for mixture-of-experts ([SkyRL-FP8] MoE: routed experts hold most
+ * parameters; MXFP8 recipe). Routed rows are grouped by expert; rows
+ * offsets[e] .. offsets[e+1]-1 belong to expert e:
+ *   Y[t][n] = sum_k deq(X)[t][k] * deq(W[e])[n][k].
+ *   recipe FP8RL_RECIPE_MXFP8: xq uint8 [T][K], sx = E8M0 uint8 [T][K/32],
+ *                              wq uint8 [E][N][K], sw = E8M0 uint8 [E][N][K/32].
+ *   offsets: DEVICE int32 [E+1], expected 0 = offsets[0] <= ... <= offsets[E] = T. The
+ *   kernel clamps every offset into [0, T] and treats a decreasing step as an empty
+ *   expert, so malformed offsets never cause an out-of-bounds access; rows not covered by
+ *   any expert are left unwritten.
+ *   y: [T][N], bf16 or fp32.
+ * Rules: K % 128 == 0, N % 16 == 0, E >= 1. FP8RL_RECIPE_BLOCK128 -> FP8RL_ERR_RECIPE. */
+fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx,
+                              const uint8_t* wq, const void* sw, const int32_t* offsets,
+                              int64_t T, int64_t E, int64_t N, int64_t K,
+                              void* y, int y_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Zero-requantization weight install ([SkyRL-FP8] "On-Policy FP8 weight sync", Fig. 3:
+ * the rollout side installs the trainer's FP8 payload and block scales without a
+ * quantizer of its own, so both sides hold bit-identical weights).
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  int recipe;        /* fp8rl_recipe */
+  int64_t rows;      /* N (for MXFP8 expert stacks: E*N) */
+  int64_t cols;      /* K */
+  uint8_t* q;        /* payload uint8 [rows][cols] */
+  void* s;           /* BLOCK128: fp32 [rows/128][cols/128];  MXFP8: E8M0 uint8 [rows][cols/32] */
+} fp8rl_weight;
+
+/* Copies src's payload and scales verbatim into dst's buffers. The descriptors must agree
+ * on recipe, rows and cols (FP8RL_ERR_RECIPE otherwise: the library never requantizes).
+ * Rules: BLOCK128: rows % 128 == 0, cols % 128 == 0; MXFP8: cols % 32 == 0. src and dst
+ * buffers must not overlap. */
+fp8rl_status fp8_weight_install(const fp8rl_weight* src, const fp8rl_weight* dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8RL_H */

@@ -49,9 +49,12 @@ MX_GROUP = 32        # MXFP8 1x32 granularity
 
 
 def _as_f32(x) -> np.ndarray:
+    """The quantizers take bf16 tensors, passed as float32 arrays of bf16-exact values."""
     x = np.asarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("quantizer input must be finite")
+    if np.any(x.view(np.uint32) & 0xFFFF):
+        raise ValueError("quantizer input must hold bf16 values (float32 with the low 16 bits zero)")
     return x
 
 

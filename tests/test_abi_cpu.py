@@ -1,0 +1,158 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every function that
+include/fp8rl.h declares under its C name, and rejects invalid arguments with the
+documented status codes before making any HIP call (no GPU needed: the pointers below are
+never dereferenced)."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import fp8_block_scaled_quant_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8rl.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_RECIPE, ERR_DEVICE, ERR_LAUNCH, ERR_WORKSPACE = range(8)
+P = 0x10000          # an aligned, never-dereferenced fake device address
+P2 = 0x20000
+MIS = 0x10008        # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(fp8\w*|mxfp8\w*)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(F.library_path()):
+        pytest.fail("libfp8rl.so is not built (run __graft_entry__.build())")
+    return F.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["fp8_quant_act_1x128", "fp8_quant_w_128x128", "mxfp8_quant_1x32", "fp8_gemm_blockscaled_fwd",
+              "fp8_gemm_blockscaled_dgrad", "fp8_gemm_blockscaled_wgrad", "fp8_grouped_gemm", "fp8_weight_install",
+              "fp8rl_abi_version", "fp8rl_status_str", "fp8rl_fwd_workspace_bytes"]:
+        assert n in names
+
+
+def test_every_declared_function_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", F.library_path()], capture_output=True, text=True).stdout
+        exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+        for n in declared_functions():
+            assert n in exported, f"{n} not exported with C linkage"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fp8rl_abi_version() == 1
+    for code in range(8):
+        assert len(lib.fp8rl_status_str(code)) > 0
+    assert lib.fp8rl_status_str(99) == b"unknown status"
+
+
+def test_workspace_size(lib):
+    assert lib.fp8rl_fwd_workspace_bytes(256, 4096) == 256 * 4096 + 256 * 32 * 4
+    assert lib.fp8rl_fwd_workspace_bytes(3, 128) == 512 + 3 * 4
+    assert lib.fp8rl_fwd_workspace_bytes(0, 128) == 0
+    assert lib.fp8rl_fwd_workspace_bytes(4, 100) == 0
+
+
+def test_quant_act_validation(lib):
+    f = lib.fp8_quant_act_1x128
+    assert f(P, 4, 256, P, None, None, None, None) == ERR_NULL          # half a pair
+    assert f(P, 4, 256, None, None, None, None, None) == ERR_NULL       # nothing requested
+    assert f(P, 4, 100, P, P, None, None, None) == ERR_SHAPE            # K % 128
+    assert f(P, -1, 128, P, P, None, None, None) == ERR_SHAPE
+    assert f(P, 100, 128, None, None, P, P, None) == ERR_SHAPE          # column groups need M % 128
+    assert f(MIS, 4, 128, P, P, None, None, None) == ERR_ALIGN
+    assert f(P, 4, 128, MIS, P, None, None, None) == ERR_ALIGN
+    assert f(P, 4, 128, P, P + 2, None, None, None) == ERR_ALIGN
+    assert f(None, 4, 128, P, P, None, None, None) == ERR_NULL
+    assert f(None, 0, 128, P, P, None, None, None) == OK                # empty: no device work
+
+
+def test_quant_w_and_mx_validation(lib):
+    assert lib.fp8_quant_w_128x128(P, 128, 128, None, P, None, None) == ERR_NULL
+    assert lib.fp8_quant_w_128x128(P, 100, 128, P, P, None, None) == ERR_SHAPE
+    assert lib.fp8_quant_w_128x128(P, 128, 64, P, P, None, None) == ERR_SHAPE
+    assert lib.fp8_quant_w_128x128(P, 128, 128, P, P, MIS, None) == ERR_ALIGN
+    assert lib.fp8_quant_w_128x128(None, 0, 128, P, P, None, None) == OK
+    assert lib.mxfp8_quant_1x32(P, 4, 48, P, P, None) == ERR_SHAPE
+    assert lib.mxfp8_quant_1x32(P, 4, 64, None, P, None) == ERR_NULL
+    assert lib.mxfp8_quant_1x32(P, 4, 64, MIS, P, None) == ERR_ALIGN
+    assert lib.mxfp8_quant_1x32(None, 0, 64, P, P, None) == OK
+
+
+def test_gemm_validation(lib):
+    fwd = lib.fp8_gemm_blockscaled_fwd
+    assert fwd(P, P, P, P, P, 4, 128, 128, P, 0, None, 0, None) == ERR_NULL      # both forms of X
+    assert fwd(None, None, None, P, P, 4, 128, 128, P, 0, None, 0, None) == ERR_NULL
+    assert fwd(P, None, None, P, P, 4, 128, 128, P, 0, None, 0, None) == ERR_NULL
+    assert fwd(P, P, None, P, P, 4, 128, 128, P, 7, None, 0, None) == ERR_RECIPE
+    assert fwd(P, P, None, P, P, 4, 128, 100, P, 0, None, 0, None) == ERR_SHAPE   # K % 128
+    assert fwd(P, P, None, P, P, 4, 100, 128, P, 0, None, 0, None) == ERR_SHAPE   # N % 128
+    assert fwd(P, P, None, P, P, 0, 128, 128, P, 0, None, 0, None) == OK
+    assert fwd(P, P, None, MIS, P, 4, 128, 128, P, 0, None, 0, None) == ERR_ALIGN
+    assert fwd(None, None, P, P, P, 4, 128, 128, P, 0, None, 0, None) == ERR_WORKSPACE
+    assert fwd(None, None, P, P, P, 4, 128, 128, P, 0, P2, 100, None) == ERR_WORKSPACE
+    assert fwd(None, None, P, P, P, 4, 128, 128, P, 0, MIS, 1 << 20, None) == ERR_ALIGN
+    dg = lib.fp8_gemm_blockscaled_dgrad
+    assert dg(P, P, None, P, 4, 128, 128, P, 0, None) == ERR_NULL
+    assert dg(P, P, P, P, 4, 100, 128, P, 0, None) == ERR_SHAPE
+    assert dg(P, P, P, P, 4, 128, 100, P, 0, None) == ERR_SHAPE
+    assert dg(P, P, P, P, 4, 128, 128, P, 3, None) == ERR_RECIPE
+    assert dg(P, P, P, P, 0, 128, 128, P, 0, None) == OK
+    wg = lib.fp8_gemm_blockscaled_wgrad
+    assert wg(P, P, P, P, 100, 128, 128, P, 0, None) == ERR_SHAPE                  # tokens % 128
+    assert wg(P, P, P, P, 128, 128, 128, None, 0, None) == ERR_NULL
+    assert wg(P, P, P, P, 128, 128, 128, MIS, 0, None) == ERR_ALIGN
+    assert wg(P, P, P, P, 128, 0, 128, P, 0, None) == OK
+
+
+def test_grouped_validation(lib):
+    g = lib.fp8_grouped_gemm
+    assert g(F.RECIPE_BLOCK128, P, P, P, P, P, 64, 2, 128, 128, P, 0, None) == ERR_RECIPE
+    assert g(F.RECIPE_MXFP8, P, P, P, P, P, 64, 0, 128, 128, P, 0, None) == ERR_SHAPE
+    assert g(F.RECIPE_MXFP8, P, P, P, P, P, 64, 2, 128, 96, P, 0, None) == ERR_SHAPE   # K % 128
+    assert g(F.RECIPE_MXFP8, P, P, P, P, P, 64, 2, 120, 128, P, 0, None) == ERR_SHAPE  # N % 16
+    assert g(F.RECIPE_MXFP8, P, P, P, P, None, 64, 2, 128, 128, P, 0, None) == ERR_NULL
+    assert g(F.RECIPE_MXFP8, P, P, P, P, P + 2, 64, 2, 128, 128, P, 0, None) == ERR_ALIGN
+    assert g(F.RECIPE_MXFP8, P, P, P, P, P, 0, 2, 128, 128, P, 0, None) == OK
+
+
+def test_install_validation(lib):
+    W = F._Weight
+    a = W(F.RECIPE_BLOCK128, 256, 256, P, P)
+    assert lib.fp8_weight_install(ctypes.byref(a), ctypes.byref(W(F.RECIPE_MXFP8, 256, 256, P2, P2)), None) == ERR_RECIPE
+    assert lib.fp8_weight_install(ctypes.byref(a), ctypes.byref(W(F.RECIPE_BLOCK128, 128, 256, P2, P2)), None) == ERR_RECIPE
+    assert lib.fp8_weight_install(ctypes.byref(a), None, None) == ERR_NULL
+    bad = W(F.RECIPE_BLOCK128, 100, 256, P, P)
+    assert lib.fp8_weight_install(ctypes.byref(bad), ctypes.byref(W(F.RECIPE_BLOCK128, 100, 256, P2, P2)), None) == ERR_SHAPE
+    mx = W(F.RECIPE_MXFP8, 3, 48, P, P)
+    assert lib.fp8_weight_install(ctypes.byref(mx), ctypes.byref(W(F.RECIPE_MXFP8, 3, 48, P2, P2)), None) == ERR_SHAPE
+    odd = W(7, 128, 128, P, P)
+    assert lib.fp8_weight_install(ctypes.byref(odd), ctypes.byref(W(7, 128, 128, P2, P2)), None) == ERR_RECIPE
+    nul = W(F.RECIPE_BLOCK128, 128, 128, None, P)
+    assert lib.fp8_weight_install(ctypes.byref(nul), ctypes.byref(W(F.RECIPE_BLOCK128, 128, 128, P2, P2)), None) == ERR_NULL
+    e = W(F.RECIPE_BLOCK128, 0, 128, None, None)
+    assert lib.fp8_weight_install(ctypes.byref(e), ctypes.byref(W(F.RECIPE_BLOCK128, 0, 128, None, None)), None) == OK
+
+
+def _gpu_present():
+    return os.path.exists("/dev/kfd")
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-GPU error path; a GPU is present")
+def test_valid_call_without_a_gpu_reports_device_error(lib):
+    # Arguments pass validation; the device query then fails on a host without a GPU.
+    assert lib.fp8_quant_act_1x128(P, 4, 128, P, P, None, None, None) == ERR_DEVICE
