@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp8rl {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -81,21 +83,37 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Raw buffer descriptor over [base, base + bytes): loads at byte offsets >= bytes return
-// zero instead of touching memory (the hardware range check of raw buffers, stride 0).
-// The last dword is the gfx9 buffer format word.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Raw buffer descriptor over [base, base + bytes) as four SGPR words: loads at byte
+// offsets >= bytes return zero instead of touching memory (the hardware range check of
+// raw buffers, stride 0). The last word is the gfx9 buffer format word.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)p);
 }
 
 // Direct buffer -> LDS copies (buffer_load_dword{,x4} ... lds): lane i's 16 (or 4) bytes
-// from rsrc + voff land at lds_base + 16 * i (or 4 * i). lds_base must be wave-uniform.
-// The per-lane state is one 32-bit offset; the descriptor lives in SGPRs.
-__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
+// from rsrc + voff land at LDS address lds + 16 * i (or 4 * i); lds must be wave-uniform.
+// Issued as inline assembly on purpose: the copy's completion is awaited explicitly
+// (wait_vmem() followed by a barrier before the stage is read), so the compiler must not
+// insert its own conservative vmcnt waits in front of unrelated LDS reads.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
 }
-__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, 0, 0, 0);
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -108,23 +126,67 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 
 // MFMA operand fragment for v_mfma_*_16x16x128_f8f6f4: lane l holds row (l & 15) of a
 // 16 x 128 FP8 tile; lane group g = l >> 4 holds K bytes [16g, 16g+16) in bytes 0..15 and
-// [64+16g, 64+16g+16) in bytes 16..31. `tile` is the swizzled 128-byte-row LDS tile.
-__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row0, int lane) {
-  const int row = row0 + (lane & 15);
+// [64+16g, 64+16g+16) in bytes 16..31. In the swizzled 128-byte-row LDS tile, every
+// fragment that starts on a multiple of 16 rows has the same swizzle phase, so a lane's
+// two byte offsets are computed once (FragOffsets) and fragment f of a run of fragments
+// is read at those offsets + f * 2048 (an immediate offset of the LDS read).
+struct FragOffsets {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ FragOffsets frag_offsets(int row0, int lane) {
+  const int row = row0 + (lane & 15);   // row0 % 16 == 0
   const int g = lane >> 4;
-  const uint8_t* base = tile + row * 128;
-  const uint4 lo = *reinterpret_cast<const uint4*>(base + (swz(row, g) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(base + (swz(row, g + 4) << 4));
-  v8i f;
-  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
-  return f;
+  FragOffsets o;
+  o.lo = (uint32_t)(row * 128 + (swz(row, g) << 4));
+  o.hi = (uint32_t)(row * 128 + (swz(row, g + 4) << 4));
+  return o;
 }
+// LDS reads issued in program order as inline assembly (the compiler neither hoists them
+// nor inserts waits for them); the consumer calls lds_wait(...) on the destination
+// registers, which orders every later use after the wait.
+template <int OFF>
+__device__ __forceinline__ v4i ds_read16(uint32_t addr) {
+  v4i r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ float ds_read4f(uint32_t addr) {
+  float r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N)); }
+// Tie a value to the preceding wait so no use of it can be scheduled before the wait.
+template <typename T>
+__device__ __forceinline__ void hold(T& v) { asm volatile("" : "+v"(v)); }
 
+// Fragment f of a run (see FragOffsets) from the LDS tile at byte address `tile`.
+template <int F>
+__device__ __forceinline__ void read_frag(uint32_t tile, FragOffsets o, v4i& lo, v4i& hi) {
+  lo = ds_read16<F * 2048>(tile + o.lo);
+  hi = ds_read16<F * 2048>(tile + o.hi);
+}
+__device__ __forceinline__ v8i join(const v4i& lo, const v4i& hi) {
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
 // 16x16x128 FP8 MFMA (E4M3 x E4M3, cbsz = blgp = 0). Scales are E8M0 bytes; lane
 // (i + 16 b) supplies the scale of row i for K block [32b, 32b+32). 127 = 1.0.
 __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Logical tile index for workgroup `bid` of `nblocks`: the hardware deals workgroups to

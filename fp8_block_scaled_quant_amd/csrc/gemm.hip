@@ -39,10 +39,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   constexpr int OFF_B = BM * 128;
   constexpr int OFF_SA = OFF_B + BN * 128;
   constexpr int OFF_SB = OFF_SA + BM * 4;
-  constexpr int STAGE = OFF_SB + NSB * 4;
+  constexpr int STAGE = OFF_SA + NT * 4;   // one 64-float scale slot per wave (A, B, then unused)
   static_assert(BM % WM == 0 && BN % WN == 0 && TM % 16 == 0 && TN % 16 == 0, "tile shape");
   static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
   static_assert(NT >= BM + NSB, "one scale load per wave");
+  static_assert(OFF_SB + NSB * 4 <= STAGE, "scale slots");
   static_assert(kRowB || TN <= 128, "a wave's n range must sit inside one 128-row scale block");
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
@@ -70,22 +71,19 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
 
   // Staged loads go through raw buffer descriptors whose range ends at the last valid row
   // of the tile, so rows past the end of A / B (and their scales) read as zero without a
-  // memory access; their results are never stored. Per lane: one 32-bit offset per load.
+  // memory access; their results are never stored.
   constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;
+  // Load `it` covers tile rows it * NT/8 .. : the same per-lane offset works for every
+  // `it` once the descriptor base moves by it * (NT/8) * K bytes, because NT/8 is a
+  // multiple of 16 and so leaves the row swizzle phase ((r >> 1) & 7) unchanged.
+  static_assert((NT / 8) % 16 == 0, "swizzle phase must repeat across loads");
   const int64_t rows_a = min((int64_t)BM, M - m0), rows_b = min((int64_t)BN, N - n0);
-  uint32_t offA[LA], offB[LB];
-#pragma unroll
-  for (int it = 0; it < LA; ++it) {
-    const int Lc = it * NT + tid, r = Lc >> 3;
-    offA[it] = (uint32_t)(r * K) + (uint32_t)(swz(r, Lc & 7) << 4);
-  }
-#pragma unroll
-  for (int it = 0; it < LB; ++it) {
-    const int Lc = it * NT + tid, r = Lc >> 3;
-    offB[it] = (uint32_t)(r * K) + (uint32_t)(swz(r, Lc & 7) << 4);
-  }
+  const int lr = tid >> 3;
+  const uint32_t off0 = (uint32_t)(lr * K) + (uint32_t)(swz(lr, tid & 7) << 4);
   const uint32_t bytesA = (uint32_t)((rows_a - 1) * K + 128), bytesB = (uint32_t)((rows_b - 1) * K + 128);
-  // Scale loads: waves [0, BM/64) fetch sA of the tile rows, the next NSB/64 waves fetch sB.
+  // Scale loads: waves [0, BM/64) fetch sA of the tile rows, the next NSB/64 waves fetch
+  // sB; every other wave issues the same instruction through an empty descriptor (no
+  // memory access) into its own unused slot, which keeps the K step branch-free.
   const bool sa_wave = wave < BM / 64;
   const bool sb_wave = !sa_wave && wave < BM / 64 + NSB / 64;
   const float* baseS;
@@ -99,24 +97,33 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   } else if (kRowB) {
     baseS = p.sB + n0 * p.sb_ld_n;
     offS = (uint32_t)(((wave - BM / 64) * 64 + lane) * p.sb_ld_n * 4);
-    bytesS = (uint32_t)((rows_b - 1) * p.sb_ld_n * 4 + 4);
+    bytesS = sb_wave ? (uint32_t)((rows_b - 1) * p.sb_ld_n * 4 + 4) : 0u;
     sstep = 1;
   } else {
     baseS = p.sB + nb0 * p.sb_ld_n;
     offS = (uint32_t)(lane * p.sb_ld_n * 4);
-    bytesS = (uint32_t)((nbl - nb0) * p.sb_ld_n * 4 + 4);
+    bytesS = sb_wave ? (uint32_t)((nbl - nb0) * p.sb_ld_n * 4 + 4) : 0u;
     sstep = p.sb_ld_k;
   }
-  const int s_lds = sa_wave ? OFF_SA + wave * 256 : OFF_SB + (wave - BM / 64) * 256;
 
-  auto issue = [&](int kb, uint8_t* sm) {
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + m0 * K + kb * 128, bytesA);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + n0 * K + kb * 128, bytesB);
+  // Stage the operands of K block kb into the stage at LDS address st. For kb >= nkb every
+  // descriptor is empty: the loads write zeros without touching memory.
+  auto issue = [&](int kb, uint32_t st) __attribute__((always_inline)) {
+    const bool live = kb < nkb;
+    const int kbc = live ? kb : 0;
 #pragma unroll
-    for (int it = 0; it < LA; ++it) buf2lds16(ra, offA[it], sm + (it * NT + wave * 64) * 16);
+    for (int it = 0; it < LA; ++it) {
+      const int64_t r0 = (int64_t)it * (NT / 8);
+      const uint32_t nb = (live && bytesA > r0 * K) ? (uint32_t)(bytesA - r0 * K) : 0u;
+      dma16(make_rsrc(p.A + (m0 + r0) * K + kbc * 128, nb), off0, st + (it * NT + wave * 64) * 16);
+    }
 #pragma unroll
-    for (int it = 0; it < LB; ++it) buf2lds16(rb, offB[it], sm + OFF_B + (it * NT + wave * 64) * 16);
-    if (sa_wave || sb_wave) buf2lds4(make_rsrc(baseS + kb * sstep, bytesS), offS, sm + s_lds);
+    for (int it = 0; it < LB; ++it) {
+      const int64_t r0 = (int64_t)it * (NT / 8);
+      const uint32_t nb = (live && bytesB > r0 * K) ? (uint32_t)(bytesB - r0 * K) : 0u;
+      dma16(make_rsrc(p.B + (n0 + r0) * K + kbc * 128, nb), off0, st + OFF_B + (it * NT + wave * 64) * 16);
+    }
+    dma4(make_rsrc(baseS + kbc * sstep, live ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
   };
 
   v4f acc[FN][FM];
@@ -125,61 +132,115 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* sm) {
-    const float* scA = reinterpret_cast<const float*>(sm + OFF_SA);
-    const float* scB = reinterpret_cast<const float*>(sm + OFF_SB);
-    v8i af[FM];
+  // Per-lane LDS byte offsets inside a stage (fragment rows, scale slots).
+  const FragOffsets fa = frag_offsets(wm0, lane), fb = frag_offsets(wn0, lane);
+  const uint32_t o_sa = OFF_SA + (wm0 + (lane & 15)) * 4;
+  const uint32_t o_sb = kRowB ? OFF_SB + (wn0 + 4 * (lane >> 4)) * 4 : OFF_SB + (uint32_t)(((n0 + wn0) >> 7) - nb0) * 4;
+
+  // One K block from the stage at st. A fragments stay in registers for the whole block; B
+  // fragments are double-buffered (fragment i+1 is read while fragment i feeds the MFMAs);
+  // the FMAs that fold tile t-1 into the accumulators follow the MFMA of tile t
+  // (t = i * FM + j), so one MFMA result is in flight while the previous one is folded.
+  auto compute = [&](uint32_t st) __attribute__((always_inline)) {
+    const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi;
+    const uint32_t b_lo = st + OFF_B + fb.lo, b_hi = st + OFF_B + fb.hi;
+    const uint32_t sa_ad = st + o_sa, sb_ad = st + o_sb;
+    v4i alo[FM], ahi[FM];
     float sa[FM];
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      af[j] = load_frag(sm, wm0 + 16 * j, lane);
-      sa[j] = scA[wm0 + 16 * j + (lane & 15)];
-    }
+    static_for<0, FM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      alo[j] = ds_read16<j * 2048>(a_lo);
+      ahi[j] = ds_read16<j * 2048>(a_hi);
+      sa[j] = ds_read4f<j * 64>(sa_ad);
+    });
+    float sb = 0.f;
+    v4i sbv;
+    if (!kRowB) sb = ds_read4f<0>(sb_ad);
+    else sbv = ds_read16<0>(sb_ad);
+    v4i blo = ds_read16<0>(b_lo), bhi = ds_read16<0>(b_hi);
+    lds_wait<0>();
+    v8i af[FM];
     float prod[FM];
+    static_for<0, FM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      hold(alo[j]);
+      hold(ahi[j]);
+      hold(sa[j]);
+      af[j] = join(alo[j], ahi[j]);
+    });
+    hold(sb);
+    hold(sbv);
+    hold(blo);
+    hold(bhi);
     if (!kRowB) {
-      const float sb = scB[((n0 + wn0) >> 7) - nb0];
 #pragma unroll
       for (int j = 0; j < FM; ++j) prod[j] = sa[j] * sb;
     }
+    v4f pprev = v4f{0.f, 0.f, 0.f, 0.f};
+    v4i sbprev = sbv;
+    auto fold = [&](int i, int j, const v4f& pr, const v4i& sbw) __attribute__((always_inline)) {
+      if (kRowB) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const v8i bfr = load_frag(sm + OFF_B, wn0 + 16 * i, lane);
-      float4 sb4;
-      if (kRowB) sb4 = *reinterpret_cast<const float4*>(scB + wn0 + 16 * i + 4 * (lane >> 4));
+        for (int r = 0; r < 4; ++r)
+          acc[i][j][r] = __builtin_fmaf(pr[r], sa[j] * __int_as_float(sbw[r]), acc[i][j][r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], prod[j], acc[i][j][r]);
+      }
+    };
+    static_for<0, FN>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      v4i nlo, nhi, nsb;
+      if constexpr (i + 1 < FN) {
+        nlo = ds_read16<(i + 1) * 2048>(b_lo);
+        nhi = ds_read16<(i + 1) * 2048>(b_hi);
+        if (kRowB) nsb = ds_read16<(i + 1) * 64>(sb_ad);
+      }
+      const v8i bf = join(blo, bhi);
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const v4f pr = mfma_fp8(bfr, af[j], v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
+        const v4f pc = mfma_fp8(bf, af[j], v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
+        if (j > 0) fold(i, j - 1, pprev, sbv);
+        else if (i > 0) fold(i - 1, FM - 1, pprev, sbprev);
+        pprev = pc;
+      }
+      sbprev = sbv;
+      if constexpr (i + 1 < FN) {
+        __builtin_amdgcn_sched_barrier(0);   // this step's MFMAs stay ahead of the wait
+        lds_wait<0>();
+        hold(nlo);
+        hold(nhi);
+        blo = nlo;
+        bhi = nhi;
         if (kRowB) {
-          acc[i][j][0] = __builtin_fmaf(pr[0], sa[j] * sb4.x, acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(pr[1], sa[j] * sb4.y, acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(pr[2], sa[j] * sb4.z, acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(pr[3], sa[j] * sb4.w, acc[i][j][3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], prod[j], acc[i][j][r]);
+          hold(nsb);
+          sbv = nsb;
         }
       }
-    }
+    });
+    fold(FN - 1, FM - 1, pprev, sbprev);
   };
 
-  // K loop over pairs of blocks (stage 0 then stage 1) with a single exit, and a peeled
-  // last block when the count is odd.
-  issue(0, sm0);
+  // K loop. Each step: wait until this wave's copies into the current stage have landed,
+  // barrier (all waves' copies landed, and everyone is done reading the other stage),
+  // start copying K block kb+1 into the other stage, then compute on the current one.
+  const uint32_t st0 = lds_addr(sm0), st1 = lds_addr(sm1);
+  issue(0, st0);
   int kb = 0;
   for (; kb + 2 <= nkb; kb += 2) {
     wait_vmem();
     __syncthreads();
-    issue(kb + 1, sm1);
-    compute(sm0);
+    issue(kb + 1, st1);
+    compute(st0);
     wait_vmem();
     __syncthreads();
-    if (kb + 2 < nkb) issue(kb + 2, sm0);
-    compute(sm1);
+    issue(kb + 2, st0);
+    compute(st1);
   }
   if (kb < nkb) {
     wait_vmem();
     __syncthreads();
-    compute(sm0);
+    compute(st0);
   }
 
   // Epilogue: lane holds C[m][n .. n+3] of each 16x16 tile.

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_mx(GroupedParams p) {
   constexpr int OFF_B = BM * 128;
   constexpr int OFF_SA = OFF_B + BN * 128;
   constexpr int OFF_SB = OFF_SA + BM * 4;
-  constexpr int STAGE = OFF_SB + BN * 4;
+  constexpr int STAGE = OFF_SA + NT * 4;   // one 64-dword scale slot per wave (X, W, then unused)
   static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0 && NT >= BM + BN, "load split");
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
@@ -82,21 +82,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_mx(GroupedParams p) {
   const int nkc = (int)(K / 128);
 
   // Raw buffer descriptors end at the expert's last row / at N, so rows past them read as
-  // zero without a memory access (see the dense GEMM).
+  // zero without a memory access (see the dense GEMM); one per-lane offset per operand.
   constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;
+  static_assert((NT / 8) % 16 == 0, "swizzle phase must repeat across loads");
   const int64_t rows_a = min((int64_t)BM, row_end - m0), rows_b = min((int64_t)BN, N - n0);
-  uint32_t offA[LA], offB[LB];
-#pragma unroll
-  for (int it = 0; it < LA; ++it) {
-    const int Lc = it * NT + tid, r = Lc >> 3;
-    offA[it] = (uint32_t)(r * K) + (uint32_t)(swz(r, Lc & 7) << 4);
-  }
-#pragma unroll
-  for (int it = 0; it < LB; ++it) {
-    const int Lc = it * NT + tid, r = Lc >> 3;
-    offB[it] = (uint32_t)(r * K) + (uint32_t)(swz(r, Lc & 7) << 4);
-  }
+  const int lr = tid >> 3;
+  const uint32_t off0 = (uint32_t)(lr * K) + (uint32_t)(swz(lr, tid & 7) << 4);
   const uint32_t bytesA = (uint32_t)((rows_a - 1) * K + 128), bytesB = (uint32_t)((rows_b - 1) * K + 128);
+  // Scale dwords (4 E8M0 bytes of one row for one 128-wide K chunk): waves [0, BM/64)
+  // fetch X's, the next BN/64 waves W's, the rest issue an empty load into a spare slot.
   const bool sa_wave = wave < BM / 64;
   const bool sb_wave = !sa_wave && wave < (BM + BN) / 64;
   const uint8_t* baseS;
@@ -108,18 +102,25 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_mx(GroupedParams p) {
   } else {
     baseS = Wsb + n0 * (K / 32);
     offS = (uint32_t)(((wave - BM / 64) * 64 + lane) * (K / 32));
-    bytesS = (uint32_t)((rows_b - 1) * (K / 32) + 4);
+    bytesS = sb_wave ? (uint32_t)((rows_b - 1) * (K / 32) + 4) : 0u;
   }
-  const int s_lds = sa_wave ? OFF_SA + wave * 256 : OFF_SB + (wave - BM / 64) * 256;
 
-  auto issue = [&](int kc, uint8_t* sm) {
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.X + m0 * K + kc * 128, bytesA);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Wb + n0 * K + kc * 128, bytesB);
+  auto issue = [&](int kc, uint32_t st) __attribute__((always_inline)) {
+    const bool live = kc < nkc;
+    const int kcc = live ? kc : 0;
 #pragma unroll
-    for (int it = 0; it < LA; ++it) buf2lds16(ra, offA[it], sm + (it * NT + wave * 64) * 16);
+    for (int it = 0; it < LA; ++it) {
+      const int64_t r0 = (int64_t)it * (NT / 8);
+      const uint32_t nb = (live && bytesA > r0 * K) ? (uint32_t)(bytesA - r0 * K) : 0u;
+      dma16(make_rsrc(p.X + (m0 + r0) * K + kcc * 128, nb), off0, st + (it * NT + wave * 64) * 16);
+    }
 #pragma unroll
-    for (int it = 0; it < LB; ++it) buf2lds16(rb, offB[it], sm + OFF_B + (it * NT + wave * 64) * 16);
-    if (sa_wave || sb_wave) buf2lds4(make_rsrc(baseS + kc * 4, bytesS), offS, sm + s_lds);
+    for (int it = 0; it < LB; ++it) {
+      const int64_t r0 = (int64_t)it * (NT / 8);
+      const uint32_t nb = (live && bytesB > r0 * K) ? (uint32_t)(bytesB - r0 * K) : 0u;
+      dma16(make_rsrc(Wb + (n0 + r0) * K + kcc * 128, nb), off0, st + OFF_B + (it * NT + wave * 64) * 16);
+    }
+    dma4(make_rsrc(baseS + kcc * 4, live ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
   };
 
   v4f acc[FN][FM];
@@ -128,44 +129,83 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_mx(GroupedParams p) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int bsh = 8 * (lane >> 4);  // this lane supplies the scale of K block (lane >> 4)
-  auto compute = [&](const uint8_t* sm) {
-    const uint32_t* scA = reinterpret_cast<const uint32_t*>(sm + OFF_SA);
-    const uint32_t* scB = reinterpret_cast<const uint32_t*>(sm + OFF_SB);
+  const FragOffsets fa = frag_offsets(wm0, lane), fb = frag_offsets(wn0, lane);
+  const uint32_t o_sa = OFF_SA + (wm0 + (lane & 15)) * 4, o_sb = OFF_SB + (wn0 + (lane & 15)) * 4;
+  const int bsh = 8 * (lane >> 4);  // this lane supplies the scale of 32-wide K block (lane >> 4)
+
+  // One 128-wide K chunk: A fragments and their scale bytes stay in registers, B fragments
+  // are double-buffered; the scaled MFMA accumulates directly (no VALU rescale).
+  auto compute = [&](uint32_t st) __attribute__((always_inline)) {
+    const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi;
+    const uint32_t b_lo = st + OFF_B + fb.lo, b_hi = st + OFF_B + fb.hi;
+    const uint32_t sa_ad = st + o_sa, sb_ad = st + o_sb;
+    v4i alo[FM], ahi[FM];
+    float uaf[FM];
+    static_for<0, FM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      alo[j] = ds_read16<j * 2048>(a_lo);
+      ahi[j] = ds_read16<j * 2048>(a_hi);
+      uaf[j] = ds_read4f<j * 64>(sa_ad);
+    });
+    v4i blo = ds_read16<0>(b_lo), bhi = ds_read16<0>(b_hi);
+    float ubf = ds_read4f<0>(sb_ad);
+    lds_wait<0>();
     v8i af[FM];
     int ua[FM];
+    static_for<0, FM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      hold(alo[j]);
+      hold(ahi[j]);
+      hold(uaf[j]);
+      af[j] = join(alo[j], ahi[j]);
+      ua[j] = (int)(__float_as_uint(uaf[j]) >> bsh);
+    });
+    hold(blo);
+    hold(bhi);
+    hold(ubf);
+    static_for<0, FN>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      v4i nlo, nhi;
+      float nub;
+      if constexpr (i + 1 < FN) {
+        nlo = ds_read16<(i + 1) * 2048>(b_lo);
+        nhi = ds_read16<(i + 1) * 2048>(b_hi);
+        nub = ds_read4f<(i + 1) * 64>(sb_ad);
+      }
+      const v8i bf = join(blo, bhi);
+      const int ub = (int)(__float_as_uint(ubf) >> bsh);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      af[j] = load_frag(sm, wm0 + 16 * j, lane);
-      ua[j] = (int)(scA[wm0 + 16 * j + (lane & 15)] >> bsh);
-    }
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const v8i bfr = load_frag(sm + OFF_B, wn0 + 16 * i, lane);
-      const int ub = (int)(scB[wn0 + 16 * i + (lane & 15)] >> bsh);
-#pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_fp8(bfr, af[j], acc[i][j], ub, ua[j]);
-    }
+      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_fp8(bf, af[j], acc[i][j], ub, ua[j]);
+      if constexpr (i + 1 < FN) {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait<0>();
+        hold(nlo);
+        hold(nhi);
+        hold(nub);
+        blo = nlo;
+        bhi = nhi;
+        ubf = nub;
+      }
+    });
   };
 
-  // K loop over pairs of blocks (stage 0 then stage 1) with a single exit, and a peeled
-  // last block when the count is odd.
-  issue(0, sm0);
+  const uint32_t st0 = lds_addr(sm0), st1 = lds_addr(sm1);
+  issue(0, st0);
   int kc = 0;
   for (; kc + 2 <= nkc; kc += 2) {
     wait_vmem();
     __syncthreads();
-    issue(kc + 1, sm1);
-    compute(sm0);
+    issue(kc + 1, st1);
+    compute(st0);
     wait_vmem();
     __syncthreads();
-    if (kc + 2 < nkc) issue(kc + 2, sm0);
-    compute(sm1);
+    issue(kc + 2, st0);
+    compute(st1);
   }
   if (kc < nkc) {
     wait_vmem();
     __syncthreads();
-    compute(sm0);
+    compute(st0);
   }
 
 #pragma unroll
