@@ -117,6 +117,13 @@ __device__ __forceinline__ void dma4(v4i rsrc, uint32_t voff, uint32_t lds) {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding (they
+// complete in issue order, so this waits for all but the N most recent).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
 
 // Swizzled LDS layout for 128-byte rows of FP8 (one 128-wide K block per row): the 16-byte
 // chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7). With 64 banks of 4 bytes,

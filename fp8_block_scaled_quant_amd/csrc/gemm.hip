@@ -10,7 +10,7 @@
 // * One v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0 scales) consumes exactly one
 //   128-wide K block of a 16x16 output tile, starting from a zero accumulator. Its fp32
 //   partial is then folded into the running sum with one FMA per output:
-//   acc += P * (sA * sB).
+//   acc += P * (sA * sB), kLag MFMAs later so the wave does not wait on the result.
 // * Tiles are computed transposed (MFMA first operand = B rows n, second = A rows m), so
 //   the 4 outputs a lane holds share one m and four consecutive n inside one 128-row
 //   block of B: one scale product per lane per K block for the forward/DGrad recipe.
@@ -30,6 +30,9 @@
 
 namespace fp8rl {
 
+// Distance, in MFMA tiles, between an MFMA and the FMAs that fold its result.
+constexpr int kLag = 3;
+
 template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) {
   constexpr int NT = WM * WN * 64;
@@ -45,6 +48,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   static_assert(NT >= BM + NSB, "one scale load per wave");
   static_assert(OFF_SB + NSB * 4 <= STAGE, "scale slots");
   static_assert(kRowB || TN <= 128, "a wave's n range must sit inside one 128-row scale block");
+  static_assert(kLag < FM, "a folded tile is at most one B fragment behind");
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
 
@@ -176,7 +180,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
 #pragma unroll
       for (int j = 0; j < FM; ++j) prod[j] = sa[j] * sb;
     }
-    v4f pprev = v4f{0.f, 0.f, 0.f, 0.f};
+    // Tiles run in the order t = i * FM + j; the FMAs that fold tile t - kLag into the
+    // accumulators follow the MFMA of tile t, so the wave never stalls on a fresh MFMA
+    // result. `pipe` holds the kLag + 1 most recent MFMA results.
+    v4f pipe[kLag + 1];
     v4i sbprev = sbv;
     auto fold = [&](int i, int j, const v4f& pr, const v4i& sbw) __attribute__((always_inline)) {
       if (kRowB) {
@@ -199,10 +206,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
       const v8i bf = join(blo, bhi);
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const v4f pc = mfma_fp8(bf, af[j], v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
-        if (j > 0) fold(i, j - 1, pprev, sbv);
-        else if (i > 0) fold(i - 1, FM - 1, pprev, sbprev);
-        pprev = pc;
+        const int t = i * FM + j;
+        pipe[t % (kLag + 1)] = mfma_fp8(bf, af[j], v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
+        if (t >= kLag) {
+          const int u = t - kLag;
+          fold(u / FM, u % FM, pipe[u % (kLag + 1)], (u / FM == i) ? sbv : sbprev);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the MFMA / fold interleave as written
       }
       sbprev = sbv;
       if constexpr (i + 1 < FN) {
@@ -218,7 +228,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
         }
       }
     });
-    fold(FN - 1, FM - 1, pprev, sbprev);
+#pragma unroll
+    for (int u = FN * FM - kLag; u < FN * FM; ++u) fold(u / FM, u % FM, pipe[u % (kLag + 1)], sbprev);
   };
 
   // K loop. Each step: wait until this wave's copies into the current stage have landed,
