@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|decode|backward|moe]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload dense|decode|backward|moe|install] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
 HBM. The default workload is the dense layer shaped like a ~9B model's MLP
@@ -16,13 +16,20 @@ quantizers). `roofline` reports the dominant kernel (the gate/up GEMM) from HIP 
 recorded on the stream the library launches on, against the 5.0 PFLOP/s dense FP8 MFMA
 peak; `quant_roofline` the X quantizer against 8 TB/s HBM.
 
-Other workloads (--workload) time the decode, backward and MoE paths the same way.
+Other workloads (--workload) time the decode, backward, MoE and weight-install paths the
+same way. HBM-bound workloads (decode, install) cycle through copies of their inputs that
+together exceed 1 GiB, so the 256 MB last-level cache cannot serve a launch from the previous
+one. `roofline.traffic` is the dominant kernel's HBM bytes per launch from rocprofv3
+FETCH_SIZE + WRITE_SIZE counter runs (scaled by what the same counters read for the install
+copy of known size); it is reported only while the kernel's sources hash to the ones the
+counters were taken on, else null.
 Prints ONE JSON line on stdout.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +44,49 @@ if ROOT not in sys.path:
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% of FP8 MFMA peak); quantizer GB/s (% of HBM)"
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+ROTATE_BYTES = 1 << 30          # HBM-bound inputs cycle through at least this many bytes
+
+CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
+
+# HBM bytes per launch of each workload's dominant kernel, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs of this script, each scaled by the ratio of known bytes to counted bytes of the
+# install copy. Keyed by the sha256 of the kernel's sources at the time of the counter runs.
+# FETCH_SIZE counts half the bytes the install copy reads (factor 1.999); WRITE_SIZE counts them
+# exactly (factor 1.000). Both count L2 <-> fabric transfers, so lines served by the 256 MB
+# last-level cache are included.
+MEASURED_TRAFFIC = {
+    "gemm_gu": {"sha": "19dbec339ced1c21", "gb": 1.6292},        # read 1.2262 + write 0.4030
+    "dgrad": {"sha": "19dbec339ced1c21", "gb": 1.3010},          # read 1.2338 + write 0.0671
+    "decode_n24576": {"sha": "33c3cfbbc2f3d590", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
+    "grouped_gu": {"sha": "25fb882b1212ec97", "gb": 0.7667},     # read 0.6996 + write 0.0671
+    "install_gu": {"sha": "75a15a79b467f5c4", "gb": 0.2014},     # read 0.1007 + write 0.1007
+}
+
+
+def _sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gemm_gu": ("gemm.hip", "device.hpp", "internal.hpp"),
+    "dgrad": ("gemm.hip", "device.hpp", "internal.hpp"),
+    "decode_n24576": ("gemm.hip", "quant.hip", "device.hpp", "internal.hpp"),
+    "grouped_gu": ("grouped.hip", "device.hpp", "internal.hpp"),
+    "install_gu": ("install.hip", "device.hpp", "internal.hpp"),
+}
+
+
+def _traffic(kernel):
+    """(GB per launch, sources sha) if the counters were taken on the current sources, else (None, sha)."""
+    sha = _sources_sha(KERNEL_SOURCES[kernel]) if kernel in KERNEL_SOURCES else None
+    rec = MEASURED_TRAFFIC.get(kernel)
+    if rec is not None and rec["sha"] == sha:
+        return rec["gb"], sha
+    return None, sha
 
 
 def _args():
@@ -44,7 +94,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "decode", "backward", "moe"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "decode", "backward", "moe", "install"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -130,26 +180,35 @@ def decode_setup(torch, F, W, dev):
     d = W.decode_rollout()
     x = W.to_bf16_tensor(d["x"]).to(dev)
     M, K = x.shape
-    mats = {}
+    set_bytes = sum(n * K + (n // 128) * (K // 128) * 4 for n in W.DECODE_N)
+    n_sets = -(-ROTATE_BYTES // set_bytes)
+    sets = [dict() for _ in range(n_sets)]
+    ys = {}
     for n in W.DECODE_N:
         wq, sw, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d[f"w{n}"]).to(dev))
-        # installed (rollout-owned) copies
-        iq, is_ = torch.empty_like(wq), torch.empty_like(sw)
-        F.fp8_weight_install(wq, sw, iq, is_)
-        mats[n] = (iq, is_, torch.empty((M, n), dtype=torch.bfloat16, device=dev))
+        for st in sets:     # installed (rollout-owned) copies, identical bytes
+            iq, is_ = torch.empty_like(wq), torch.empty_like(sw)
+            F.fp8_weight_install(wq, sw, iq, is_)
+            st[n] = (iq, is_)
+        ys[n] = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        del wq, sw
     ws = torch.empty(F.fp8rl_fwd_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
     timers = {f"decode_n{n}": EventTimer(torch) for n in W.DECODE_N}
+    it = [0]
 
     def step(timed):
-        for n, (iq, is_, y) in mats.items():
+        st = sets[it[0] % n_sets]
+        it[0] += 1
+        for n, (iq, is_) in st.items():
             if timed: timers[f"decode_n{n}"].start()
-            F.fp8_gemm_blockscaled_fwd(wq=iq, sw=is_, x_bf16=x, y=y, workspace=ws)
+            F.fp8_gemm_blockscaled_fwd(wq=iq, sw=is_, x_bf16=x, y=ys[n], workspace=ws)
             if timed: timers[f"decode_n{n}"].stop()
 
     nmax = max(W.DECODE_N)
     info = dict(
         config={"workload": "decode_rollout", "rows_M": M, "K": K, "N": list(W.DECODE_N),
-                "activations": "bf16, quantized 1x128 inside the call", "weights": "installed E4M3 128x128"},
+                "activations": "bf16, quantized 1x128 inside the call", "weights": "installed E4M3 128x128",
+                "weight_copies": n_sets},
         flops=sum(2.0 * M * n * K for n in W.DECODE_N),
         dominant=(f"decode_n{nmax}", "hbm", (nmax * K + nmax * K // 128 // 128 * 4) / 1e9, "GB/s", PEAK_HBM_GBS,
                   "weight stream: E4M3 payload + fp32 block scales per launch"),
@@ -237,6 +296,48 @@ def moe_setup(torch, F, W, dev):
     return step, timers, info
 
 
+def install_setup(torch, F, W, dev):
+    """Weight install of the dense layer's gate/up and down weights (payload + fp32 block scales),
+    the rollout side's whole per-sync work for that layer. A plain copy of known size, so its
+    counter readings also calibrate the FETCH_SIZE / WRITE_SIZE figures of the other kernels."""
+    d = W.dense_forward(with_down=True)
+    srcs = []
+    for k in ("w_gu", "w_dn"):
+        wq, sw, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d[k]).to(dev))
+        srcs.append((wq, sw))
+    del d
+    per_set = sum(q.numel() + s_.numel() * 4 for q, s_ in srcs)
+    n_sets = -(-ROTATE_BYTES // (2 * per_set))
+    pairs = []
+    for _ in range(n_sets):
+        pairs.append([(q.clone(), s_.clone(), torch.empty_like(q), torch.empty_like(s_)) for q, s_ in srcs])
+    del srcs
+    names = ("install_gu", "install_dn")
+    timers = {k: EventTimer(torch) for k in names}
+    it = [0]
+
+    def step(timed):
+        ps = pairs[it[0] % n_sets]
+        it[0] += 1
+        for k, (sq, ss, dq, ds) in zip(names, ps):
+            if timed: timers[k].start()
+            F.fp8_weight_install(sq, ss, dq, ds)
+            if timed: timers[k].stop()
+
+    gu_bytes = 2 * (pairs[0][0][0].numel() + pairs[0][0][1].numel() * 4)
+    info = dict(
+        config={"workload": "weight_install_dense_layer_9b", "tensors": ["gate_up 24576x4096", "down 4096x12288"],
+                "recipe": "blockwise 128x128, E4M3 payload + fp32 scales", "copies": n_sets},
+        flops=None,
+        bytes=2 * per_set,
+        dominant=("install_gu", "hbm", gu_bytes / 1e9, "GB/s", PEAK_HBM_GBS,
+                  f"read + write of the gate/up payload and scales = {gu_bytes} B per launch"),
+        quant=None,
+        gemm_keys=(),
+    )
+    return step, timers, info
+
+
 # ---------------------------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample of the same workload
 # ---------------------------------------------------------------------------------------------
@@ -299,7 +400,8 @@ def main():
 
     dev = torch.device("cuda", 0)
     F.load_library()
-    setup = {"dense": dense_setup, "decode": decode_setup, "backward": backward_setup, "moe": moe_setup}[a.workload]
+    setup = {"dense": dense_setup, "decode": decode_setup, "backward": backward_setup, "moe": moe_setup,
+             "install": install_setup}[a.workload]
     step, timers, info = setup(torch, F, W, dev)
 
     for _ in range(a.warmup):
@@ -317,10 +419,15 @@ def main():
     dom_ms = timers[name].mean_ms()
     achieved = per_launch / (dom_ms * 1e-3)
     gemm_ms = sum(timers[k].mean_ms() for k in info["gemm_keys"])
+    traffic, sha = _traffic(name)
+    if info["flops"] is not None:
+        value, vunit = round(info["flops"] / (ms_per_step * 1e-3) / 1e12, 2), "TFLOP/s"
+    else:
+        value, vunit = round(info["bytes"] / (ms_per_step * 1e-3) / 1e9, 1), "GB/s"
     out = {
         "metric": METRIC,
-        "value": round(info["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": vunit,
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
@@ -332,17 +439,19 @@ def main():
         "data": "synthetic",
         "config": info["config"],
         "roofline": {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None, "per_launch": per_unit},
-        "gemm_tflops": round(info["flops"] / (gemm_ms * 1e-3) / 1e12, 2),
+                     "frac": round(achieved / peak, 4), "traffic": traffic, "traffic_unit": "GB per launch (HBM)",
+                     "sources_sha": sha, "per_launch": per_unit},
         "kernel_us": breakdown,
     }
+    if info["gemm_keys"]:
+        out["gemm_tflops"] = round(info["flops"] / (gemm_ms * 1e-3) / 1e12, 2)
     if info["quant"] is not None:
         qname, qgb, qdesc = info["quant"]
         qms = timers[qname].mean_ms()
         out["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
                                  "per_launch": qdesc}
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and a.workload != "install":
         out["cpu_baseline"] = cpu_baseline(a.workload)
     print(json.dumps(out))
 
