@@ -42,113 +42,119 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------------
-// 128 x 128 tile kernel, 256 threads.
+// 128 x 128 tile kernel, 512 threads (8 waves), one tile per workgroup.
 //   kBlock = false: activation mode. Row output = 1x128 groups (q [R][C], s [R][C/128]),
 //                   column output = 128x1 groups written transposed (qt [C][R], st [C][R/128]).
 //   kBlock = true : weight mode. One scale for the whole 128x128 block (s [R/128][C/128]);
 //                   qt, if requested, is the byte transpose of q (same scale, same bytes).
-// Grid: one workgroup per tile, blockIdx.x = rb * (C/128) + cb.
-// Thread t loads row t/2, columns (t%2)*64 .. +64 (8 x 16-byte loads). For the column pass
-// the tile goes through LDS; wave w then reads rows 32w .. 32w+31 of the column pair
-// (2l, 2l+1) held in 32-bit word l (conflict-free: a wave reads 64 consecutive words).
+// Grid: blockIdx.x = rb * (C/128) + cb.
+// Thread t owns the 4x8 sub-block rows 4*(t/16) .. +3, columns 8*(t%16) .. +7. Each wave
+// load instruction then reads 4 whole 256-byte row segments, and each row-output store
+// writes whole 128-byte lines. Row amax: max over the 16 lanes sharing a row.
+// Column pass: each thread transposes its sub-block in registers (byte permutes) into a
+// column-major LDS tile, [column][128 rows of bf16], whose 16-byte chunks (8 rows) are
+// XOR-swizzled by column/8 so that neither the writes nor the reads conflict. Eight lanes
+// then own one column (16 rows each): column amax over those 8 lanes, and each store
+// instruction writes 8 whole 128-byte lines of qt.
 // ---------------------------------------------------------------------------------------
 template <bool kBlock>
-__global__ __launch_bounds__(256) void k_quant_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+__global__ __launch_bounds__(512) void k_quant_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                     uint8_t* __restrict__ q, float* __restrict__ s,
                                                     uint8_t* __restrict__ qt, float* __restrict__ st) {
-  constexpr int LDW = 68;  // LDS row stride in words (64 + 4 keeps 16-byte row writes conflict-free)
-  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * LDW];
-  __shared__ float red[4 * 128];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];   // [column][row pair]
+  __shared__ float red[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid & 15, rg = tid >> 4;                               // rg: 0..31
   const int64_t ncb = C / 128;
   const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
-  const int r = tid >> 1, h = tid & 1;
   const bool want_rows = q != nullptr, want_cols = qt != nullptr;
 
-  const uint4* src = reinterpret_cast<const uint4*>(x + (rb * 128 + r) * C + cb * 128 + h * 64);
-  uint4 v[8];
+  const uint16_t* src = x + (rb * 128 + 4 * rg) * C + cb * 128 + c * 8;
+  uint4 v[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = src[i];
+  for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(src + (int64_t)i * C);
 
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    amax = fmaxf(amax, fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w))));
-
-  BlockScale row_bs;
+  double rblk = 0.0;
   if (kBlock) {
+    float a = 0.0f;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    if (lane == 0) red[wave] = amax;
+    for (int i = 0; i < 4; ++i)
+      a = fmaxf(a, fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w))));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if (lane == 0) red[wave] = a;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    row_bs = block_scale(amax);
-    if (tid == 0) s[rb * (C / 128) + cb] = row_bs.s;
-  } else {
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    row_bs = block_scale(amax);
-    if (want_rows && h == 0) s[(rb * 128 + r) * (C / 128) + cb] = row_bs.s;
-  }
-
-  if (want_rows) {
-    uint4* dst = reinterpret_cast<uint4*>(q + (rb * 128 + r) * C + cb * 128 + h * 64);
+    a = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+    const BlockScale bs = block_scale(a);
+    if (tid == 0) s[rb * ncb + cb] = bs.s;
+    rblk = bs.r;
+    if (want_rows) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
+            quant8(v[i].x, v[i].y, v[i].z, v[i].w, rblk);
+    }
+  } else if (want_rows) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint2 lo = quant8(v[2 * i].x, v[2 * i].y, v[2 * i].z, v[2 * i].w, row_bs.r);
-      const uint2 hi = quant8(v[2 * i + 1].x, v[2 * i + 1].y, v[2 * i + 1].z, v[2 * i + 1].w, row_bs.r);
-      dst[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      float a = fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w)));
+      a = fmaxf(a, __shfl_xor(a, 1));
+      a = fmaxf(a, __shfl_xor(a, 2));
+      a = fmaxf(a, __shfl_xor(a, 4));
+      a = fmaxf(a, __shfl_xor(a, 8));
+      const BlockScale bs = block_scale(a);
+      if (c == 0) s[(rb * 128 + 4 * rg + i) * ncb + cb] = bs.s;
+      *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
+          quant8(v[i].x, v[i].y, v[i].z, v[i].w, bs.r);
     }
   }
   if (!want_cols) return;
 
-  uint4* trow = reinterpret_cast<uint4*>(tile + r * LDW + h * 32);
+  // Column 8c+j, rows 4rg..4rg+3 = 8 bytes: half (rg & 1) of the 16-byte chunk rg >> 1,
+  // stored at chunk position (rg >> 1) ^ c.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) trow[i] = v[i];
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;   // high or low bf16 of each word
+    const int p = j >> 1;
+    const uint32_t a0 = p == 0 ? v[0].x : p == 1 ? v[0].y : p == 2 ? v[0].z : v[0].w;
+    const uint32_t a1 = p == 0 ? v[1].x : p == 1 ? v[1].y : p == 2 ? v[1].z : v[1].w;
+    const uint32_t a2 = p == 0 ? v[2].x : p == 1 ? v[2].y : p == 2 ? v[2].z : v[2].w;
+    const uint32_t a3 = p == 0 ? v[3].x : p == 1 ? v[3].y : p == 2 ? v[3].z : v[3].w;
+    *reinterpret_cast<uint2*>(tile + (8 * c + j) * 64 + (((rg >> 1) ^ c) & 15) * 4 + (rg & 1) * 2) =
+        make_uint2(__builtin_amdgcn_perm(a1, a0, sel), __builtin_amdgcn_perm(a3, a2, sel));
+  }
   __syncthreads();
 
-  uint32_t col[32];
+  // Wave w: columns 16w .. 16w+15, 8 per round; lane: column +lane/8, rows 16k .. 16k+15.
+  // The two chunks are read in an order (odd first for half the lanes) that keeps every
+  // group of 8 or 16 lanes on distinct banks.
+  const int k = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) col[i] = tile[(32 * wave + i) * LDW + lane];
-
-  double r0, r1;
-  if (kBlock) {
-    r0 = r1 = row_bs.r;
-  } else {
-    float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      m0 = fmaxf(m0, fabsf(bf16_lo(col[i])));
-      m1 = fmaxf(m1, fabsf(bf16_hi(col[i])));
+  for (int rd = 0; rd < 2; ++rd) {
+    const int col = 16 * wave + 8 * rd + (lane >> 3);
+    const int sw = (2 * wave + rd) & 15;                            // = (col / 8) & 15
+    const int a = 2 * k + ((k >> 2) ^ (col & 1));
+    const uint4 A = *reinterpret_cast<const uint4*>(tile + col * 64 + ((a ^ sw) * 4));
+    const uint4 B = *reinterpret_cast<const uint4*>(tile + col * 64 + (((a ^ 1) ^ sw) * 4));
+    const bool even = (a & 1) == 0;
+    const uint4 lo = even ? A : B, hi = even ? B : A;               // rows 16k..+7, 16k+8..+15
+    double r;
+    if (kBlock) {
+      r = rblk;
+    } else {
+      float m = fmaxf(fmaxf(fmaxf(absmax2(lo.x), absmax2(lo.y)), fmaxf(absmax2(lo.z), absmax2(lo.w))),
+                      fmaxf(fmaxf(absmax2(hi.x), absmax2(hi.y)), fmaxf(absmax2(hi.z), absmax2(hi.w))));
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      const BlockScale bs = block_scale(m);
+      r = bs.r;
+      if (k == 0) st[(cb * 128 + col) * (R / 128) + rb] = bs.s;
     }
-    red[wave * 128 + 2 * lane] = m0;
-    red[wave * 128 + 2 * lane + 1] = m1;
-    __syncthreads();
-    m0 = fmaxf(fmaxf(red[2 * lane], red[128 + 2 * lane]), fmaxf(red[256 + 2 * lane], red[384 + 2 * lane]));
-    m1 = fmaxf(fmaxf(red[2 * lane + 1], red[128 + 2 * lane + 1]),
-               fmaxf(red[256 + 2 * lane + 1], red[384 + 2 * lane + 1]));
-    const BlockScale b0 = block_scale(m0), b1 = block_scale(m1);
-    r0 = b0.r;
-    r1 = b1.r;
-    if (wave == 0) {
-      st[(cb * 128 + 2 * lane) * (R / 128) + rb] = b0.s;
-      st[(cb * 128 + 2 * lane + 1) * (R / 128) + rb] = b1.s;
-    }
+    const uint2 o0 = quant8(lo.x, lo.y, lo.z, lo.w, r);
+    const uint2 o1 = quant8(hi.x, hi.y, hi.z, hi.w, r);
+    *reinterpret_cast<uint4*>(qt + (cb * 128 + col) * R + rb * 128 + 16 * k) = make_uint4(o0.x, o0.y, o1.x, o1.y);
   }
-  // column c = 2*lane (low halves) and 2*lane+1 (high halves), rows 32*wave .. +31
-  uint32_t o0[8], o1[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    o0[i] = pack4_e4m3(scaled(bf16_lo(col[4 * i]), r0), scaled(bf16_lo(col[4 * i + 1]), r0),
-                       scaled(bf16_lo(col[4 * i + 2]), r0), scaled(bf16_lo(col[4 * i + 3]), r0));
-    o1[i] = pack4_e4m3(scaled(bf16_hi(col[4 * i]), r1), scaled(bf16_hi(col[4 * i + 1]), r1),
-                       scaled(bf16_hi(col[4 * i + 2]), r1), scaled(bf16_hi(col[4 * i + 3]), r1));
-  }
-  uint4* d0 = reinterpret_cast<uint4*>(qt + (cb * 128 + 2 * lane) * R + rb * 128 + 32 * wave);
-  uint4* d1 = reinterpret_cast<uint4*>(qt + (cb * 128 + 2 * lane + 1) * R + rb * 128 + 32 * wave);
-  d0[0] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-  d0[1] = make_uint4(o0[4], o0[5], o0[6], o0[7]);
-  d1[0] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-  d1[1] = make_uint4(o1[4], o1[5], o1[6], o1[7]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -200,14 +206,14 @@ hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint
 
 hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                  float* st, hipStream_t stream) {
-  hipLaunchKernelGGL(k_quant_tile<false>, dim3((unsigned)((K / 128) * (M / 128))), dim3(256), 0, stream, x, M, K,
+  hipLaunchKernelGGL(k_quant_tile<false>, dim3((unsigned)((K / 128) * (M / 128))), dim3(512), 0, stream, x, M, K,
                      q, s, qt, st);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                   hipStream_t stream) {
-  hipLaunchKernelGGL(k_quant_tile<true>, dim3((unsigned)((K / 128) * (N / 128))), dim3(256), 0, stream, w, N, K,
+  hipLaunchKernelGGL(k_quant_tile<true>, dim3((unsigned)((K / 128) * (N / 128))), dim3(512), 0, stream, w, N, K,
                      q, s, qt, (float*)nullptr);
   return hipGetLastError();
 }
