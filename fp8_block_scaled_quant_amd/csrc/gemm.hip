@@ -295,9 +295,11 @@ static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) 
   return hipGetLastError();
 }
 
-// Tile choice: 256x256 tiles (8 waves, 64x128 per wave) when there are enough of them to
-// fill the 256 CUs; 128x128 tiles (4 waves, 64x64 per wave) otherwise.
+// Tile choice: at most 256 rows with block-scaled B go to the few-row kernel (skinny.hip);
+// otherwise 256x256 tiles (8 waves, 64x128 per wave) when there are enough of them to fill
+// the 256 CUs, else 128x128 tiles (4 waves, 64x64 per wave).
 hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, hipStream_t stream) {
+  if (!row_scale_b && p.M <= 256) return launch_gemm_skinny(p, f32, stream);
   const int64_t big_tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   const bool big = big_tiles >= 256;
   if (row_scale_b) {

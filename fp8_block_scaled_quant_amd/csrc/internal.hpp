@@ -30,6 +30,8 @@ struct GemmParams {
   int accumulate;
 };
 hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, hipStream_t stream);
+// Few-row form (M <= 256, block-scaled B only): all rows per workgroup, one workgroup per CU.
+hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream);
 
 struct GroupedParams {
   const uint8_t* X;     // [T][K]

@@ -160,6 +160,24 @@ def test_fwd_decodes_every_e4m3_code():
     assert np.all(got[~finite] == 0)
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 8320, 256), (100, 4224, 384), (256, 12416, 128), (64, 16640, 256),
+                                   (33, 24704, 128)])
+def test_fwd_few_rows(M, N, K):
+    """M <= 256 runs the few-row kernel, whose workgroups each take a run of 16-row weight
+    fragments. These N give 2, 3, 4, 6 and 8 fragments per workgroup; 8320 and 16640 leave
+    a last workgroup with fewer fragments, and runs straddle 128-row scale blocks."""
+    x, w = _quantized_pair(M, N, K, 5500 + M)
+    xq, sx, _, _ = F.fp8_quant_act_1x128(bf16_dev(x))
+    wq, sw, _ = F.fp8_quant_w_128x128(bf16_dev(w))
+    y32 = F.fp8_gemm_blockscaled_fwd(xq, sx, wq, sw, out_dtype=torch.float32)
+    y16 = F.fp8_gemm_blockscaled_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16)
+    rxq, rsx = OQ.quant_act_1x128(x)
+    rwq, rsw = OQ.quant_w_128x128(w)
+    ref = OG.gemm_fwd(rxq, rsx, rwq, rsw)
+    assert_gemm_close(host(y32), ref, "few-row fwd f32")
+    assert_bf16_consistent(y16, y32, ref, "few-row fwd bf16")
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 4096, 512), (200, 1024, 384)])
 def test_fwd_bf16_input_matches_two_step(M, N, K):
     x, w = _quantized_pair(M, N, K, 6000 + M)
@@ -175,7 +193,7 @@ def test_fwd_bf16_input_matches_two_step(M, N, K):
     assert_gemm_close(host(fused), OG.gemm_fwd(rxq, rsx, rwq, rsw), "fused fwd")
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 512, 384), (130, 256, 640), (1, 128, 128)])
+@pytest.mark.parametrize("M,N,K", [(256, 512, 384), (130, 256, 640), (1, 128, 128), (200, 256, 8320)])
 def test_dgrad(M, N, K):
     dy = _rand((M, N), 7000 + M, 1e-3)
     w = _rand((N, K), 7001 + M, 0.02)
