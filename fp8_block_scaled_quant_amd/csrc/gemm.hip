@@ -254,32 +254,82 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     compute(st0);
   }
 
-  // Epilogue: lane holds C[m][n .. n+3] of each 16x16 tile.
+  // Epilogue. The tile goes out through LDS (the stages are free after the K loop), so that
+  // every global store instruction writes whole 128-byte lines instead of 16-byte (fp32) or
+  // 8-byte (bf16) pieces of 16 rows; lane l holds C[m][n .. n+3] of each 16x16 tile.
+  // fp32: one wave row (TM rows) at a time, read back and added to when accumulating.
+  // bf16: the whole tile at once, rows [0, BM/2) in sm0 and the rest in sm1.
+  wait_vmem();  // the empty copy issued past the last K block still writes (zeros) to a stage
+  if constexpr (kF32) {
+    constexpr int ROWF = BN * 4 + 16;                // staged row stride in bytes
+    constexpr int CPR = BN * 4 / 16;                 // 16-byte chunks per row
+    constexpr int RPP = NT / CPR;                    // rows per pass
+    static_assert(TM * ROWF <= STAGE && NT % CPR == 0 && TM % RPP == 0, "fp32 staging");
+    const int cr = tid / CPR, cc = tid % CPR;
+    const int64_t n = n0 + cc * 4;
 #pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int64_t m = m0 + wm0 + 16 * j + (lane & 15);
-    if (m >= M) continue;
+    for (int q = 0; q < WM; ++q) {
+      uint8_t* buf = (q & 1) ? sm1 : sm0;
+      __syncthreads();                               // the stage is free (K loop / previous chunk)
+      if (wave % WM == q) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int64_t n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
-      if (n >= N) continue;
-      if (kF32) {
-        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + m * p.ldc + n);
-        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (p.accumulate) {
-          const float4 o = *dst;
-          v.x += o.x;
-          v.y += o.y;
-          v.z += o.z;
-          v.w += o.w;
+        for (int j = 0; j < FM; ++j) {
+          uint8_t* rowp = buf + (16 * j + (lane & 15)) * ROWF;
+#pragma unroll
+          for (int i = 0; i < FN; ++i)
+            *reinterpret_cast<float4*>(rowp + (wn0 + 16 * i + 4 * (lane >> 4)) * 4) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
-        *dst = v;
-      } else {
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r0 = 0; r0 < TM; r0 += RPP) {
+        const int r = r0 + cr;
+        const int64_t m = m0 + q * TM + r;
+        float4 v = *reinterpret_cast<const float4*>(buf + r * ROWF + cc * 16);
+        if (m < M && n < N) {
+          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + m * p.ldc + n);
+          if (p.accumulate) {
+            const float4 o = *dst;
+            v.x += o.x;
+            v.y += o.y;
+            v.z += o.z;
+            v.w += o.w;
+          }
+          *dst = v;
+        }
+      }
+    }
+  } else {
+    constexpr int ROW = BN * 2 + 16;                 // staged row stride in bytes
+    constexpr int HALF = BM / 2;
+    static_assert(HALF * ROW <= STAGE, "half a bf16 tile fits in one stage");
+    __syncthreads();                                 // every wave is done reading the stages
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int r = wm0 + 16 * j + (lane & 15);
+      uint8_t* rowp = (r < HALF ? sm0 : sm1) + (r % HALF) * ROW;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int c = wn0 + 16 * i + 4 * (lane >> 4);
         uint2 v;
         v.x = f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16);
         v.y = f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n) = v;
+        *reinterpret_cast<uint2*>(rowp + c * 2) = v;
       }
+    }
+    __syncthreads();
+    constexpr int CPR = BN * 2 / 16;                 // 16-byte chunks per row
+    constexpr int RPP = NT / CPR;                    // rows per pass
+    static_assert(NT % CPR == 0 && BM % RPP == 0, "copy-out split");
+    const int cr = tid / CPR, cc = tid % CPR;
+    const int64_t n = n0 + cc * 8;
+#pragma unroll
+    for (int r0 = 0; r0 < BM; r0 += RPP) {
+      const int r = r0 + cr;
+      const int64_t m = m0 + r;
+      const uint4 v = *reinterpret_cast<const uint4*>((r < HALF ? sm0 : sm1) + (r % HALF) * ROW + cc * 16);
+      if (m < M && n < N) *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n) = v;
     }
   }
 }
