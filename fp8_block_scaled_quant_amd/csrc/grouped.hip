@@ -229,15 +229,19 @@ __global__ __launch_bounds__(WM* WN * 64) void k_grouped_mx(GroupedParams p) {
   }
 }
 
+// 256x256 tiles, 8 waves of 64x128 (the dense GEMM's large-tile shape): measured faster than
+// 128x128 / 128x256 / 256x128 tiles on the routed-MoE shapes even though ragged experts
+// leave more of the last m-tile empty.
 hipError_t launch_grouped_mx(const GroupedParams& p, bool f32, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128;
+  constexpr int BM = 256, BN = 256, WM = 4, WN = 2;
   // Upper bound on m-tiles for well-formed offsets: sum_e ceil(c_e / BM) <= T / BM + E.
   const int64_t mtiles = (p.T + BM - 1) / BM + p.E;
   const int64_t grid = mtiles * ((p.N + BN - 1) / BN);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (f32)
-    hipLaunchKernelGGL((k_grouped_mx<BM, BN, 2, 2, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_grouped_mx<BM, BN, WM, WN, true>), dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_grouped_mx<BM, BN, 2, 2, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_grouped_mx<BM, BN, WM, WN, false>), dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, p);
   return hipGetLastError();
 }
 
