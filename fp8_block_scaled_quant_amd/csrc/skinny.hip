@@ -9,9 +9,9 @@
 // * Every workgroup takes all M rows (up to 256, rows past M read as zero) and a contiguous
 //   run of F 16-row fragments of B, so a launch of N / (16 F) workgroups (256 for the
 //   decode shapes) puts one workgroup on every CU and streams each weight byte once.
-// * 4 waves; wave w owns A rows 64w .. 64w+63 (4 MFMA fragments) against all F fragments of
-//   B. Per K block a wave reads 4 A and F B fragments from LDS (about 80 KB per workgroup
-//   for F = 6) against 4 F MFMAs.
+// * NW waves (4 in use); wave w owns A rows (256/NW) w .. (256/NW)(w+1)-1 against all F
+//   fragments of B. With 4 waves a wave reads 4 A and F B fragments from LDS per K block
+//   (about 80 KB per workgroup for F = 6) against 4 F MFMAs.
 // * Three LDS stages filled by direct global->LDS copies: the copies of K blocks kb+1 and
 //   kb+2 are in flight while kb is computed.
 // * Scales: one fp32 per A row per K block, and one per B fragment per K block (a 16-row
@@ -29,26 +29,32 @@ namespace {
 constexpr int kSkinnyM = 256;   // rows per workgroup (all of M)
 constexpr int kSkinnyLag = 3;
 
-template <int F>
+template <int F, int NW>
 struct SkinnyShape {
-  static constexpr int NT = 256;                      // 4 waves
+  static constexpr int NT = NW * 64;
+  static constexpr int FM = kSkinnyM / (16 * NW);     // A fragments per wave
   static constexpr int BN = 16 * F;
-  static constexpr int LB = (BN + 31) / 32;           // B copies per thread (32 rows each)
+  static constexpr int CR = NT / 8;                   // rows per copy (8 lanes per 128-byte row)
+  static constexpr int LA = kSkinnyM / CR;            // A copies per thread
+  static constexpr int LB = (BN + CR - 1) / CR;       // B copies per thread
   static constexpr int OFF_B = kSkinnyM * 128;
-  static constexpr int OFF_SA = OFF_B + LB * 32 * 128;
-  static constexpr int OFF_SB = OFF_SA + kSkinnyM * 4;
-  static constexpr int STAGE = OFF_SB + 4 * 256;      // one 64-float scale slot per wave
+  static constexpr int OFF_SA = OFF_B + LB * CR * 128;
+  // one 64-float scale slot per wave for sA (rows 0..255 are slots 0..3) and for sB: every
+  // wave's copy lands in its own slot, even an empty one (which writes zeros)
+  static constexpr int OFF_SB = OFF_SA + NW * 256;
+  static constexpr int STAGE = OFF_SB + NW * 256;
   static constexpr int LDS = 3 * STAGE;
+  static_assert(CR % 16 == 0, "swizzle phase must repeat across copies");
 };
 
 }  // namespace
 
-template <int F, bool kF32>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
-  using S = SkinnyShape<F>;
-  constexpr int FM = 4;                                 // A fragments per wave
+template <int F, int NW, bool kF32>
+__global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
+  using S = SkinnyShape<F, NW>;
+  constexpr int FM = S::FM;
+  constexpr int WR = 16 * FM;                           // A rows per wave
   static_assert(S::LDS <= 160 * 1024, "LDS budget");
-  static_assert(kSkinnyLag < FM, "a folded tile is at most one B fragment behind");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
 
   const int tid = threadIdx.x;
@@ -61,15 +67,15 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
   const int64_t rows_b = (N - n0) < S::BN ? (N - n0) : S::BN;
   const int fvalid = (int)(rows_b / 16);                // fragments inside N (N % 16 == 0)
 
-  // Operand copies: thread t moves 16 bytes of row t/8 (+32 per copy), chunk t%8 swizzled.
+  // Operand copies: thread t moves 16 bytes of row t/8 (+CR per copy), chunk t%8 swizzled.
   const int lr = tid >> 3;
   const uint32_t off0 = (uint32_t)(lr * K) + (uint32_t)(swz(lr, tid & 7) << 4);
   const uint32_t bytesA = (uint32_t)((rows_a - 1) * K + 128), bytesB = (uint32_t)((rows_b - 1) * K + 128);
-  // Scale copies: wave w fetches sA of rows 64w + lane; wave 0 also fetches the F fragment
-  // scales of B (lanes past the last valid fragment repeat it), the other waves issue the
-  // same copy through an empty descriptor so every wave counts the same number of copies.
-  const uint32_t offSA = (uint32_t)((wave * 64 + lane) * p.sa_ld * 4);
-  const uint32_t bytesSA = (uint32_t)((rows_a - 1) * p.sa_ld * 4 + 4);
+  // Scale copies: waves 0..3 fetch sA of rows 64w + lane; wave 0 also fetches the F fragment
+  // scales of B (lanes past the last valid fragment repeat it); every other copy goes
+  // through an empty descriptor, so that every wave counts the same number of copies.
+  const uint32_t offSA = (uint32_t)(((wave & 3) * 64 + lane) * p.sa_ld * 4);
+  const uint32_t bytesSA = wave < 4 ? (uint32_t)((rows_a - 1) * p.sa_ld * 4 + 4) : 0u;
   const int fl = lane < fvalid ? lane : fvalid - 1;
   const uint32_t offSB = (uint32_t)(((n0 + 16 * fl) >> 7) * p.sb_ld_n * 4);
   const uint32_t bytesSB = wave == 0 ? (uint32_t)(((N - 1) >> 7) * p.sb_ld_n * 4 + 4) : 0u;
@@ -78,21 +84,21 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
     const bool live = kb < nkb;
     const int kbc = live ? kb : 0;
 #pragma unroll
-    for (int it = 0; it < kSkinnyM / 32; ++it) {
-      const int64_t r0 = (int64_t)it * 32;
+    for (int it = 0; it < S::LA; ++it) {
+      const int64_t r0 = (int64_t)it * S::CR;
       const uint32_t nb = (live && bytesA > r0 * K) ? (uint32_t)(bytesA - r0 * K) : 0u;
-      dma16(make_rsrc(p.A + r0 * K + kbc * 128, nb), off0, st + (it * 256 + wave * 64) * 16);
+      dma16(make_rsrc(p.A + r0 * K + kbc * 128, nb), off0, st + (it * S::NT + wave * 64) * 16);
     }
 #pragma unroll
     for (int it = 0; it < S::LB; ++it) {
-      const int64_t r0 = (int64_t)it * 32;
+      const int64_t r0 = (int64_t)it * S::CR;
       const uint32_t nb = (live && bytesB > r0 * K) ? (uint32_t)(bytesB - r0 * K) : 0u;
-      dma16(make_rsrc(p.B + (n0 + r0) * K + kbc * 128, nb), off0, st + S::OFF_B + (it * 256 + wave * 64) * 16);
+      dma16(make_rsrc(p.B + (n0 + r0) * K + kbc * 128, nb), off0, st + S::OFF_B + (it * S::NT + wave * 64) * 16);
     }
     dma4(make_rsrc(p.sA + kbc, live ? bytesSA : 0u), offSA, st + S::OFF_SA + wave * 256);
     dma4(make_rsrc(p.sB + (int64_t)kbc * p.sb_ld_k, live ? bytesSB : 0u), offSB, st + S::OFF_SB + wave * 256);
   };
-  constexpr int kCopies = kSkinnyM / 32 + S::LB + 2;    // copies per wave per stage
+  constexpr int kCopies = S::LA + S::LB + 2;            // copies per wave per stage
 
   v4f acc[F][FM];
 #pragma unroll
@@ -100,8 +106,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const FragOffsets fa = frag_offsets(wave * 64, lane), fb = frag_offsets(0, lane);
-  const uint32_t o_sa = S::OFF_SA + (wave * 64 + (lane & 15)) * 4;
+  const FragOffsets fa = frag_offsets(wave * WR, lane), fb = frag_offsets(0, lane);
+  const uint32_t o_sa = S::OFF_SA + (wave * WR + (lane & 15)) * 4;
 
   auto compute = [&](uint32_t st) __attribute__((always_inline)) {
     const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi;
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
       }
     });
 #pragma unroll
-    for (int u = F * FM - kSkinnyLag; u < F * FM; ++u) fold(u);
+    for (int u = (F * FM > kSkinnyLag ? F * FM - kSkinnyLag : 0); u < F * FM; ++u) fold(u);
   };
 
   // K loop over three stages: before computing block kb, wait until this wave's copies of
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
   // Epilogue: lane holds C[m][n .. n+3] of each 16x16 tile.
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int64_t m = wave * 64 + 16 * j + (lane & 15);
+    const int64_t m = wave * WR + 16 * j + (lane & 15);
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
@@ -218,14 +224,18 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmParams p) {
   }
 }
 
+// 4 waves of 64 rows: measured faster than 8 waves of 32 rows for every decode shape.
+constexpr int kSkinnyWaves = 4;
+
 template <int F>
 static hipError_t launch_skinny_f(const GemmParams& p, bool f32, hipStream_t stream) {
+  constexpr int NW = kSkinnyWaves;
   const int64_t blocks = (p.N + 16 * F - 1) / (16 * F);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (f32)
-    hipLaunchKernelGGL((k_gemm_skinny<F, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_skinny<F, NW, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<F, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_skinny<F, NW, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -30,12 +30,21 @@ Readings where the pages are silent:
   [-127, 127]; amax = 0 gives e = 0. The E8M0 byte is e + 127, and
   q = E4M3(x * 2**-e) with the power-of-two scaling exact.
 
+Power-of-two block scales ([SkyRL-FP8] "Deep dive: FP8 quantization with FP32 and
+power-of-two block scales": the same blockwise granularity with exponent-only scales).
+Reading: the MX exponent rule applied to the 1x128 / 128x1 / 128x128 group, i.e.
+s = 2**e with e the smallest integer such that amax <= 448 * 2**e, clamped to
+[-127, 127] (0 for an all-zero group), stored as an fp32 value; q = E4M3(x * 2**-e),
+an exact scaling, which never saturates.
+
 Pinned by tests/test_oracle_quantize.py: a pure-Python brute force with exact
 fractions and a nearest-in-table encoder on small groups, the invariants that
 the amax element of every group encodes to +-448 and that a group scaled by
 2**j keeps its codes with the scale scaled by 2**j, the half-ulp error bound,
 group locality (changing one element changes only its own group), and the MX
-invariant 224 < amax * 2**-e <= 448.
+invariant 224 < amax * 2**-e <= 448. The power-of-two block quantizers: the same
+brute force with exponent-only scales for all three layouts, 224 < amax / s <= 448,
+2**j equivariance, and fl32(amax / 448) <= s < 2 fl32(amax / 448).
 """
 
 from __future__ import annotations
@@ -125,6 +134,52 @@ def mx_exponent(amax) -> np.ndarray:
     e = np.where(a <= E4M3_MAX * np.ldexp(1.0, e), e, e + 1)
     e = np.where(a == 0, 0, e)
     return np.clip(e, -127, 127).astype(np.int64)
+
+
+def _pow2_scale(amax):
+    """e = mx_exponent(amax) and s = 2**e as fp32 (exact, also at 2**-127)."""
+    e = mx_exponent(amax)
+    return e, np.ldexp(np.float64(1.0), e).astype(np.float32)
+
+
+def quant_act_1x128_pow2(x):
+    """1x128 quantization of X[M][K] with power-of-two scales.
+
+    Returns (q uint8 [M][K], s float32 [M][K/128], every s a power of two)."""
+    x = _as_f32(x)
+    M, K = x.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    g = x.reshape(M, K // GROUP, GROUP).astype(np.float64)
+    amax = np.max(np.abs(g), axis=2) if M else np.zeros((0, K // GROUP))
+    e, s = _pow2_scale(amax)
+    q = encode_e4m3(np.ldexp(g, -e[:, :, None]))      # exact power-of-two scaling in fp64
+    return q.reshape(M, K), s
+
+
+def quant_act_128x1_pow2(x):
+    """128x1 quantization with power-of-two scales, written transposed: row-wise of X^T.
+
+    Returns (qt uint8 [K][M], st float32 [K][M/128])."""
+    x = _as_f32(x)
+    if x.shape[0] % GROUP:
+        raise ValueError("M must be a multiple of 128 for 128x1 groups")
+    return quant_act_1x128_pow2(np.ascontiguousarray(x.T))
+
+
+def quant_w_128x128_pow2(w):
+    """128x128 block quantization of W[N][K] with power-of-two scales.
+
+    Returns (q uint8 [N][K], s float32 [N/128][K/128])."""
+    w = _as_f32(w)
+    N, K = w.shape
+    if N % GROUP or K % GROUP:
+        raise ValueError("N and K must be multiples of 128")
+    b = w.reshape(N // GROUP, GROUP, K // GROUP, GROUP).astype(np.float64)
+    amax = np.max(np.abs(b), axis=(1, 3))
+    e, s = _pow2_scale(amax)
+    q = encode_e4m3(np.ldexp(b, -e[:, None, :, None]))
+    return q.reshape(N, K), s
 
 
 def quant_mx_1x32(x):

@@ -216,3 +216,86 @@ def test_shape_checks():
         Q.quant_mx_1x32(np.zeros((2, 40), np.float32))
     q, s = Q.quant_act_1x128(np.zeros((0, 256), np.float32))
     assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+# ------------------------------------------------------------------------------------------
+# power-of-two block scales (1x128 / 128x1 / 128x128 groups with exponent-only scales)
+# ------------------------------------------------------------------------------------------
+
+def _brute_pow2_group(vals):
+    """One group by hand: e = smallest integer with amax <= 448 * 2**e (clamped to
+    [-127, 127], 0 for an all-zero group), q = nearest-even E4M3 of x * 2**-e (exact)."""
+    amax = max(abs(float(v)) for v in vals)
+    e = _brute_mx_exponent(amax)
+    codes = [_enc_fraction(Fraction(float(v)) / Fraction(2) ** e, bool(np.signbit(v))) for v in vals]
+    return codes, e
+
+
+def test_pow2_1x128_brute_force():
+    x = _sample((4, 384), 20)
+    x[0, 0:128] = 0.0                         # all-zero group -> e = 0
+    x[1, 130] = 448.0 * 2.0 ** -3             # amax exactly 448 * 2**-3 -> e = -3
+    x[2, 300] = 1792.0 + 8.0                  # just above 448 * 2**2 -> e = 3
+    x[3, 5] = 9.2e-41                         # a subnormal among normal values
+    x = bf16_round(x)                         # (the planted values above are bf16-exact)
+    q, s = Q.quant_act_1x128_pow2(x)
+    assert q.shape == (4, 384) and s.shape == (4, 3) and s.dtype == np.float32
+    for r in range(4):
+        for g in range(3):
+            vals = x[r, g * 128:(g + 1) * 128]
+            codes, e = _brute_pow2_group(vals)
+            assert list(q[r, g * 128:(g + 1) * 128]) == codes
+            assert Fraction(float(s[r, g])) == Fraction(2) ** e
+    assert s[0, 0] == 1.0 and s[1, 1] == np.float32(2.0 ** -3)
+
+
+def test_pow2_128x128_and_128x1_brute_force():
+    w = _sample((256, 256), 21, 0.02)
+    w[7, 140] = -0.75
+    q, s = Q.quant_w_128x128_pow2(w)
+    assert s.shape == (2, 2)
+    for bi in range(2):
+        for bj in range(2):
+            blk = w[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128].reshape(-1)
+            codes, e = _brute_pow2_group(blk)
+            assert Fraction(float(s[bi, bj])) == Fraction(2) ** e
+            assert list(q[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128].reshape(-1)) == codes
+    x = _sample((256, 128), 22)
+    qt, st = Q.quant_act_128x1_pow2(x)
+    assert qt.shape == (128, 256) and st.shape == (128, 2)
+    for k in (0, 63, 127):
+        for mb in range(2):
+            codes, e = _brute_pow2_group(x[mb * 128:(mb + 1) * 128, k])
+            assert list(qt[k, mb * 128:(mb + 1) * 128]) == codes
+            assert Fraction(float(st[k, mb])) == Fraction(2) ** e
+
+
+@pytest.mark.parametrize("fn", ["act", "w"])
+def test_pow2_range_invariant_and_fp32_bracket(fn):
+    """Every nonzero group in range: 224 < amax / s <= 448 (the amax element's code lies in
+    (224, 448], nothing saturates), and the FP32 recipe's scale s32 = fl32(amax / 448)
+    satisfies s32 <= s < 2 * s32."""
+    x = _sample((256, 512), 23, 3.0)
+    x[:, 7] *= np.float32(200.0)
+    x = bf16_round(x)
+    if fn == "act":
+        q, s = Q.quant_act_1x128_pow2(x)
+        _, s32 = Q.quant_act_1x128(x)
+        amax = np.max(np.abs(x.reshape(256, 4, 128)), axis=2)
+    else:
+        q, s = Q.quant_w_128x128_pow2(x)
+        _, s32 = Q.quant_w_128x128(x)
+        amax = np.max(np.abs(x.reshape(2, 128, 4, 128)), axis=(1, 3))
+    ratio = amax.astype(np.float64) / s.astype(np.float64)
+    assert np.all(ratio > 224) and np.all(ratio <= 448)
+    assert np.all(s32 <= s) and np.all(s < 2 * s32.astype(np.float64))
+    assert not np.any((q & 0x7F) == 0x7F)                     # no NaN codes
+
+
+@pytest.mark.parametrize("j", [-20, -1, 1, 9])
+def test_pow2_equivariance(j):
+    x = _sample((128, 256), 24)
+    q1, s1 = Q.quant_act_1x128_pow2(x)
+    q2, s2 = Q.quant_act_1x128_pow2(bf16_round(x * np.float32(2.0 ** j)))
+    assert np.array_equal(q1, q2)
+    assert np.array_equal(s2.astype(np.float64), s1.astype(np.float64) * 2.0 ** j)
