@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload dense|decode|backward|moe|install] [--no-cpu-baseline]
+                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
 HBM. The default workload is the dense layer shaped like a ~9B model's MLP
@@ -17,7 +17,8 @@ recorded on the stream the library launches on, against the 5.0 PFLOP/s dense FP
 peak; `quant_roofline` the X quantizer against 8 TB/s HBM.
 
 Other workloads (--workload) time the decode, backward, MoE and weight-install paths the
-same way. HBM-bound workloads (decode, install) cycle through copies of their inputs that
+same way; dense_pow2 and backward_pow2 run the dense layer with power-of-two block scales,
+which the scaled MFMA applies itself. HBM-bound workloads (decode, install) cycle through copies of their inputs that
 together exceed 1 GiB, so the 256 MB last-level cache cannot serve a launch from the previous
 one. `roofline.traffic` is the dominant kernel's HBM bytes per launch from rocprofv3
 FETCH_SIZE + WRITE_SIZE counter runs (scaled by what the same counters read for the install
@@ -55,8 +56,9 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "4c6da90fc94ad118", "gb": 1.6281},        # read 1.2257 + write 0.4024
-    "dgrad": {"sha": "4c6da90fc94ad118", "gb": 1.3006},          # read 1.2335 + write 0.0671
+    "gemm_gu": {"sha": "47d9ca8caad91577", "gb": 1.6281},        # read 1.2257 + write 0.4024
+    "gemm_gu_pow2": {"sha": "47d9ca8caad91577", "gb": 1.6279},   # read 1.2255 + write 0.4024
+    "dgrad": {"sha": "47d9ca8caad91577", "gb": 1.3004},          # read 1.2333 + write 0.0671
     "decode_n24576": {"sha": "c094817a1510f042", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
     "grouped_gu": {"sha": "18256618dd51e4a8", "gb": 0.5542},     # read 0.4871 + write 0.0672
     "install_gu": {"sha": "2385c944f460ef11", "gb": 0.2014},     # read 0.1007 + write 0.1007
@@ -73,7 +75,9 @@ def _sources_sha(files):
 
 KERNEL_SOURCES = {
     "gemm_gu": ("gemm.hip", "device.hpp", "internal.hpp"),
+    "gemm_gu_pow2": ("gemm.hip", "device.hpp", "internal.hpp"),
     "dgrad": ("gemm.hip", "device.hpp", "internal.hpp"),
+    "dgrad_pow2": ("gemm.hip", "device.hpp", "internal.hpp"),
     "decode_n24576": ("skinny.hip", "gemm.hip", "quant.hip", "device.hpp", "internal.hpp"),
     "grouped_gu": ("grouped.hip", "device.hpp", "internal.hpp"),
     "install_gu": ("install.hip", "device.hpp", "internal.hpp"),
@@ -94,7 +98,8 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "decode", "backward", "moe", "install"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "dense_pow2", "decode", "backward", "backward_pow2", "moe",
+                                                         "install"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -125,8 +130,12 @@ class EventTimer:
 # workloads
 # ---------------------------------------------------------------------------------------------
 
-def dense_setup(torch, F, W, dev):
+def dense_setup(torch, F, W, dev, pow2=False):
     d = W.dense_forward(with_down=True)
+    if pow2:
+        quant_act, quant_w, gemm = F.fp8_quant_act_1x128_pow2, F.fp8_quant_w_128x128_pow2, F.fp8_gemm_blockscaled_pow2_fwd
+    else:
+        quant_act, quant_w, gemm = F.fp8_quant_act_1x128, F.fp8_quant_w_128x128, F.fp8_gemm_blockscaled_fwd
     t = {k: W.to_bf16_tensor(v).to(dev) for k, v in d.items()}
     M, K = t["x"].shape
     N = t["w_gu"].shape[0]
@@ -147,23 +156,25 @@ def dense_setup(torch, F, W, dev):
     def step(timed):
         tm = timers if timed else None
         if tm: tm["quant_x"].start()
-        F.fp8_quant_act_1x128(t["x"], q=b["xq"], s=b["sx"], qt=b["xqt"], st=b["sxt"], rowwise=True, colwise=True)
+        quant_act(t["x"], q=b["xq"], s=b["sx"], qt=b["xqt"], st=b["sxt"], rowwise=True, colwise=True)
         if tm: tm["quant_x"].stop(); tm["quant_w"].start()
-        F.fp8_quant_w_128x128(t["w_gu"], q=b["wq_gu"], s=b["sw_gu"])
-        F.fp8_quant_w_128x128(t["w_dn"], q=b["wq_dn"], s=b["sw_dn"])
+        quant_w(t["w_gu"], q=b["wq_gu"], s=b["sw_gu"])
+        quant_w(t["w_dn"], q=b["wq_dn"], s=b["sw_dn"])
         if tm: tm["quant_w"].stop(); tm["gemm_gu"].start()
-        F.fp8_gemm_blockscaled_fwd(b["xq"], b["sx"], b["wq_gu"], b["sw_gu"], y=b["y_gu"])
+        gemm(b["xq"], b["sx"], b["wq_gu"], b["sw_gu"], y=b["y_gu"])
         if tm: tm["gemm_gu"].stop(); tm["quant_x2"].start()
-        F.fp8_quant_act_1x128(t["x2"], q=b["x2q"], s=b["sx2"])
+        quant_act(t["x2"], q=b["x2q"], s=b["sx2"])
         if tm: tm["quant_x2"].stop(); tm["gemm_dn"].start()
-        F.fp8_gemm_blockscaled_fwd(b["x2q"], b["sx2"], b["wq_dn"], b["sw_dn"], y=b["y_dn"])
+        gemm(b["x2q"], b["sx2"], b["wq_dn"], b["sw_dn"], y=b["y_dn"])
         if tm: tm["gemm_dn"].stop()
 
     flops_gu = 2.0 * M * N * K
     flops_dn = 2.0 * M * N2 * K2
     info = dict(
-        config={"workload": "dense_layer_forward_9b", "tokens_M": M, "hidden_K": K, "gate_up_N": N,
-                "down_N": N2, "down_K": K2, "recipe": "blockwise 1x128 act / 128x128 weight, E4M3, fp32 scales",
+        config={"workload": "dense_layer_forward_9b" + ("_pow2" if pow2 else ""), "tokens_M": M, "hidden_K": K,
+                "gate_up_N": N, "down_N": N2, "down_K": K2,
+                "recipe": "blockwise 1x128 act / 128x128 weight, E4M3, "
+                          + ("power-of-two scales applied by the scaled MFMA" if pow2 else "fp32 scales"),
                 "out": "bf16"},
         flops=flops_gu + flops_dn,
         dominant=("gemm_gu", "mfma", flops_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
@@ -172,6 +183,7 @@ def dense_setup(torch, F, W, dev):
         quant=("quant_x", (M * K * (2 + 1 + 1) + 2 * M * K // 128 * 4) / 1e9,
                "bf16 read 2 B + row and column E4M3 payloads 1 B each + fp32 scales per element"),
         gemm_keys=("gemm_gu", "gemm_dn"),
+        traffic_key="gemm_gu_pow2" if pow2 else "gemm_gu",
     )
     return step, timers, info
 
@@ -218,15 +230,21 @@ def decode_setup(torch, F, W, dev):
     return step, timers, info
 
 
-def backward_setup(torch, F, W, dev):
+def backward_setup(torch, F, W, dev, pow2=False):
     d = W.dense_forward(with_down=False)
+    if pow2:
+        quant_act, quant_w = F.fp8_quant_act_1x128_pow2, F.fp8_quant_w_128x128_pow2
+        dgrad, wgrad = F.fp8_gemm_blockscaled_pow2_dgrad, F.fp8_gemm_blockscaled_pow2_wgrad
+    else:
+        quant_act, quant_w = F.fp8_quant_act_1x128, F.fp8_quant_w_128x128
+        dgrad, wgrad = F.fp8_gemm_blockscaled_dgrad, F.fp8_gemm_blockscaled_wgrad
     dy = W.to_bf16_tensor(W.dense_backward()["dy"]).to(dev)
     x = W.to_bf16_tensor(d["x"]).to(dev)
     w = W.to_bf16_tensor(d["w_gu"]).to(dev)
     M, K = x.shape
     N = w.shape[0]
-    _, _, xqt, sxt = F.fp8_quant_act_1x128(x, rowwise=False, colwise=True)      # saved from the forward
-    wq, sw, wqt = F.fp8_quant_w_128x128(w, transpose=True)
+    _, _, xqt, sxt = quant_act(x, rowwise=False, colwise=True)      # saved from the forward
+    wq, sw, wqt = quant_w(w, transpose=True)
     u8, f32 = torch.uint8, torch.float32
     b = dict(dyq=torch.empty((M, N), dtype=u8, device=dev), sdy=torch.empty((M, N // 128), dtype=f32, device=dev),
              dyqt=torch.empty((N, M), dtype=u8, device=dev), sdyt=torch.empty((N, M // 128), dtype=f32, device=dev),
@@ -235,22 +253,24 @@ def backward_setup(torch, F, W, dev):
 
     def step(timed):
         if timed: timers["quant_dy"].start()
-        F.fp8_quant_act_1x128(dy, q=b["dyq"], s=b["sdy"], qt=b["dyqt"], st=b["sdyt"], rowwise=True, colwise=True)
+        quant_act(dy, q=b["dyq"], s=b["sdy"], qt=b["dyqt"], st=b["sdyt"], rowwise=True, colwise=True)
         if timed: timers["quant_dy"].stop(); timers["dgrad"].start()
-        F.fp8_gemm_blockscaled_dgrad(b["dyq"], b["sdy"], wqt, sw, dx=b["dx"])
+        dgrad(b["dyq"], b["sdy"], wqt, sw, dx=b["dx"])
         if timed: timers["dgrad"].stop(); timers["wgrad"].start()
-        F.fp8_gemm_blockscaled_wgrad(b["dyqt"], b["sdyt"], xqt, sxt, dw=b["dw"])
+        wgrad(b["dyqt"], b["sdyt"], xqt, sxt, dw=b["dw"])
         if timed: timers["wgrad"].stop()
 
     fl = 2.0 * M * N * K
     info = dict(
-        config={"workload": "dense_layer_backward_gate_up", "tokens_M": M, "N": N, "K": K,
-                "dgrad_out": "bf16", "wgrad_out": "fp32"},
+        config={"workload": "dense_layer_backward_gate_up" + ("_pow2" if pow2 else ""), "tokens_M": M, "N": N, "K": K,
+                "scales": "power-of-two, applied by the scaled MFMA" if pow2 else "fp32", "dgrad_out": "bf16",
+                "wgrad_out": "fp32"},
         flops=2 * fl,
         dominant=("dgrad", "mfma", fl / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS, f"2*M*N*K = {fl:.4g} FLOP per launch"),
         quant=("quant_dy", (M * N * 4 + 2 * M * N // 128 * 4) / 1e9,
                "bf16 read 2 B + row and column E4M3 payloads + fp32 scales per element"),
         gemm_keys=("dgrad", "wgrad"),
+        traffic_key="dgrad_pow2" if pow2 else "dgrad",
     )
     return step, timers, info
 
@@ -370,11 +390,16 @@ def cpu_baseline(workload: str, budget_s: float = 12.0):
         x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
         w = W.bf16_round(rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02))
 
+        pow2 = workload.endswith("_pow2")
+        quant_act = OQ.quant_act_1x128_pow2 if pow2 else OQ.quant_act_1x128
+        quant_w = OQ.quant_w_128x128_pow2 if pow2 else OQ.quant_w_128x128
+
         def chunk():
-            xq, sx = OQ.quant_act_1x128(x)
-            wq, sw = OQ.quant_w_128x128(w)
+            xq, sx = quant_act(x)
+            wq, sw = quant_w(w)
             OG.gemm_fwd(xq, sx, wq, sw)
-        what = f"oracle 1x128 + 128x128 quantization and fp64 dequantized GEMM, {m}x{n}x{k} chunk of the gate/up layer"
+        what = (f"oracle 1x128 + 128x128 {'power-of-two scale ' if pow2 else ''}quantization and fp64 dequantized "
+                f"GEMM, {m}x{n}x{k} chunk of the gate/up layer")
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -400,7 +425,8 @@ def main():
 
     dev = torch.device("cuda", 0)
     F.load_library()
-    setup = {"dense": dense_setup, "decode": decode_setup, "backward": backward_setup, "moe": moe_setup,
+    setup = {"dense": dense_setup, "dense_pow2": lambda *args: dense_setup(*args, pow2=True), "decode": decode_setup,
+             "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup,
              "install": install_setup}[a.workload]
     step, timers, info = setup(torch, F, W, dev)
 
@@ -419,7 +445,7 @@ def main():
     dom_ms = timers[name].mean_ms()
     achieved = per_launch / (dom_ms * 1e-3)
     gemm_ms = sum(timers[k].mean_ms() for k in info["gemm_keys"])
-    traffic, sha = _traffic(name)
+    traffic, sha = _traffic(info.get("traffic_key", name))
     if info["flops"] is not None:
         value, vunit = round(info["flops"] / (ms_per_step * 1e-3) / 1e12, 2), "TFLOP/s"
     else:

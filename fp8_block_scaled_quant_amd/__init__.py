@@ -26,6 +26,8 @@ __all__ = [
     "fp8rl_abi_version", "fp8_quant_act_1x128", "fp8_quant_w_128x128", "mxfp8_quant_1x32",
     "fp8_gemm_blockscaled_fwd", "fp8rl_fwd_workspace_bytes", "fp8_gemm_blockscaled_dgrad",
     "fp8_gemm_blockscaled_wgrad", "fp8_grouped_gemm", "fp8_weight_install",
+    "fp8_quant_act_1x128_pow2", "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd",
+    "fp8_gemm_blockscaled_pow2_dgrad", "fp8_gemm_blockscaled_pow2_wgrad",
 ]
 
 RECIPE_BLOCK128 = 0
@@ -59,6 +61,11 @@ _SIGNATURES = {
     "fp8_gemm_blockscaled_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_grouped_gemm": ([_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_weight_install": ([ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), _vp], _int),
+    "fp8_quant_act_1x128_pow2": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
+    "fp8_quant_w_128x128_pow2": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
+    "fp8_gemm_blockscaled_pow2_fwd": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_gemm_blockscaled_pow2_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_gemm_blockscaled_pow2_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
 }
 
 
@@ -130,6 +137,15 @@ def fp8_quant_act_1x128(x, q=None, s=None, qt=None, st=None, *, rowwise=True, co
 
     Returns (q [M][K] u8, s [M][K/128] f32, qt [K][M] u8, st [K][M/128] f32); outputs not
     requested are None."""
+    return _quant_act("fp8_quant_act_1x128", x, q, s, qt, st, rowwise, colwise)
+
+
+def fp8_quant_act_1x128_pow2(x, q=None, s=None, qt=None, st=None, *, rowwise=True, colwise=False):
+    """As fp8_quant_act_1x128, with power-of-two scales (stored as fp32)."""
+    return _quant_act("fp8_quant_act_1x128_pow2", x, q, s, qt, st, rowwise, colwise)
+
+
+def _quant_act(entry, x, q, s, qt, st, rowwise, colwise):
     lib = load_library()
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
@@ -146,14 +162,22 @@ def fp8_quant_act_1x128(x, q=None, s=None, qt=None, st=None, *, rowwise=True, co
         st = _out(st, torch.float32, (K, M // 128), dev, "st")
     else:
         qt = st = None
-    _check(lib.fp8_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(dev)),
-           "fp8_quant_act_1x128")
+    _check(getattr(lib, entry)(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(dev)), entry)
     return q, s, qt, st
 
 
 def fp8_quant_w_128x128(w, q=None, s=None, qt=None, *, transpose=False):
     """128x128-block weight quantization. Returns (q [N][K] u8, s [N/128][K/128] f32,
     qt [K][N] u8 or None)."""
+    return _quant_w("fp8_quant_w_128x128", w, q, s, qt, transpose)
+
+
+def fp8_quant_w_128x128_pow2(w, q=None, s=None, qt=None, *, transpose=False):
+    """As fp8_quant_w_128x128, with power-of-two block scales (stored as fp32)."""
+    return _quant_w("fp8_quant_w_128x128_pow2", w, q, s, qt, transpose)
+
+
+def _quant_w(entry, w, q, s, qt, transpose):
     lib = load_library()
     N, K = w.shape
     _need(w, torch.bfloat16, (N, K), "w")
@@ -161,7 +185,7 @@ def fp8_quant_w_128x128(w, q=None, s=None, qt=None, *, transpose=False):
     q = _out(q, torch.uint8, (N, K), dev, "q")
     s = _out(s, torch.float32, (N // 128, K // 128), dev, "s")
     qt = _out(qt, torch.uint8, (K, N), dev, "qt") if transpose else None
-    _check(lib.fp8_quant_w_128x128(_ptr(w), N, K, _ptr(q), _ptr(s), _ptr(qt), _stream(dev)), "fp8_quant_w_128x128")
+    _check(getattr(lib, entry)(_ptr(w), N, K, _ptr(q), _ptr(s), _ptr(qt), _stream(dev)), entry)
     return q, s, qt
 
 
@@ -220,8 +244,32 @@ def fp8_gemm_blockscaled_fwd(xq=None, sx=None, wq=None, sw=None, *, x_bf16=None,
     return y
 
 
+def fp8_gemm_blockscaled_pow2_fwd(xq, sx, wq, sw, *, out_dtype=torch.bfloat16, y=None):
+    """Y[M][N] = deq(X) deq(W)^T for power-of-two block scales (FP8 X only)."""
+    lib = load_library()
+    N, K = wq.shape
+    M = xq.shape[0]
+    _need(wq, torch.uint8, (N, K), "wq")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    _need(xq, torch.uint8, (M, K), "xq")
+    _need(sx, torch.float32, (M, K // 128), "sx")
+    y = _out(y, out_dtype, (M, N), wq.device, "y")
+    _check(lib.fp8_gemm_blockscaled_pow2_fwd(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y),
+                                             _odt(out_dtype), _stream(wq.device)), "fp8_gemm_blockscaled_pow2_fwd")
+    return y
+
+
 def fp8_gemm_blockscaled_dgrad(dyq, sdy, wqt, sw, *, out_dtype=torch.bfloat16, dx=None):
     """dX[M][K] = deq(dY) deq(W) with wqt = W's byte transpose [K][N], sw [N/128][K/128]."""
+    return _dgrad("fp8_gemm_blockscaled_dgrad", dyq, sdy, wqt, sw, out_dtype, dx)
+
+
+def fp8_gemm_blockscaled_pow2_dgrad(dyq, sdy, wqt, sw, *, out_dtype=torch.bfloat16, dx=None):
+    """As fp8_gemm_blockscaled_dgrad, for power-of-two block scales."""
+    return _dgrad("fp8_gemm_blockscaled_pow2_dgrad", dyq, sdy, wqt, sw, out_dtype, dx)
+
+
+def _dgrad(entry, dyq, sdy, wqt, sw, out_dtype, dx):
     lib = load_library()
     M, N = dyq.shape
     K = wqt.shape[0]
@@ -230,13 +278,22 @@ def fp8_gemm_blockscaled_dgrad(dyq, sdy, wqt, sw, *, out_dtype=torch.bfloat16, d
     _need(wqt, torch.uint8, (K, N), "wqt")
     _need(sw, torch.float32, (N // 128, K // 128), "sw")
     dx = _out(dx, out_dtype, (M, K), dyq.device, "dx")
-    _check(lib.fp8_gemm_blockscaled_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wqt), _ptr(sw), M, N, K, _ptr(dx),
-                                          _odt(out_dtype), _stream(dyq.device)), "fp8_gemm_blockscaled_dgrad")
+    _check(getattr(lib, entry)(_ptr(dyq), _ptr(sdy), _ptr(wqt), _ptr(sw), M, N, K, _ptr(dx), _odt(out_dtype),
+                               _stream(dyq.device)), entry)
     return dx
 
 
 def fp8_gemm_blockscaled_wgrad(dyqt, sdyt, xqt, sxt, *, dw=None, accumulate=False):
     """dW[N][K] (fp32) = deq(dY)^T deq(X) from the column-wise copies dyqt [N][M], xqt [K][M]."""
+    return _wgrad("fp8_gemm_blockscaled_wgrad", dyqt, sdyt, xqt, sxt, dw, accumulate)
+
+
+def fp8_gemm_blockscaled_pow2_wgrad(dyqt, sdyt, xqt, sxt, *, dw=None, accumulate=False):
+    """As fp8_gemm_blockscaled_wgrad, for power-of-two scales."""
+    return _wgrad("fp8_gemm_blockscaled_pow2_wgrad", dyqt, sdyt, xqt, sxt, dw, accumulate)
+
+
+def _wgrad(entry, dyqt, sdyt, xqt, sxt, dw, accumulate):
     lib = load_library()
     N, M = dyqt.shape
     K = xqt.shape[0]
@@ -247,8 +304,8 @@ def fp8_gemm_blockscaled_wgrad(dyqt, sdyt, xqt, sxt, *, dw=None, accumulate=Fals
     if accumulate and dw is None:
         raise ValueError("accumulate=True needs dw")
     dw = _out(dw, torch.float32, (N, K), dyqt.device, "dw")
-    _check(lib.fp8_gemm_blockscaled_wgrad(_ptr(dyqt), _ptr(sdyt), _ptr(xqt), _ptr(sxt), M, N, K, _ptr(dw),
-                                          1 if accumulate else 0, _stream(dyqt.device)), "fp8_gemm_blockscaled_wgrad")
+    _check(getattr(lib, entry)(_ptr(dyqt), _ptr(sdyt), _ptr(xqt), _ptr(sxt), M, N, K, _ptr(dw),
+                               1 if accumulate else 0, _stream(dyqt.device)), entry)
     return dw
 
 

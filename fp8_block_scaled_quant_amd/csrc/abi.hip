@@ -64,8 +64,12 @@ const char* fp8rl_status_str(fp8rl_status s) {
   return "unknown status";
 }
 
-fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
-                                 float* st, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fp8rl_status quant_act_impl(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
+                            bool pow2, void* stream) {
   if ((q == nullptr) != (s == nullptr) || (qt == nullptr) != (st == nullptr)) return FP8RL_ERR_NULL;
   if (q == nullptr && qt == nullptr) return FP8RL_ERR_NULL;
   if (fp8rl_status e = check_dims(M, K)) return e;
@@ -77,12 +81,12 @@ fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_
       (st && !aligned(st, 4)))
     return FP8RL_ERR_ALIGN;
   if (fp8rl_status e = check_device()) return e;
-  if (qt == nullptr) return launched(launch_quant_rows_1x128(x, M, K, q, s, as_stream(stream)));
-  return launched(launch_quant_act_tile(x, M, K, q, s, qt, st, as_stream(stream)));
+  if (qt == nullptr) return launched(launch_quant_rows_1x128(x, M, K, q, s, pow2, as_stream(stream)));
+  return launched(launch_quant_act_tile(x, M, K, q, s, qt, st, pow2, as_stream(stream)));
 }
 
-fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
-                                 void* stream) {
+fp8rl_status quant_w_impl(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt, bool pow2,
+                          void* stream) {
   if (q == nullptr || s == nullptr) return FP8RL_ERR_NULL;
   if (fp8rl_status e = check_dims(N, K)) return e;
   if (N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
@@ -90,7 +94,31 @@ fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_
   if (w == nullptr) return FP8RL_ERR_NULL;
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || (qt && !aligned(qt, 16))) return FP8RL_ERR_ALIGN;
   if (fp8rl_status e = check_device()) return e;
-  return launched(launch_quant_w_128x128(w, N, K, q, s, qt, as_stream(stream)));
+  return launched(launch_quant_w_128x128(w, N, K, q, s, qt, pow2, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                 float* st, void* stream) {
+  return quant_act_impl(x, M, K, q, s, qt, st, false, stream);
+}
+
+fp8rl_status fp8_quant_act_1x128_pow2(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                      float* st, void* stream) {
+  return quant_act_impl(x, M, K, q, s, qt, st, true, stream);
+}
+
+fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                 void* stream) {
+  return quant_w_impl(w, N, K, q, s, qt, false, stream);
+}
+
+fp8rl_status fp8_quant_w_128x128_pow2(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                      void* stream) {
+  return quant_w_impl(w, N, K, q, s, qt, true, stream);
 }
 
 fp8rl_status mxfp8_quant_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0, void* stream) {
@@ -138,7 +166,7 @@ fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const 
     const size_t qpad = ((size_t)(M * K) + 255) & ~(size_t)255;
     uint8_t* wxq = static_cast<uint8_t*>(workspace);
     float* wsx = reinterpret_cast<float*>(wxq + qpad);
-    if (launch_quant_rows_1x128(x_bf16, M, K, wxq, wsx, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
+    if (launch_quant_rows_1x128(x_bf16, M, K, wxq, wsx, false, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
     xq = wxq;
     sx = wsx;
   }
@@ -156,11 +184,45 @@ fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const 
   p.sb_ld_k = 1;
   p.ldc = N;
   p.accumulate = 0;
-  return launched(launch_gemm_blockscaled(p, false, y_dtype == FP8RL_OUT_F32, st));
+  return launched(launch_gemm_blockscaled(p, false, y_dtype == FP8RL_OUT_F32, false, st));
 }
 
-fp8rl_status fp8_gemm_blockscaled_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wqt, const float* sw,
-                                        int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* stream) {
+fp8rl_status fp8_gemm_blockscaled_pow2_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                           int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
+  if (xq == nullptr || sx == nullptr || wq == nullptr || sw == nullptr || y == nullptr) return FP8RL_ERR_NULL;
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
+  if (fp8rl_status e = check_dims(M, K)) return e;
+  if (fp8rl_status e = check_dims(N, K)) return e;
+  if (fp8rl_status e = check_dims(M, N)) return e;
+  if (K % 128 != 0 || N % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8RL_OK;
+  if (K == 0) return FP8RL_ERR_SHAPE;
+  if (!aligned(xq, 16) || !aligned(sx, 4) || !aligned(wq, 16) || !aligned(sw, 4) || !aligned(y, 16))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  GemmParams p{};
+  p.A = xq;
+  p.B = wq;
+  p.sA = sx;
+  p.sB = sw;
+  p.C = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.sa_ld = K / 128;
+  p.sb_ld_n = K / 128;
+  p.sb_ld_k = 1;
+  p.ldc = N;
+  p.accumulate = 0;
+  return launched(launch_gemm_blockscaled(p, false, y_dtype == FP8RL_OUT_F32, true, as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+fp8rl_status dgrad_impl(const uint8_t* dyq, const float* sdy, const uint8_t* wqt, const float* sw, int64_t M,
+                        int64_t N, int64_t K, void* dx, int dx_dtype, bool pow2, void* stream) {
   if (dyq == nullptr || sdy == nullptr || wqt == nullptr || sw == nullptr || dx == nullptr) return FP8RL_ERR_NULL;
   if (dx_dtype != FP8RL_OUT_BF16 && dx_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
   if (fp8rl_status e = check_dims(M, N)) return e;
@@ -186,11 +248,11 @@ fp8rl_status fp8_gemm_blockscaled_dgrad(const uint8_t* dyq, const float* sdy, co
   p.sb_ld_k = K / 128;
   p.ldc = K;
   p.accumulate = 0;
-  return launched(launch_gemm_blockscaled(p, false, dx_dtype == FP8RL_OUT_F32, as_stream(stream)));
+  return launched(launch_gemm_blockscaled(p, false, dx_dtype == FP8RL_OUT_F32, pow2, as_stream(stream)));
 }
 
-fp8rl_status fp8_gemm_blockscaled_wgrad(const uint8_t* dyqt, const float* sdyt, const uint8_t* xqt, const float* sxt,
-                                        int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream) {
+fp8rl_status wgrad_impl(const uint8_t* dyqt, const float* sdyt, const uint8_t* xqt, const float* sxt, int64_t M,
+                        int64_t N, int64_t K, float* dw, int accumulate, bool pow2, void* stream) {
   if (dyqt == nullptr || sdyt == nullptr || xqt == nullptr || sxt == nullptr || dw == nullptr) return FP8RL_ERR_NULL;
   if (fp8rl_status e = check_dims(M, N)) return e;
   if (fp8rl_status e = check_dims(M, K)) return e;
@@ -215,7 +277,33 @@ fp8rl_status fp8_gemm_blockscaled_wgrad(const uint8_t* dyqt, const float* sdyt, 
   p.sb_ld_k = 1;
   p.ldc = K;
   p.accumulate = accumulate ? 1 : 0;
-  return launched(launch_gemm_blockscaled(p, true, true, as_stream(stream)));
+  return launched(launch_gemm_blockscaled(p, true, true, pow2, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8rl_status fp8_gemm_blockscaled_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wqt, const float* sw,
+                                        int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* stream) {
+  return dgrad_impl(dyq, sdy, wqt, sw, M, N, K, dx, dx_dtype, false, stream);
+}
+
+fp8rl_status fp8_gemm_blockscaled_pow2_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wqt,
+                                             const float* sw, int64_t M, int64_t N, int64_t K, void* dx,
+                                             int dx_dtype, void* stream) {
+  return dgrad_impl(dyq, sdy, wqt, sw, M, N, K, dx, dx_dtype, true, stream);
+}
+
+fp8rl_status fp8_gemm_blockscaled_wgrad(const uint8_t* dyqt, const float* sdyt, const uint8_t* xqt, const float* sxt,
+                                        int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream) {
+  return wgrad_impl(dyqt, sdyt, xqt, sxt, M, N, K, dw, accumulate, false, stream);
+}
+
+fp8rl_status fp8_gemm_blockscaled_pow2_wgrad(const uint8_t* dyqt, const float* sdyt, const uint8_t* xqt,
+                                             const float* sxt, int64_t M, int64_t N, int64_t K, float* dw,
+                                             int accumulate, void* stream) {
+  return wgrad_impl(dyqt, sdyt, xqt, sxt, M, N, K, dw, accumulate, true, stream);
 }
 
 fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, const uint8_t* wq, const void* sw,

@@ -24,6 +24,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// MXFP8 exponent for a group amax: the smallest integer e with amax <= 448 * 2^e, clamped
+// to [-127, 127]; 0 for amax == 0. For amax = 1.m * 2^F (m the 23-bit field), 448 * 2^(F-8)
+// = 1.75 * 2^F, so e = F - 8 when the mantissa field is <= 0x600000, else F - 7. A
+// subnormal amax (< 2^-126) needs e <= -134, i.e. the clamp value -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t u = __float_as_uint(amax);
+  const int be = (int)((u >> 23) & 0xffu);
+  if (be == 0) return -127;
+  const int F = be - 127;
+  int e = ((u & 0x7fffffu) <= 0x600000u) ? F - 8 : F - 7;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // Scale of a 1x128 / 128x1 / 128x128 group: s = fl32(amax / 448) (IEEE division; hipcc's
 // default fp32 division is correctly rounded), 1.0 for an all-zero group. `r` is the
 // fp64 reciprocal used to form the scaled values (see scaled()).
@@ -37,6 +51,24 @@ __device__ __forceinline__ BlockScale block_scale(float amax) {
   b.s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
   b.r = 1.0 / (double)b.s;
   return b;
+}
+
+// Power-of-two block scale: s = 2^e with the MX exponent rule (smallest e with
+// amax <= 448 * 2^e, clamped to [-127, 127]; 2^-127 is an exact fp32 subnormal). The
+// scaled value x * 2^-e is then exact (scaled() computes it without rounding) and at most
+// 448 in magnitude.
+__device__ __forceinline__ BlockScale block_scale_pow2(float amax) {
+  const int e = mx_exponent(amax);
+  BlockScale b;
+  b.s = ldexpf(1.0f, e);
+  b.r = ldexp(1.0, -e);
+  return b;
+}
+
+template <bool kPow2>
+__device__ __forceinline__ BlockScale group_scale(float amax) {
+  if constexpr (kPow2) return block_scale_pow2(amax);
+  else return block_scale(amax);
 }
 
 // The fp32 quotient fl32(x / s) for a bf16 value x with |x| <= amax, computed as
@@ -69,19 +101,6 @@ __device__ __forceinline__ float absmax2(uint32_t w) {
   return fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w)));
 }
 
-// MXFP8 exponent for a group amax: the smallest integer e with amax <= 448 * 2^e, clamped
-// to [-127, 127]; 0 for amax == 0. For amax = 1.m * 2^F (m the 23-bit field), 448 * 2^(F-8)
-// = 1.75 * 2^F, so e = F - 8 when the mantissa field is <= 0x600000, else F - 7. A
-// subnormal amax (< 2^-126) needs e <= -134, i.e. the clamp value -127.
-__device__ __forceinline__ int mx_exponent(float amax) {
-  if (amax == 0.0f) return 0;
-  const uint32_t u = __float_as_uint(amax);
-  const int be = (int)((u >> 23) & 0xffu);
-  if (be == 0) return -127;
-  const int F = be - 127;
-  int e = ((u & 0x7fffffu) <= 0x600000u) ? F - 8 : F - 7;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
 
 // Raw buffer descriptor over [base, base + bytes) as four SGPR words: loads at byte
 // offsets >= bytes return zero instead of touching memory (the hardware range check of

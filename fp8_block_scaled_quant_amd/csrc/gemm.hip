@@ -33,7 +33,7 @@ namespace fp8rl {
 // Distance, in MFMA tiles, between an MFMA and the FMAs that fold its result.
 constexpr int kLag = 3;
 
-template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32>
+template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, bool kPow2>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -140,6 +140,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   const FragOffsets fa = frag_offsets(wm0, lane), fb = frag_offsets(wn0, lane);
   const uint32_t o_sa = OFF_SA + (wm0 + (lane & 15)) * 4;
   const uint32_t o_sb = kRowB ? OFF_SB + (wn0 + 4 * (lane >> 4)) * 4 : OFF_SB + (uint32_t)(((n0 + wn0) >> 7) - nb0) * 4;
+  const uint32_t o_sbr = OFF_SB + (wn0 + (lane & 15)) * 4;     // row (lane & 15) of each B fragment
 
   // One K block from the stage at st. A fragments stay in registers for the whole block; B
   // fragments are double-buffered (fragment i+1 is read while fragment i feeds the MFMAs);
@@ -176,60 +177,105 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     hold(sbv);
     hold(blo);
     hold(bhi);
-    if (!kRowB) {
+    if constexpr (kPow2) {
+      // Power-of-two scales: the scaled MFMA applies 2^(e_a + e_b) itself (E8M0 bytes are
+      // the scales' fp32 exponent fields; 2^-127, an fp32 subnormal, gives byte 0), so the
+      // products accumulate directly. Lane l supplies the scale of row l & 15 for all four
+      // 32-wide parts of the K block.
+      int ua[FM];
 #pragma unroll
-      for (int j = 0; j < FM; ++j) prod[j] = sa[j] * sb;
-    }
-    // Tiles run in the order t = i * FM + j; the FMAs that fold tile t - kLag into the
-    // accumulators follow the MFMA of tile t, so the wave never stalls on a fresh MFMA
-    // result. `pipe` holds the kLag + 1 most recent MFMA results.
-    v4f pipe[kLag + 1];
-    v4i sbprev = sbv;
-    auto fold = [&](int i, int j, const v4f& pr, const v4i& sbw) __attribute__((always_inline)) {
-      if (kRowB) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[i][j][r] = __builtin_fmaf(pr[r], sa[j] * __int_as_float(sbw[r]), acc[i][j][r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], prod[j], acc[i][j][r]);
-      }
-    };
-    static_for<0, FN>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      v4i nlo, nhi, nsb;
-      if constexpr (i + 1 < FN) {
-        nlo = ds_read16<(i + 1) * 2048>(b_lo);
-        nhi = ds_read16<(i + 1) * 2048>(b_hi);
-        if (kRowB) nsb = ds_read16<(i + 1) * 64>(sb_ad);
-      }
-      const v8i bf = join(blo, bhi);
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int t = i * FM + j;
-        pipe[t % (kLag + 1)] = mfma_fp8(bf, af[j], v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
-        if (t >= kLag) {
-          const int u = t - kLag;
-          fold(u / FM, u % FM, pipe[u % (kLag + 1)], (u / FM == i) ? sbv : sbprev);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keep the MFMA / fold interleave as written
-      }
-      sbprev = sbv;
-      if constexpr (i + 1 < FN) {
-        __builtin_amdgcn_sched_barrier(0);   // this step's MFMAs stay ahead of the wait
+      for (int j = 0; j < FM; ++j) ua[j] = (int)(__float_as_uint(sa[j]) >> 23);
+      int ubr[FN];
+      if constexpr (kRowB) {
+        // The LDS reads land only at the wait: take the exponents after it.
+        float sbr[FN];
+        static_for<0, FN>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          sbr[i] = ds_read4f<i * 64>(st + o_sbr);
+        });
         lds_wait<0>();
-        hold(nlo);
-        hold(nhi);
-        blo = nlo;
-        bhi = nhi;
-        if (kRowB) {
-          hold(nsb);
-          sbv = nsb;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          hold(sbr[i]);
+          ubr[i] = (int)(__float_as_uint(sbr[i]) >> 23);
         }
       }
-    });
+      const int ub = kRowB ? 0 : (int)(__float_as_uint(sb) >> 23);
+      static_for<0, FN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        v4i nlo, nhi;
+        if constexpr (i + 1 < FN) {
+          nlo = ds_read16<(i + 1) * 2048>(b_lo);
+          nhi = ds_read16<(i + 1) * 2048>(b_hi);
+        }
+        const v8i bf = join(blo, bhi);
 #pragma unroll
-    for (int u = FN * FM - kLag; u < FN * FM; ++u) fold(u / FM, u % FM, pipe[u % (kLag + 1)], sbprev);
+        for (int j = 0; j < FM; ++j) acc[i][j] = mfma_fp8(bf, af[j], acc[i][j], kRowB ? ubr[i] : ub, ua[j]);
+        if constexpr (i + 1 < FN) {
+          __builtin_amdgcn_sched_barrier(0);
+          lds_wait<0>();
+          hold(nlo);
+          hold(nhi);
+          blo = nlo;
+          bhi = nhi;
+        }
+      });
+    } else {
+      if (!kRowB) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) prod[j] = sa[j] * sb;
+      }
+      // Tiles run in the order t = i * FM + j; the FMAs that fold tile t - kLag into the
+      // accumulators follow the MFMA of tile t, so the wave never stalls on a fresh MFMA
+      // result. `pipe` holds the kLag + 1 most recent MFMA results.
+      v4f pipe[kLag + 1];
+      v4i sbprev = sbv;
+      auto fold = [&](int i, int j, const v4f& pr, const v4i& sbw) __attribute__((always_inline)) {
+        if (kRowB) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = __builtin_fmaf(pr[r], sa[j] * __int_as_float(sbw[r]), acc[i][j][r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], prod[j], acc[i][j][r]);
+        }
+      };
+      static_for<0, FN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        v4i nlo, nhi, nsb;
+        if constexpr (i + 1 < FN) {
+          nlo = ds_read16<(i + 1) * 2048>(b_lo);
+          nhi = ds_read16<(i + 1) * 2048>(b_hi);
+          if (kRowB) nsb = ds_read16<(i + 1) * 64>(sb_ad);
+        }
+        const v8i bf = join(blo, bhi);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int t = i * FM + j;
+          pipe[t % (kLag + 1)] = mfma_fp8(bf, af[j], v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
+          if (t >= kLag) {
+            const int u = t - kLag;
+            fold(u / FM, u % FM, pipe[u % (kLag + 1)], (u / FM == i) ? sbv : sbprev);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // keep the MFMA / fold interleave as written
+        }
+        sbprev = sbv;
+        if constexpr (i + 1 < FN) {
+          __builtin_amdgcn_sched_barrier(0);   // this step's MFMAs stay ahead of the wait
+          lds_wait<0>();
+          hold(nlo);
+          hold(nhi);
+          blo = nlo;
+          bhi = nhi;
+          if (kRowB) {
+            hold(nsb);
+            sbv = nsb;
+          }
+        }
+      });
+#pragma unroll
+      for (int u = FN * FM - kLag; u < FN * FM; ++u) fold(u / FM, u % FM, pipe[u % (kLag + 1)], sbprev);
+    }
   };
 
   // K loop. Each step: wait until this wave's copies into the current stage have landed,
@@ -334,28 +380,32 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool kRowB>
+template <int BM, int BN, int WM, int WN, bool kRowB, bool kPow2>
 static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles), block(WM * WN * 64);
   if (f32)
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kPow2>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kPow2>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-// Tile choice: at most 256 rows with block-scaled B go to the few-row kernel (skinny.hip);
+// Tile choice: at most 256 rows with block-scaled fp32 scales go to the few-row kernel (skinny.hip);
 // otherwise 256x256 tiles (8 waves, 64x128 per wave) when there are enough of them to fill
 // the 256 CUs, else 128x128 tiles (4 waves, 64x64 per wave).
-hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, hipStream_t stream) {
-  if (!row_scale_b && p.M <= 256) return launch_gemm_skinny(p, f32, stream);
+hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, bool pow2, hipStream_t stream) {
+  if (!pow2 && !row_scale_b && p.M <= 256) return launch_gemm_skinny(p, f32, stream);
   const int64_t big_tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   const bool big = big_tiles >= 256;
-  if (row_scale_b) {
-    return big ? launch_cfg<256, 256, 4, 2, true>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true>(p, f32, stream);
+  if (pow2) {
+    if (row_scale_b)
+      return big ? launch_cfg<256, 256, 4, 2, true, true>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, true>(p, f32, stream);
+    return big ? launch_cfg<256, 256, 4, 2, false, true>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false, true>(p, f32, stream);
   }
-  return big ? launch_cfg<256, 256, 4, 2, false>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false>(p, f32, stream);
+  if (row_scale_b)
+    return big ? launch_cfg<256, 256, 4, 2, true, false>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, false>(p, f32, stream);
+  return big ? launch_cfg<256, 256, 4, 2, false, false>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false, false>(p, f32, stream);
 }
 
 }  // namespace fp8rl

@@ -7,12 +7,13 @@
 
 namespace fp8rl {
 
-hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+// pow2: power-of-two group scales (exponent rule of MXFP8) instead of fl32(amax / 448).
+hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, bool pow2,
                                    hipStream_t stream);
 hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
-                                 float* st, hipStream_t stream);
+                                 float* st, bool pow2, hipStream_t stream);
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
-                                  hipStream_t stream);
+                                  bool pow2, hipStream_t stream);
 hipError_t launch_quant_mx_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0,
                                 hipStream_t stream);
 
@@ -29,7 +30,9 @@ struct GemmParams {
   int64_t sa_ld, sb_ld_n, sb_ld_k, ldc;
   int accumulate;
 };
-hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, hipStream_t stream);
+// pow2: every scale is a power of two (the pow2 quantizers' output); the scaled MFMA then
+// applies them (their fp32 exponent fields) and no rescale step is needed.
+hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, bool pow2, hipStream_t stream);
 // Few-row form (M <= 256, block-scaled B only): all rows per workgroup, one workgroup per CU.
 hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream);
 

@@ -1,5 +1,6 @@
 // FP8 quantizer kernels: 1x128 rows, 128x1 columns (transposed output), 128x128 blocks,
-// and MXFP8 1x32 groups. Method: [AIS] symmetric quantizer equation on the E4M3 grid;
+// and MXFP8 1x32 groups. The blockwise kernels take kPow2 = true for power-of-two scales
+// ([SkyRL-FP8] "Deep dive": exponent-only block scales; MX exponent rule per group). Method: [AIS] symmetric quantizer equation on the E4M3 grid;
 // granularities from [Jet-RL] "Quantization scheme" and [SkyRL-FP8] (block and MXFP8
 // recipes). Each kernel is a single pass over its bf16 input: coalesced 16-byte loads,
 // group amax by lane shuffles (or LDS for 128x1 / 128x128), and E4M3 conversion.
@@ -13,6 +14,7 @@ namespace fp8rl {
 // element g * 128 and its scale is s[g] (row-major [M][K/128]). 8 lanes per group, 16
 // elements (32 bytes) per lane; one wave covers 8 consecutive groups = 2 KB of input.
 // ---------------------------------------------------------------------------------------
+template <bool kPow2>
 __global__ __launch_bounds__(256) void k_quant_rows_1x128(const uint16_t* __restrict__ x,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ s,
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(const uint16_t* __rest
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   amax = fmaxf(amax, __shfl_xor(amax, 4));
-  const BlockScale bs = block_scale(amax);
+  const BlockScale bs = group_scale<kPow2>(amax);
   if (valid) {
     const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
     const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(const uint16_t* __rest
 // then own one column (16 rows each): column amax over those 8 lanes, and each store
 // instruction writes 8 whole 128-byte lines of qt.
 // ---------------------------------------------------------------------------------------
-template <bool kBlock>
+template <bool kBlock, bool kPow2>
 __global__ __launch_bounds__(512) void k_quant_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                     uint8_t* __restrict__ q, float* __restrict__ s,
                                                     uint8_t* __restrict__ qt, float* __restrict__ st) {
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(512) void k_quant_tile(const uint16_t* __restrict__
     if (lane == 0) red[wave] = a;
     __syncthreads();
     a = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
-    const BlockScale bs = block_scale(a);
+    const BlockScale bs = group_scale<kPow2>(a);
     if (tid == 0) s[rb * ncb + cb] = bs.s;
     rblk = bs.r;
     if (want_rows) {
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(512) void k_quant_tile(const uint16_t* __restrict__
       a = fmaxf(a, __shfl_xor(a, 2));
       a = fmaxf(a, __shfl_xor(a, 4));
       a = fmaxf(a, __shfl_xor(a, 8));
-      const BlockScale bs = block_scale(a);
+      const BlockScale bs = group_scale<kPow2>(a);
       if (c == 0) s[(rb * 128 + 4 * rg + i) * ncb + cb] = bs.s;
       *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
           quant8(v[i].x, v[i].y, v[i].z, v[i].w, bs.r);
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(512) void k_quant_tile(const uint16_t* __restrict__
       m = fmaxf(m, __shfl_xor(m, 1));
       m = fmaxf(m, __shfl_xor(m, 2));
       m = fmaxf(m, __shfl_xor(m, 4));
-      const BlockScale bs = block_scale(m);
+      const BlockScale bs = group_scale<kPow2>(m);
       r = bs.r;
       if (k == 0) st[(cb * 128 + col) * (R / 128) + rb] = bs.s;
     }
@@ -195,26 +197,35 @@ __global__ __launch_bounds__(256) void k_quant_mx_1x32(const uint16_t* __restric
 // ---------------------------------------------------------------------------------------
 // Launchers (argument validation happens in the C ABI layer before these are called).
 // ---------------------------------------------------------------------------------------
-hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, bool pow2,
                                    hipStream_t stream) {
   const int64_t ngroups = M * (K / 128);
   const int64_t threads = ngroups * 8;
   const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(k_quant_rows_1x128, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, s, ngroups);
+  if (pow2)
+    hipLaunchKernelGGL(k_quant_rows_1x128<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, s, ngroups);
+  else
+    hipLaunchKernelGGL(k_quant_rows_1x128<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, s, ngroups);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
-                                 float* st, hipStream_t stream) {
-  hipLaunchKernelGGL(k_quant_tile<false>, dim3((unsigned)((K / 128) * (M / 128))), dim3(512), 0, stream, x, M, K,
-                     q, s, qt, st);
+                                 float* st, bool pow2, hipStream_t stream) {
+  const dim3 grid((unsigned)((K / 128) * (M / 128)));
+  if (pow2)
+    hipLaunchKernelGGL((k_quant_tile<false, true>), grid, dim3(512), 0, stream, x, M, K, q, s, qt, st);
+  else
+    hipLaunchKernelGGL((k_quant_tile<false, false>), grid, dim3(512), 0, stream, x, M, K, q, s, qt, st);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL(k_quant_tile<true>, dim3((unsigned)((K / 128) * (N / 128))), dim3(512), 0, stream, w, N, K,
-                     q, s, qt, (float*)nullptr);
+                                  bool pow2, hipStream_t stream) {
+  const dim3 grid((unsigned)((K / 128) * (N / 128)));
+  if (pow2)
+    hipLaunchKernelGGL((k_quant_tile<true, true>), grid, dim3(512), 0, stream, w, N, K, q, s, qt, (float*)nullptr);
+  else
+    hipLaunchKernelGGL((k_quant_tile<true, false>), grid, dim3(512), 0, stream, w, N, K, q, s, qt, (float*)nullptr);
   return hipGetLastError();
 }
 

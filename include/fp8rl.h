@@ -64,7 +64,7 @@ typedef enum {
 } fp8rl_out;
 
 /* ABI version of this header. */
-#define FP8RL_ABI_VERSION 1
+#define FP8RL_ABI_VERSION 2
 int fp8rl_abi_version(void);
 const char* fp8rl_status_str(fp8rl_status status);
 
@@ -95,6 +95,18 @@ fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K,
  * Rules: N % 128 == 0, K % 128 == 0. */
 fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K,
                                  uint8_t* q, float* s, uint8_t* qt, void* stream);
+
+/* The same two quantizers with power-of-two block scales ([SkyRL-FP8] "Deep dive: FP8
+ * quantization with FP32 and power-of-two block scales": exponent-only scales at the same
+ * block granularity). Per group: s = 2^e with e the smallest integer such that
+ * amax <= 448 * 2^e, clamped to [-127, 127] (e = 0 for an all-zero group); s is stored as an
+ * fp32 value (2^-127 as the fp32 subnormal); q = E4M3(x * 2^-e), exact scaling that never
+ * saturates. Arguments, layouts and rules are those of the calls above; bytes and scales
+ * are bit-identical to the CPU oracle. The _pow2 GEMMs below take these scales. */
+fp8rl_status fp8_quant_act_1x128_pow2(const uint16_t* x, int64_t M, int64_t K,
+                                      uint8_t* q, float* s, uint8_t* qt, float* st, void* stream);
+fp8rl_status fp8_quant_w_128x128_pow2(const uint16_t* w, int64_t N, int64_t K,
+                                      uint8_t* q, float* s, uint8_t* qt, void* stream);
 
 /* MXFP8 quantization, one E8M0 scale per 1x32 group along K ([SkyRL-FP8] "When
  * independent quantization breaks policy consistency": one scale per 1x32 block; "Deep
@@ -150,6 +162,27 @@ fp8rl_status fp8_gemm_blockscaled_wgrad(const uint8_t* dyqt, const float* sdyt,
                                         const uint8_t* xqt, const float* sxt,
                                         int64_t M, int64_t N, int64_t K,
                                         float* dw, int accumulate, void* stream);
+
+/* Forward, DGrad and WGrad for power-of-two block scales (the _pow2 quantizers' output):
+ * the same products, layouts and rules as fp8_gemm_blockscaled_fwd (FP8 X only: xq, sx),
+ * _dgrad and _wgrad, but the scaled MFMA applies each block's 2^e itself, taken from the
+ * exponent field of the fp32 scale, so there is no per-block rescale step ([SkyRL-FP8]
+ * "Deep dive": power-of-two scales are applied by the hardware's block-scaled matrix
+ * instructions). Precondition: every scale is a power of two in [2^-127, 2^127]; for any
+ * other value only its exponent field is used (the mantissa is ignored). Any M is served
+ * by the tiled kernel (there is no few-row form). */
+fp8rl_status fp8_gemm_blockscaled_pow2_fwd(const uint8_t* xq, const float* sx,
+                                           const uint8_t* wq, const float* sw,
+                                           int64_t M, int64_t N, int64_t K,
+                                           void* y, int y_dtype, void* stream);
+fp8rl_status fp8_gemm_blockscaled_pow2_dgrad(const uint8_t* dyq, const float* sdy,
+                                             const uint8_t* wqt, const float* sw,
+                                             int64_t M, int64_t N, int64_t K,
+                                             void* dx, int dx_dtype, void* stream);
+fp8rl_status fp8_gemm_blockscaled_pow2_wgrad(const uint8_t* dyqt, const float* sdyt,
+                                             const uint8_t* xqt, const float* sxt,
+                                             int64_t M, int64_t N, int64_t K,
+                                             float* dw, int accumulate, void* stream);
 
 /* Grouped GEMM for mixture-of-experts ([SkyRL-FP8] MoE: routed experts hold most
  * parameters; MXFP8 recipe). Routed rows are grouped by expert; rows
