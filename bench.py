@@ -59,9 +59,10 @@ MEASURED_TRAFFIC = {
     "gemm_gu": {"sha": "47d9ca8caad91577", "gb": 1.6281},        # read 1.2257 + write 0.4024
     "gemm_gu_pow2": {"sha": "47d9ca8caad91577", "gb": 1.6279},   # read 1.2255 + write 0.4024
     "dgrad": {"sha": "47d9ca8caad91577", "gb": 1.3004},          # read 1.2333 + write 0.0671
-    "decode_n24576": {"sha": "c094817a1510f042", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
-    "grouped_gu": {"sha": "18256618dd51e4a8", "gb": 0.5542},     # read 0.4871 + write 0.0672
-    "install_gu": {"sha": "2385c944f460ef11", "gb": 0.2014},     # read 0.1007 + write 0.1007
+    "dgrad_pow2": {"sha": "47d9ca8caad91577", "gb": 1.3004},     # read 1.2333 + write 0.0671
+    "decode_n24576": {"sha": "f0ab91830ef18133", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
+    "grouped_gu": {"sha": "91547e59995d80c3", "gb": 0.5539},     # read 0.4868 + write 0.0672
+    "install_gu": {"sha": "c4b1fdd282a2ee0f", "gb": 0.2014},     # read 0.1007 + write 0.1007
 }
 
 
