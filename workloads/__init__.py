@@ -155,3 +155,18 @@ def moe_mxfp8(n_tokens=4096, hidden=2048, n_experts=64, topk=8, n_gu=1024, n_dn=
         "w_dn": normal_bf16((n_experts, n_dn, k_dn), 0.02, config, 3),
         "h": normal_bf16((n_tokens * topk, k_dn), 1.0, config, 4),
     }
+
+
+def fused_producers(m=8192, hidden=4096, f=12288, config=6):
+    """Inputs of the fused producers in the dense layer: the gate/up GEMM output
+    GU [M][2F] = [gate | up] ~ N(0,1) with 0.1% of channels x50 (the SwiGLU producer's
+    input, M = 8192 tokens, F = 12288), the residual stream X [M][4096] ~ N(0,1) with 0.1%
+    of channels x50 and the RMSNorm weight gamma [4096] = 1 + N(0, 0.1) (the RMSNorm
+    producer's inputs); eps = 1e-6."""
+    gu32 = _normal32(_rng(config, 0), (m, 2 * f), 1.0)
+    gu = bf16_round(with_outlier_channels(gu32, 0.001, 50.0, _rng(config, 1)))
+    del gu32
+    x32 = _normal32(_rng(config, 2), (m, hidden), 1.0)
+    x = bf16_round(with_outlier_channels(x32, 0.001, 50.0, _rng(config, 3)))
+    gamma = bf16_round(np.float32(1.0) + _normal32(_rng(config, 4), (hidden,), 0.1))
+    return {"gu": gu, "x": x, "gamma": gamma, "eps": 1e-6}
