@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install] [--no-cpu-baseline]
+                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install|producers] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
 HBM. The default workload is the dense layer shaped like a ~9B model's MLP
@@ -82,6 +82,7 @@ KERNEL_SOURCES = {
     "decode_n24576": ("skinny.hip", "gemm.hip", "quant.hip", "device.hpp", "internal.hpp"),
     "grouped_gu": ("grouped.hip", "device.hpp", "internal.hpp"),
     "install_gu": ("install.hip", "device.hpp", "internal.hpp"),
+    "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp", "internal.hpp"),
 }
 
 
@@ -100,7 +101,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense", choices=["dense", "dense_pow2", "decode", "backward", "backward_pow2", "moe",
-                                                         "install"])
+                                                         "install", "producers"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -359,9 +360,96 @@ def install_setup(torch, F, W, dev):
     return step, timers, info
 
 
+def producers_setup(torch, F, W, dev):
+    """The fused producers of the dense layer, each writing the row-wise FP8 copy the next
+    GEMM reads and the column-wise (128x1, transposed) copy its WGrad reads:
+    RMSNorm of the residual stream X 8192x4096 -> FP8 (input of the gate/up GEMM), and
+    SwiGLU of the gate/up output GU 8192x24576 -> FP8 H 8192x12288 (input of the down GEMM).
+    The unfused chains (bf16 producer, then the quantizer) are timed after the timed steps
+    for comparison."""
+    d = W.fused_producers()
+    gu = W.to_bf16_tensor(d["gu"]).to(dev)
+    x0 = W.to_bf16_tensor(d["x"]).to(dev)
+    gamma = W.to_bf16_tensor(d["gamma"]).to(dev)
+    eps = d["eps"]
+    del d
+    M, F2 = gu.shape
+    Fh = F2 // 2
+    K = x0.shape[1]
+    n_x = max(1, -(-ROTATE_BYTES // (x0.numel() * 2)))          # X copies: the step reads >= 1 GiB of X
+    xs = [x0.clone() for _ in range(n_x)]
+    del x0
+    u8, f32 = torch.uint8, torch.float32
+    b = dict(hq=torch.empty((M, Fh), dtype=u8, device=dev), hs=torch.empty((M, Fh // 128), dtype=f32, device=dev),
+             hqt=torch.empty((Fh, M), dtype=u8, device=dev), hst=torch.empty((Fh, M // 128), dtype=f32, device=dev),
+             xq=torch.empty((M, K), dtype=u8, device=dev), xs=torch.empty((M, K // 128), dtype=f32, device=dev),
+             xqt=torch.empty((K, M), dtype=u8, device=dev), xst=torch.empty((K, M // 128), dtype=f32, device=dev),
+             rstd=torch.empty((M,), dtype=f32, device=dev))
+    timers = {k: EventTimer(torch) for k in ("rmsnorm_fp8", "swiglu_fp8")}
+    it = [0]
+
+    def step(timed):
+        x = xs[it[0] % n_x]
+        it[0] += 1
+        if timed: timers["rmsnorm_fp8"].start()
+        F.fp8_rmsnorm_quant_1x128(x, gamma, eps, q=b["xq"], s=b["xs"], qt=b["xqt"], st=b["xst"], rstd=b["rstd"],
+                                  colwise=True)
+        if timed: timers["rmsnorm_fp8"].stop(); timers["swiglu_fp8"].start()
+        F.fp8_swiglu_quant_1x128(gu, q=b["hq"], s=b["hs"], qt=b["hqt"], st=b["hst"], colwise=True)
+        if timed: timers["swiglu_fp8"].stop()
+
+    def unfused(reps=10):
+        """Mean microseconds of the unfused chains: bf16 producer, then the quantizer."""
+        t = {k: EventTimer(torch) for k in ("rmsnorm_bf16", "quant_y", "swiglu_bf16", "quant_h")}
+        h = torch.empty((M, Fh), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        for i in range(reps + 2):
+            x = xs[i % n_x]
+            tm = t if i >= 2 else None
+            if tm: tm["rmsnorm_bf16"].start()
+            F.fp8_rmsnorm_bf16(x, gamma, eps, y=y, rstd=b["rstd"])
+            if tm: tm["rmsnorm_bf16"].stop(); tm["quant_y"].start()
+            F.fp8_quant_act_1x128(y, q=b["xq"], s=b["xs"], qt=b["xqt"], st=b["xst"], colwise=True)
+            if tm: tm["quant_y"].stop(); tm["swiglu_bf16"].start()
+            F.fp8_swiglu_bf16(gu, h=h)
+            if tm: tm["swiglu_bf16"].stop(); tm["quant_h"].start()
+            F.fp8_quant_act_1x128(h, q=b["hq"], s=b["hs"], qt=b["hqt"], st=b["hst"], colwise=True)
+            if tm: tm["quant_h"].stop()
+        torch.cuda.synchronize()
+        return {k: round(v.mean_ms() * 1e3, 2) for k, v in t.items()}
+
+    # algorithmic bytes: bf16 inputs once, both FP8 copies, both scale sets (+ gamma, r)
+    sw_bytes = M * F2 * 2 + 2 * M * Fh + 2 * (M * Fh // 128) * 4
+    rms_bytes = M * K * 2 + K * 2 + 2 * M * K + 2 * (M * K // 128) * 4 + M * 4
+    info = dict(
+        config={"workload": "fused_producers_dense_layer_9b", "rmsnorm": f"X {M}x{K} -> FP8 rows + cols",
+                "swiglu": f"GU {M}x{F2} -> FP8 H {M}x{Fh} rows + cols", "recipe": "1x128 / 128x1, fp32 scales",
+                "x_copies": n_x},
+        flops=None,
+        bytes=sw_bytes + rms_bytes,
+        dominant=("swiglu_fp8", "hbm", sw_bytes / 1e9, "GB/s", PEAK_HBM_GBS,
+                  f"bf16 GU read 4 B + two E4M3 copies 2 B + fp32 scales per output element = {sw_bytes} B"),
+        quant=("rmsnorm_fp8", rms_bytes / 1e9, "bf16 X read 2 B + two E4M3 copies 2 B + scales and r per element"),
+        gemm_keys=(),
+        extra=unfused,
+    )
+    return step, timers, info
+
+
 # ---------------------------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample of the same workload
 # ---------------------------------------------------------------------------------------------
+
+def _repeat(chunk, budget_s):
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        chunk()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            return reps, dt
+
 
 def cpu_baseline(workload: str, budget_s: float = 12.0):
     """Time the oracle (as it stands) on a bounded sample of the workload: one chunk of the
@@ -375,6 +463,22 @@ def cpu_baseline(workload: str, budget_s: float = 12.0):
     except Exception:
         threads = os.cpu_count() or 1
     rng = np.random.default_rng(0)
+    if workload == "producers":
+        from oracle import producers as OP
+        m, f, k = 128, 12288, 4096
+        gu = W.bf16_round(rng.standard_normal((m, 2 * f)).astype(np.float32))
+        x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        gamma = W.bf16_round(np.float32(1.0) + rng.standard_normal(k).astype(np.float32) * np.float32(0.1))
+        nbytes = (m * 2 * f * 2 + 2 * m * f + 2 * (m * f // 128) * 4) + (m * k * 2 + 2 * m * k + 2 * (m * k // 128) * 4)
+        OP.silu_bf16_table()                       # built once per process, outside the timing
+
+        def chunk():
+            OP.swiglu_quant_1x128(gu, colwise=True)
+            OP.rmsnorm_quant_1x128(x, gamma, 1e-6, colwise=True)
+        reps, dt = _repeat(chunk, budget_s)
+        return {"value": reps * nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{reps} x oracle SwiGLU -> FP8 (rows + cols) of GU {m}x{2 * f} and RMSNorm -> FP8 "
+                          f"(rows + cols) of X {m}x{k}, 128 token rows of the dense layer", "seconds": round(dt, 2)}
     if workload == "moe":
         m, n, k = 512, 1024, 2048
         x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
@@ -401,14 +505,7 @@ def cpu_baseline(workload: str, budget_s: float = 12.0):
             OG.gemm_fwd(xq, sx, wq, sw)
         what = (f"oracle 1x128 + 128x128 {'power-of-two scale ' if pow2 else ''}quantization and fp64 dequantized "
                 f"GEMM, {m}x{n}x{k} chunk of the gate/up layer")
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        chunk()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s:
-            break
+    reps, dt = _repeat(chunk, budget_s)
     return {"value": reps * 2.0 * m * n * k / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{reps} x {what}", "seconds": round(dt, 2)}
 
@@ -428,7 +525,7 @@ def main():
     F.load_library()
     setup = {"dense": dense_setup, "dense_pow2": lambda *args: dense_setup(*args, pow2=True), "decode": decode_setup,
              "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup,
-             "install": install_setup}[a.workload]
+             "install": install_setup, "producers": producers_setup}[a.workload]
     step, timers, info = setup(torch, F, W, dev)
 
     for _ in range(a.warmup):
@@ -478,6 +575,8 @@ def main():
         out["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
                                  "per_launch": qdesc}
+    if "extra" in info:
+        out["unfused_kernel_us"] = info["extra"]()
     if not a.no_cpu_baseline and a.workload != "install":
         out["cpu_baseline"] = cpu_baseline(a.workload)
     print(json.dumps(out))

@@ -28,6 +28,7 @@ __all__ = [
     "fp8_gemm_blockscaled_wgrad", "fp8_grouped_gemm", "fp8_weight_install",
     "fp8_quant_act_1x128_pow2", "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd",
     "fp8_gemm_blockscaled_pow2_dgrad", "fp8_gemm_blockscaled_pow2_wgrad",
+    "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16", "fp8_rmsnorm_quant_1x128",
 ]
 
 RECIPE_BLOCK128 = 0
@@ -66,6 +67,10 @@ _SIGNATURES = {
     "fp8_gemm_blockscaled_pow2_fwd": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_blockscaled_pow2_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_blockscaled_pow2_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_swiglu_bf16": ([_vp, _i64, _i64, _vp, _vp], _int),
+    "fp8_swiglu_quant_1x128": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _int, _vp], _int),
+    "fp8_rmsnorm_bf16": ([_vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _vp], _int),
+    "fp8_rmsnorm_quant_1x128": ([_vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _int, _vp], _int),
 }
 
 
@@ -164,6 +169,75 @@ def _quant_act(entry, x, q, s, qt, st, rowwise, colwise):
         qt = st = None
     _check(getattr(lib, entry)(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(dev)), entry)
     return q, s, qt, st
+
+
+def _act_outputs(M, K, dev, q, s, qt, st, rowwise, colwise):
+    if rowwise:
+        q = _out(q, torch.uint8, (M, K), dev, "q")
+        s = _out(s, torch.float32, (M, K // 128), dev, "s")
+    else:
+        q = s = None
+    if colwise:
+        qt = _out(qt, torch.uint8, (K, M), dev, "qt")
+        st = _out(st, torch.float32, (K, M // 128), dev, "st")
+    else:
+        qt = st = None
+    return q, s, qt, st
+
+
+def fp8_swiglu_bf16(gu, h=None):
+    """h[M][F] = bf16(fl32(bf16(silu(gate)) * up)) for gu [M][2F] = [gate | up] (bf16)."""
+    lib = load_library()
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be 2-D with an even number of columns")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    _need(gu, torch.bfloat16, (M, 2 * F), "gu")
+    h = _out(h, torch.bfloat16, (M, F), gu.device, "h")
+    _check(lib.fp8_swiglu_bf16(_ptr(gu), M, F, _ptr(h), _stream(gu.device)), "fp8_swiglu_bf16")
+    return h
+
+
+def fp8_swiglu_quant_1x128(gu, q=None, s=None, qt=None, st=None, *, rowwise=True, colwise=False, pow2_scales=False):
+    """SwiGLU of gu [M][2F] quantized 1x128 (and/or 128x1, transposed) without a bf16
+    round trip. Returns (q, s, qt, st) as fp8_quant_act_1x128 does for h."""
+    lib = load_library()
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be 2-D with an even number of columns")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    _need(gu, torch.bfloat16, (M, 2 * F), "gu")
+    q, s, qt, st = _act_outputs(M, F, gu.device, q, s, qt, st, rowwise, colwise)
+    _check(lib.fp8_swiglu_quant_1x128(_ptr(gu), M, F, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), 1 if pow2_scales else 0,
+                                      _stream(gu.device)), "fp8_swiglu_quant_1x128")
+    return q, s, qt, st
+
+
+def fp8_rmsnorm_bf16(x, gamma, eps=1e-6, y=None, rstd=None):
+    """y = bf16(fl32(gamma * bf16(fl32(x * r)))), r = fl32(1/sqrt(mean(x^2) + eps)) per row.
+    Returns (y [M][K] bf16, rstd [M] f32)."""
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(gamma, torch.bfloat16, (K,), "gamma")
+    y = _out(y, torch.bfloat16, (M, K), x.device, "y")
+    rstd = _out(rstd, torch.float32, (M,), x.device, "rstd")
+    _check(lib.fp8_rmsnorm_bf16(_ptr(x), _ptr(gamma), M, K, float(eps), _ptr(y), _ptr(rstd), _stream(x.device)),
+           "fp8_rmsnorm_bf16")
+    return y, rstd
+
+
+def fp8_rmsnorm_quant_1x128(x, gamma, eps=1e-6, q=None, s=None, qt=None, st=None, rstd=None, *, rowwise=True,
+                            colwise=False, pow2_scales=False):
+    """RMSNorm of x [M][K] quantized 1x128 (and/or 128x1, transposed) without a bf16 round
+    trip. Returns (q, s, qt, st, rstd)."""
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(gamma, torch.bfloat16, (K,), "gamma")
+    q, s, qt, st = _act_outputs(M, K, x.device, q, s, qt, st, rowwise, colwise)
+    rstd = _out(rstd, torch.float32, (M,), x.device, "rstd")
+    _check(lib.fp8_rmsnorm_quant_1x128(_ptr(x), _ptr(gamma), M, K, float(eps), _ptr(rstd), _ptr(q), _ptr(s), _ptr(qt),
+                                       _ptr(st), 1 if pow2_scales else 0, _stream(x.device)), "fp8_rmsnorm_quant_1x128")
+    return q, s, qt, st, rstd
 
 
 def fp8_quant_w_128x128(w, q=None, s=None, qt=None, *, transpose=False):

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/fp8rl.h"
@@ -60,6 +62,7 @@ const char* fp8rl_status_str(fp8rl_status s) {
     case FP8RL_ERR_DEVICE: return "current HIP device is not gfx950";
     case FP8RL_ERR_LAUNCH: return "kernel launch failed";
     case FP8RL_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8RL_ERR_VALUE: return "scalar argument out of range";
   }
   return "unknown status";
 }
@@ -68,14 +71,20 @@ const char* fp8rl_status_str(fp8rl_status s) {
 
 namespace {
 
-fp8rl_status quant_act_impl(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
-                            bool pow2, void* stream) {
+// Output-pair rules of the activation quantizers and the quantizing producers.
+fp8rl_status check_act_outputs(int64_t M, uint8_t* q, float* s, uint8_t* qt, float* st) {
   if ((q == nullptr) != (s == nullptr) || (qt == nullptr) != (st == nullptr)) return FP8RL_ERR_NULL;
   if (q == nullptr && qt == nullptr) return FP8RL_ERR_NULL;
+  if (qt != nullptr && M % 128 != 0) return FP8RL_ERR_SHAPE;
+  return FP8RL_OK;
+}
+
+fp8rl_status quant_act_impl(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt, float* st,
+                            bool pow2, void* stream) {
   if (fp8rl_status e = check_dims(M, K)) return e;
   if (K % 128 != 0) return FP8RL_ERR_SHAPE;
-  if (qt != nullptr && M % 128 != 0) return FP8RL_ERR_SHAPE;
-  if (M == 0 || K == 0) return FP8RL_OK;
+  if (M == 0 || K == 0) return FP8RL_OK;                     // empty work: outputs may be empty (NULL)
+  if (fp8rl_status e = check_act_outputs(M, q, s, qt, st)) return e;
   if (x == nullptr) return FP8RL_ERR_NULL;
   if (!aligned(x, 16) || (q && !aligned(q, 16)) || (qt && !aligned(qt, 16)) || (s && !aligned(s, 4)) ||
       (st && !aligned(st, 4)))
@@ -83,6 +92,27 @@ fp8rl_status quant_act_impl(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
   if (fp8rl_status e = check_device()) return e;
   if (qt == nullptr) return launched(launch_quant_rows_1x128(x, M, K, q, s, pow2, as_stream(stream)));
   return launched(launch_quant_act_tile(x, M, K, q, s, qt, st, pow2, as_stream(stream)));
+}
+
+bool act_outputs_aligned(uint8_t* q, float* s, uint8_t* qt, float* st) {
+  return !((q && !aligned(q, 16)) || (qt && !aligned(qt, 16)) || (s && !aligned(s, 4)) || (st && !aligned(st, 4)));
+}
+
+fp8rl_status swiglu_check(const uint16_t* gu, int64_t M, int64_t F) {
+  if (fp8rl_status e = check_dims(M, 2 * F)) return e;
+  if (F % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (M > 0 && F > 0 && gu == nullptr) return FP8RL_ERR_NULL;
+  if (gu != nullptr && !aligned(gu, 16)) return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
+}
+
+fp8rl_status rms_check(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps, const float* rstd) {
+  if (fp8rl_status e = check_dims(M, K)) return e;
+  if (K % 128 != 0 || K > 65536 || M > INT32_MAX) return FP8RL_ERR_SHAPE;
+  if (!(eps > 0.0f) || !(eps <= 3.4028235e38f)) return FP8RL_ERR_VALUE;
+  if (M > 0 && K > 0 && (x == nullptr || gamma == nullptr || rstd == nullptr)) return FP8RL_ERR_NULL;
+  if ((x && !aligned(x, 16)) || (gamma && !aligned(gamma, 16)) || (rstd && !aligned(rstd, 4))) return FP8RL_ERR_ALIGN;
+  return FP8RL_OK;
 }
 
 fp8rl_status quant_w_impl(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt, bool pow2,
@@ -109,6 +139,47 @@ fp8rl_status fp8_quant_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_
 fp8rl_status fp8_quant_act_1x128_pow2(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                       float* st, void* stream) {
   return quant_act_impl(x, M, K, q, s, qt, st, true, stream);
+}
+
+fp8rl_status fp8_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, void* stream) {
+  if (fp8rl_status e = swiglu_check(gu, M, F)) return e;
+  if (M == 0 || F == 0) return FP8RL_OK;
+  if (h == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(h, 16)) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_swiglu_bf16(gu, M, F, h, as_stream(stream)));
+}
+
+fp8rl_status fp8_swiglu_quant_1x128(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s, uint8_t* qt,
+                                    float* st, int pow2_scales, void* stream) {
+  if (fp8rl_status e = swiglu_check(gu, M, F)) return e;
+  if (M == 0 || F == 0) return FP8RL_OK;
+  if (fp8rl_status e = check_act_outputs(M, q, s, qt, st)) return e;
+  if (!act_outputs_aligned(q, s, qt, st)) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_swiglu_quant(gu, M, F, q, s, qt, st, pow2_scales != 0, as_stream(stream)));
+}
+
+fp8rl_status fp8_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps, uint16_t* y,
+                              float* rstd, void* stream) {
+  if (fp8rl_status e = rms_check(x, gamma, M, K, eps, rstd)) return e;
+  if (M == 0 || K == 0) return FP8RL_OK;
+  if (y == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(y, 16)) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_rmsnorm_bf16(x, gamma, M, K, eps, y, rstd, as_stream(stream)));
+}
+
+fp8rl_status fp8_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                                     float* rstd, uint8_t* q, float* s, uint8_t* qt, float* st, int pow2_scales,
+                                     void* stream) {
+  if (fp8rl_status e = rms_check(x, gamma, M, K, eps, rstd)) return e;
+  if (M == 0 || K == 0) return FP8RL_OK;
+  if (fp8rl_status e = check_act_outputs(M, q, s, qt, st)) return e;
+  if (!act_outputs_aligned(q, s, qt, st)) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_rmsnorm_quant(x, gamma, M, K, eps, rstd, q, s, qt, st, pow2_scales != 0,
+                                       as_stream(stream)));
 }
 
 fp8rl_status fp8_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,

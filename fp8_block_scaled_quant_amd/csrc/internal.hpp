@@ -14,6 +14,15 @@ hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_
                                  float* st, bool pow2, hipStream_t stream);
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                   bool pow2, hipStream_t stream);
+// Fused producers (producers.hip). gu is [M][2F] = [gate | up]; rstd [M].
+hipError_t launch_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, hipStream_t stream);
+hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s, uint8_t* qt,
+                               float* st, bool pow2, hipStream_t stream);
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                               uint16_t* y, float* rstd, hipStream_t stream);
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                                float* rstd, uint8_t* q, float* s, uint8_t* qt, float* st, bool pow2,
+                                hipStream_t stream);
 hipError_t launch_quant_mx_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0,
                                 hipStream_t stream);
 

@@ -1,0 +1,278 @@
+// Fused FP8 producers: SwiGLU(gate, up) -> FP8 and RMSNorm -> FP8 ([Jet-RL] "Quantization
+// scheme": the FP8 activations a linear layer consumes come straight out of the operator
+// before it, so no bf16 copy goes through memory; [SkyRL-FP8] "Performance analysis" on
+// the cost of separate quantization passes). Both compute the bf16 value a bf16 framework
+// would store, then quantize it exactly as the plain quantizers do (same kernels, through
+// a source that computes the values instead of loading them):
+//   SwiGLU : h = bf16(fl32(bf16(silu(g)) * u)),   GU[M][2F] = [gate | up];
+//   RMSNorm: y = bf16(fl32(gamma * bf16(fl32(x * r)))),
+//            r = fl32(1 / sqrt(mean(x^2) + eps)) per row (also returned).
+// bf16(silu(g)) is the correctly rounded bf16 of the exact silu(g): an fp32 evaluation
+// with a rounding-ambiguity test, an fp64 fallback for the inputs it cannot settle, and
+// the series g/2 + g^2/4 for tiny g (where g/2 can sit exactly on a bf16 tie).
+#include "device.hpp"
+#include "internal.hpp"
+#include "quant_kernels.hpp"
+
+namespace fp8rl {
+
+// bf16 bits of the nearest-even rounding of an fp64 value: round to odd at fp32 precision
+// (16 bits more than bf16, also in the subnormal range), then to nearest even.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
+  float f = __double2float_rz(d);
+  if ((double)f != d) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f32_to_bf16_bits(f);
+}
+
+__device__ __noinline__ uint32_t silu_bf16_bits_f64(float g) {
+  const double x = g;
+  double v;
+  if (x >= 0.0) {
+    v = x / (1.0 + exp(-x));
+  } else {
+    const double e = exp(x);
+    v = x * e / (1.0 + e);
+  }
+  return f64_to_bf16_bits(v);
+}
+
+// bf16 bits of silu(g) for a bf16 value g.
+__device__ __forceinline__ uint32_t silu_bf16_bits(float g) {
+  const float ag = fabsf(g);
+  if (ag < 0x1p-100f) {
+    // silu(g) = g/2 + g^2/4 + O(g^3). g/2 is exact in fp32; it is a bf16 tie only below
+    // 2^-125, where the g^2/4 term decides: up in magnitude for g > 0, down for g < 0.
+    const uint32_t u = __float_as_uint(g * 0.5f);
+    const uint32_t low = u & 0xffffu;
+    const uint32_t up = (low > 0x8000u || (low == 0x8000u && g > 0.0f)) ? 1u : 0u;
+    return (u >> 16) + up;
+  }
+  if (g < -80.0f) return silu_bf16_bits_f64(g);       // exp(g) is an fp32 subnormal or near it
+  // fp32: v = g / (1 + e) or g * e / (1 + e) with e = exp(-|g|) in (0, 1]; a few ulps of
+  // error in all. When v lies within 16 ulps of a bf16 rounding midpoint the rounding is
+  // settled in fp64.
+  const float e = expf(-ag);
+  const float v = (g >= 0.0f ? g : g * e) / (1.0f + e);
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t low = bits & 0xffffu;
+  if (low - 0x7ff0u <= 0x20u) return silu_bf16_bits_f64(g);
+  return f32_to_bf16_bits(v);
+}
+
+// Eight SwiGLU outputs from eight gate and eight up values (bf16 pairs in words).
+__device__ __forceinline__ uint32_t swiglu2(uint32_t gw, uint32_t uw) {
+  const float s0 = __uint_as_float(silu_bf16_bits(bf16_lo(gw)) << 16);
+  const float s1 = __uint_as_float(silu_bf16_bits(bf16_hi(gw)) << 16);
+  const uint32_t h0 = f32_to_bf16_bits(s0 * bf16_lo(uw));
+  const uint32_t h1 = f32_to_bf16_bits(s1 * bf16_hi(uw));
+  return h0 | (h1 << 16);
+}
+__device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
+  return make_uint4(swiglu2(g.x, u.x), swiglu2(g.y, u.y), swiglu2(g.z, u.z), swiglu2(g.w, u.w));
+}
+
+// SwiGLU of GU[M][2F], presented as h[M][F].
+struct SwigluSrc {
+  const uint16_t* gu;
+  int64_t F;
+  uint32_t gpr;   // 1x128 groups per row = F / 128
+  __device__ __forceinline__ uint4 load8(int64_t row, int64_t col) const {
+    const uint16_t* p = gu + row * 2 * F + col;
+    return swiglu8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + F));
+  }
+  __device__ __forceinline__ void load16(int64_t g, int part, uint4& a, uint4& b) const {
+    const int64_t row = (int64_t)((uint64_t)g / gpr);
+    const int64_t col = (g - row * gpr) * 128 + part * 16;
+    a = load8(row, col);
+    b = load8(row, col + 8);
+  }
+};
+
+// RMSNorm output for two x values and two gamma values (bf16 pairs in words).
+__device__ __forceinline__ uint32_t rms2(uint32_t xw, uint32_t gw, float r) {
+  const float t0 = __uint_as_float(f32_to_bf16_bits(bf16_lo(xw) * r) << 16);
+  const float t1 = __uint_as_float(f32_to_bf16_bits(bf16_hi(xw) * r) << 16);
+  return f32_to_bf16_bits(bf16_lo(gw) * t0) | (f32_to_bf16_bits(bf16_hi(gw) * t1) << 16);
+}
+__device__ __forceinline__ uint4 rms8(uint4 x, uint4 g, float r) {
+  return make_uint4(rms2(x.x, g.x, r), rms2(x.y, g.y, r), rms2(x.z, g.z, r), rms2(x.w, g.w, r));
+}
+
+// RMSNorm of X[M][K] with per-row r (already computed), presented as y[M][K].
+struct RmsSrc {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  const float* rstd;
+  int64_t C;
+  uint32_t gpr;
+  __device__ __forceinline__ uint4 load8(int64_t row, int64_t col) const {
+    return rms8(*reinterpret_cast<const uint4*>(x + row * C + col), *reinterpret_cast<const uint4*>(gamma + col),
+                rstd[row]);
+  }
+  __device__ __forceinline__ void load16(int64_t g, int part, uint4& a, uint4& b) const {
+    const int64_t row = (int64_t)((uint64_t)g / gpr);
+    const int64_t col = (g - row * gpr) * 128 + part * 16;
+    a = load8(row, col);
+    b = load8(row, col + 8);
+  }
+};
+
+// h[M][F] in bf16 (the unfused SwiGLU): 8 outputs per thread.
+__global__ __launch_bounds__(256) void k_swiglu_bf16(SwigluSrc src, uint16_t* __restrict__ h, int64_t n8) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;
+  const int64_t per_row = src.F / 8;
+  const int64_t row = t / per_row;
+  const int64_t col = (t - row * per_row) * 8;
+  *reinterpret_cast<uint4*>(h + row * src.F + col) = src.load8(row, col);
+}
+
+// One workgroup (256 threads) per row of X[M][K]; thread t holds the 16-value chunks
+// t, t + 256, ... (NCH of them, K <= NCH * 4096). The sum of squares is exact per element
+// in fp64 and reduced in a fixed order, so every launch of this kernel gives the same r.
+//   kMode 0: r only;  1: r and y (bf16);  2: r and the 1x128 FP8 rows of y.
+template <int NCH, int kMode, bool kPow2>
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ gamma, int64_t K, float eps,
+                                                      float* __restrict__ rstd, uint16_t* __restrict__ y,
+                                                      uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ double red[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (int)(K / 16);
+  const uint16_t* xr = x + row * K;
+  uint4 a[NCH], b[NCH];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i;
+    a[i] = make_uint4(0, 0, 0, 0);
+    b[i] = a[i];
+    if (c < nch) {
+      const uint4* p = reinterpret_cast<const uint4*>(xr + c * 16);
+      a[i] = p[0];
+      b[i] = p[1];
+    }
+    const uint32_t w[8] = {a[i].x, a[i].y, a[i].z, a[i].w, b[i].x, b[i].y, b[i].z, b[i].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+      ss = __builtin_fma(lo, lo, ss);
+      ss = __builtin_fma(hi, hi, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+  if (tid == 0) rstd[row] = r;
+  if constexpr (kMode == 0) return;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i;
+    const bool valid = c < nch;
+    uint4 ya = make_uint4(0, 0, 0, 0), yb = ya;
+    if (valid) {
+      const uint4* gp = reinterpret_cast<const uint4*>(gamma + c * 16);
+      ya = rms8(a[i], gp[0], r);
+      yb = rms8(b[i], gp[1], r);
+    }
+    if constexpr (kMode == 1) {
+      if (valid) {
+        uint4* yp = reinterpret_cast<uint4*>(y + row * K + c * 16);
+        yp[0] = ya;
+        yp[1] = yb;
+      }
+    } else {
+      // 8 consecutive lanes hold one 1x128 group; every lane takes part in the shuffles.
+      float amax = fmaxf(fmaxf(fmaxf(absmax2(ya.x), absmax2(ya.y)), fmaxf(absmax2(ya.z), absmax2(ya.w))),
+                         fmaxf(fmaxf(absmax2(yb.x), absmax2(yb.y)), fmaxf(absmax2(yb.z), absmax2(yb.w))));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      const BlockScale bs = group_scale<kPow2>(amax);
+      if (valid) {
+        const uint2 lo = quant8(ya.x, ya.y, ya.z, ya.w, bs.r);
+        const uint2 hi = quant8(yb.x, yb.y, yb.z, yb.w, bs.r);
+        *reinterpret_cast<uint4*>(q + row * K + c * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        if ((c & 7) == 0) s[row * (K / 128) + c / 8] = bs.s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Launchers (arguments validated by the C ABI layer).
+// ---------------------------------------------------------------------------------------
+hipError_t launch_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, hipStream_t stream) {
+  const SwigluSrc src{gu, F, (uint32_t)(F / 128)};
+  const int64_t n8 = M * F / 8;
+  hipLaunchKernelGGL(k_swiglu_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, src, h, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s, uint8_t* qt,
+                               float* st, bool pow2, hipStream_t stream) {
+  const SwigluSrc src{gu, F, (uint32_t)(F / 128)};
+  if (qt == nullptr) {
+    const int64_t ngroups = M * (F / 128);
+    const dim3 grid((unsigned)((ngroups * 8 + 255) / 256));
+    if (pow2)
+      hipLaunchKernelGGL((k_quant_rows_1x128<SwigluSrc, true>), grid, dim3(256), 0, stream, src, q, s, ngroups);
+    else
+      hipLaunchKernelGGL((k_quant_rows_1x128<SwigluSrc, false>), grid, dim3(256), 0, stream, src, q, s, ngroups);
+  } else {
+    const dim3 grid((unsigned)((F / 128) * (M / 128)));
+    if (pow2)
+      hipLaunchKernelGGL((k_quant_tile<SwigluSrc, false, true>), grid, dim3(512), 0, stream, src, M, F, q, s, qt, st);
+    else
+      hipLaunchKernelGGL((k_quant_tile<SwigluSrc, false, false>), grid, dim3(512), 0, stream, src, M, F, q, s, qt,
+                         st);
+  }
+  return hipGetLastError();
+}
+
+template <int kMode, bool kPow2>
+static hipError_t launch_rms_rows(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                                  float* rstd, uint16_t* y, uint8_t* q, float* s, hipStream_t stream) {
+  const dim3 grid((unsigned)M), block(256);
+  const int64_t nch = K / 16;
+  if (nch <= 256)
+    hipLaunchKernelGGL((k_rmsnorm_rows<1, kMode, kPow2>), grid, block, 0, stream, x, gamma, K, eps, rstd, y, q, s);
+  else if (nch <= 512)
+    hipLaunchKernelGGL((k_rmsnorm_rows<2, kMode, kPow2>), grid, block, 0, stream, x, gamma, K, eps, rstd, y, q, s);
+  else if (nch <= 1024)
+    hipLaunchKernelGGL((k_rmsnorm_rows<4, kMode, kPow2>), grid, block, 0, stream, x, gamma, K, eps, rstd, y, q, s);
+  else if (nch <= 2048)
+    hipLaunchKernelGGL((k_rmsnorm_rows<8, kMode, kPow2>), grid, block, 0, stream, x, gamma, K, eps, rstd, y, q, s);
+  else
+    hipLaunchKernelGGL((k_rmsnorm_rows<16, kMode, kPow2>), grid, block, 0, stream, x, gamma, K, eps, rstd, y, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                               uint16_t* y, float* rstd, hipStream_t stream) {
+  return launch_rms_rows<1, false>(x, gamma, M, K, eps, rstd, y, nullptr, nullptr, stream);
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                                float* rstd, uint8_t* q, float* s, uint8_t* qt, float* st, bool pow2,
+                                hipStream_t stream) {
+  if (qt == nullptr)
+    return pow2 ? launch_rms_rows<2, true>(x, gamma, M, K, eps, rstd, nullptr, q, s, stream)
+                : launch_rms_rows<2, false>(x, gamma, M, K, eps, rstd, nullptr, q, s, stream);
+  // Column-wise groups need 128 whole rows per tile: r first, then the tile kernel.
+  if (hipError_t e = launch_rms_rows<0, false>(x, gamma, M, K, eps, rstd, nullptr, nullptr, nullptr, stream))
+    return e;
+  const RmsSrc src{x, gamma, rstd, K, (uint32_t)(K / 128)};
+  const dim3 grid((unsigned)((K / 128) * (M / 128)));
+  if (pow2)
+    hipLaunchKernelGGL((k_quant_tile<RmsSrc, false, true>), grid, dim3(512), 0, stream, src, M, K, q, s, qt, st);
+  else
+    hipLaunchKernelGGL((k_quant_tile<RmsSrc, false, false>), grid, dim3(512), 0, stream, src, M, K, q, s, qt, st);
+  return hipGetLastError();
+}
+
+}  // namespace fp8rl

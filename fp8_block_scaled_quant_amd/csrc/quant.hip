@@ -6,158 +6,9 @@
 // group amax by lane shuffles (or LDS for 128x1 / 128x128), and E4M3 conversion.
 #include "device.hpp"
 #include "internal.hpp"
+#include "quant_kernels.hpp"
 
 namespace fp8rl {
-
-// ---------------------------------------------------------------------------------------
-// 1x128 row groups. The groups of X[M][K] tile each row exactly, so group g starts at
-// element g * 128 and its scale is s[g] (row-major [M][K/128]). 8 lanes per group, 16
-// elements (32 bytes) per lane; one wave covers 8 consecutive groups = 2 KB of input.
-// ---------------------------------------------------------------------------------------
-template <bool kPow2>
-__global__ __launch_bounds__(256) void k_quant_rows_1x128(const uint16_t* __restrict__ x,
-                                                          uint8_t* __restrict__ q,
-                                                          float* __restrict__ s,
-                                                          int64_t ngroups) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t g = t >> 3;
-  const int part = (int)(t & 7);
-  const bool valid = g < ngroups;
-  uint4 a = make_uint4(0, 0, 0, 0), b = a;
-  if (valid) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + g * 128 + part * 16);
-    a = src[0];
-    b = src[1];
-  }
-  float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
-                     fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-  const BlockScale bs = group_scale<kPow2>(amax);
-  if (valid) {
-    const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
-    const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
-    *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    if (part == 0) s[g] = bs.s;
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// 128 x 128 tile kernel, 512 threads (8 waves), one tile per workgroup.
-//   kBlock = false: activation mode. Row output = 1x128 groups (q [R][C], s [R][C/128]),
-//                   column output = 128x1 groups written transposed (qt [C][R], st [C][R/128]).
-//   kBlock = true : weight mode. One scale for the whole 128x128 block (s [R/128][C/128]);
-//                   qt, if requested, is the byte transpose of q (same scale, same bytes).
-// Grid: blockIdx.x = rb * (C/128) + cb.
-// Thread t owns the 4x8 sub-block rows 4*(t/16) .. +3, columns 8*(t%16) .. +7. Each wave
-// load instruction then reads 4 whole 256-byte row segments, and each row-output store
-// writes whole 128-byte lines. Row amax: max over the 16 lanes sharing a row.
-// Column pass: each thread transposes its sub-block in registers (byte permutes) into a
-// column-major LDS tile, [column][128 rows of bf16], whose 16-byte chunks (8 rows) are
-// XOR-swizzled by column/8 so that neither the writes nor the reads conflict. Eight lanes
-// then own one column (16 rows each): column amax over those 8 lanes, and each store
-// instruction writes 8 whole 128-byte lines of qt.
-// ---------------------------------------------------------------------------------------
-template <bool kBlock, bool kPow2>
-__global__ __launch_bounds__(512) void k_quant_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                    uint8_t* __restrict__ q, float* __restrict__ s,
-                                                    uint8_t* __restrict__ qt, float* __restrict__ st) {
-  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];   // [column][row pair]
-  __shared__ float red[8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid & 15, rg = tid >> 4;                               // rg: 0..31
-  const int64_t ncb = C / 128;
-  const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
-  const bool want_rows = q != nullptr, want_cols = qt != nullptr;
-
-  const uint16_t* src = x + (rb * 128 + 4 * rg) * C + cb * 128 + c * 8;
-  uint4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(src + (int64_t)i * C);
-
-  double rblk = 0.0;
-  if (kBlock) {
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a = fmaxf(a, fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w))));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-    if (lane == 0) red[wave] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
-    const BlockScale bs = group_scale<kPow2>(a);
-    if (tid == 0) s[rb * ncb + cb] = bs.s;
-    rblk = bs.r;
-    if (want_rows) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
-            quant8(v[i].x, v[i].y, v[i].z, v[i].w, rblk);
-    }
-  } else if (want_rows) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w)));
-      a = fmaxf(a, __shfl_xor(a, 1));
-      a = fmaxf(a, __shfl_xor(a, 2));
-      a = fmaxf(a, __shfl_xor(a, 4));
-      a = fmaxf(a, __shfl_xor(a, 8));
-      const BlockScale bs = group_scale<kPow2>(a);
-      if (c == 0) s[(rb * 128 + 4 * rg + i) * ncb + cb] = bs.s;
-      *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
-          quant8(v[i].x, v[i].y, v[i].z, v[i].w, bs.r);
-    }
-  }
-  if (!want_cols) return;
-
-  // Column 8c+j, rows 4rg..4rg+3 = 8 bytes: half (rg & 1) of the 16-byte chunk rg >> 1,
-  // stored at chunk position (rg >> 1) ^ c.
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;   // high or low bf16 of each word
-    const int p = j >> 1;
-    const uint32_t a0 = p == 0 ? v[0].x : p == 1 ? v[0].y : p == 2 ? v[0].z : v[0].w;
-    const uint32_t a1 = p == 0 ? v[1].x : p == 1 ? v[1].y : p == 2 ? v[1].z : v[1].w;
-    const uint32_t a2 = p == 0 ? v[2].x : p == 1 ? v[2].y : p == 2 ? v[2].z : v[2].w;
-    const uint32_t a3 = p == 0 ? v[3].x : p == 1 ? v[3].y : p == 2 ? v[3].z : v[3].w;
-    *reinterpret_cast<uint2*>(tile + (8 * c + j) * 64 + (((rg >> 1) ^ c) & 15) * 4 + (rg & 1) * 2) =
-        make_uint2(__builtin_amdgcn_perm(a1, a0, sel), __builtin_amdgcn_perm(a3, a2, sel));
-  }
-  __syncthreads();
-
-  // Wave w: columns 16w .. 16w+15, 8 per round; lane: column +lane/8, rows 16k .. 16k+15.
-  // The two chunks are read in an order (odd first for half the lanes) that keeps every
-  // group of 8 or 16 lanes on distinct banks.
-  const int k = lane & 7;
-#pragma unroll
-  for (int rd = 0; rd < 2; ++rd) {
-    const int col = 16 * wave + 8 * rd + (lane >> 3);
-    const int sw = (2 * wave + rd) & 15;                            // = (col / 8) & 15
-    const int a = 2 * k + ((k >> 2) ^ (col & 1));
-    const uint4 A = *reinterpret_cast<const uint4*>(tile + col * 64 + ((a ^ sw) * 4));
-    const uint4 B = *reinterpret_cast<const uint4*>(tile + col * 64 + (((a ^ 1) ^ sw) * 4));
-    const bool even = (a & 1) == 0;
-    const uint4 lo = even ? A : B, hi = even ? B : A;               // rows 16k..+7, 16k+8..+15
-    double r;
-    if (kBlock) {
-      r = rblk;
-    } else {
-      float m = fmaxf(fmaxf(fmaxf(absmax2(lo.x), absmax2(lo.y)), fmaxf(absmax2(lo.z), absmax2(lo.w))),
-                      fmaxf(fmaxf(absmax2(hi.x), absmax2(hi.y)), fmaxf(absmax2(hi.z), absmax2(hi.w))));
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      const BlockScale bs = group_scale<kPow2>(m);
-      r = bs.r;
-      if (k == 0) st[(cb * 128 + col) * (R / 128) + rb] = bs.s;
-    }
-    const uint2 o0 = quant8(lo.x, lo.y, lo.z, lo.w, r);
-    const uint2 o1 = quant8(hi.x, hi.y, hi.z, hi.w, r);
-    *reinterpret_cast<uint4*>(qt + (cb * 128 + col) * R + rb * 128 + 16 * k) = make_uint4(o0.x, o0.y, o1.x, o1.y);
-  }
-}
 
 // ---------------------------------------------------------------------------------------
 // MXFP8 1x32 groups: 2 lanes per group, 16 elements (32 bytes) per lane. Group g starts
@@ -202,30 +53,37 @@ hipError_t launch_quant_rows_1x128(const uint16_t* x, int64_t M, int64_t K, uint
   const int64_t ngroups = M * (K / 128);
   const int64_t threads = ngroups * 8;
   const int64_t blocks = (threads + 255) / 256;
+  const PlainSrc src{x, K};
   if (pow2)
-    hipLaunchKernelGGL(k_quant_rows_1x128<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, s, ngroups);
+    hipLaunchKernelGGL((k_quant_rows_1x128<PlainSrc, true>), dim3((unsigned)blocks), dim3(256), 0, stream, src, q, s,
+                       ngroups);
   else
-    hipLaunchKernelGGL(k_quant_rows_1x128<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, s, ngroups);
+    hipLaunchKernelGGL((k_quant_rows_1x128<PlainSrc, false>), dim3((unsigned)blocks), dim3(256), 0, stream, src, q, s,
+                       ngroups);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                  float* st, bool pow2, hipStream_t stream) {
   const dim3 grid((unsigned)((K / 128) * (M / 128)));
+  const PlainSrc src{x, K};
   if (pow2)
-    hipLaunchKernelGGL((k_quant_tile<false, true>), grid, dim3(512), 0, stream, x, M, K, q, s, qt, st);
+    hipLaunchKernelGGL((k_quant_tile<PlainSrc, false, true>), grid, dim3(512), 0, stream, src, M, K, q, s, qt, st);
   else
-    hipLaunchKernelGGL((k_quant_tile<false, false>), grid, dim3(512), 0, stream, x, M, K, q, s, qt, st);
+    hipLaunchKernelGGL((k_quant_tile<PlainSrc, false, false>), grid, dim3(512), 0, stream, src, M, K, q, s, qt, st);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                   bool pow2, hipStream_t stream) {
   const dim3 grid((unsigned)((K / 128) * (N / 128)));
+  const PlainSrc src{w, K};
   if (pow2)
-    hipLaunchKernelGGL((k_quant_tile<true, true>), grid, dim3(512), 0, stream, w, N, K, q, s, qt, (float*)nullptr);
+    hipLaunchKernelGGL((k_quant_tile<PlainSrc, true, true>), grid, dim3(512), 0, stream, src, N, K, q, s, qt,
+                       (float*)nullptr);
   else
-    hipLaunchKernelGGL((k_quant_tile<true, false>), grid, dim3(512), 0, stream, w, N, K, q, s, qt, (float*)nullptr);
+    hipLaunchKernelGGL((k_quant_tile<PlainSrc, true, false>), grid, dim3(512), 0, stream, src, N, K, q, s, qt,
+                       (float*)nullptr);
   return hipGetLastError();
 }
 

@@ -47,7 +47,8 @@ typedef enum {
   FP8RL_ERR_RECIPE = 4,    /* unknown / unsupported recipe or dtype, or install descriptors disagree */
   FP8RL_ERR_DEVICE = 5,    /* current HIP device is not gfx950, or it could not be queried */
   FP8RL_ERR_LAUNCH = 6,    /* kernel launch failed */
-  FP8RL_ERR_WORKSPACE = 7  /* workspace missing or smaller than fp8rl_fwd_workspace_bytes() */
+  FP8RL_ERR_WORKSPACE = 7, /* workspace missing or smaller than fp8rl_fwd_workspace_bytes() */
+  FP8RL_ERR_VALUE = 8      /* a scalar argument is out of range (e.g. eps not positive and finite) */
 } fp8rl_status;
 
 /* Scaling recipes ([SkyRL-FP8] TL;DR and "Deep dive: FP8 quantization with FP32 and
@@ -64,7 +65,7 @@ typedef enum {
 } fp8rl_out;
 
 /* ABI version of this header. */
-#define FP8RL_ABI_VERSION 2
+#define FP8RL_ABI_VERSION 3
 int fp8rl_abi_version(void);
 const char* fp8rl_status_str(fp8rl_status status);
 
@@ -116,6 +117,42 @@ fp8rl_status fp8_quant_w_128x128_pow2(const uint16_t* w, int64_t N, int64_t K,
  *   x : bf16 [R][K];  q uint8 [R][K];  e8m0 uint8 [R][K/32].   Rules: K % 32 == 0. */
 fp8rl_status mxfp8_quant_1x32(const uint16_t* x, int64_t R, int64_t K,
                               uint8_t* q, uint8_t* e8m0, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Fused producers ([Jet-RL] "Quantization scheme": the FP8 activations a linear layer
+ * consumes are produced by the operator before it, fused with the quantization, so no bf16
+ * copy goes through memory). Each computes the bf16 value a bf16 framework stores and
+ * quantizes it exactly as fp8_quant_act_1x128 (or its _pow2 form, pow2_scales != 0) would:
+ * the bytes equal those of the unfused pair of calls. The _bf16 calls are the unfused
+ * producers (same values, stored as bf16).
+ * ------------------------------------------------------------------------------------- */
+
+/* SwiGLU. gu: bf16 [M][2F], the fused gate/up output: gate in columns [0, F), up in
+ * columns [F, 2F). h[m][f] = bf16(fl32(bf16(silu(gate)) * up)) with silu(g) = g/(1+e^-g)
+ * rounded once (nearest even) from its exact value. fp8_swiglu_bf16 writes h: bf16 [M][F].
+ * fp8_swiglu_quant_1x128 quantizes h: q,s / qt,st as in fp8_quant_act_1x128 with K = F.
+ * Rules: F % 128 == 0; M % 128 == 0 when qt is requested; at least one output pair for
+ * the quantizing form. Non-finite inputs, and products beyond the bf16 range, are outside
+ * the contract. */
+fp8rl_status fp8_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, void* stream);
+fp8rl_status fp8_swiglu_quant_1x128(const uint16_t* gu, int64_t M, int64_t F,
+                                    uint8_t* q, float* s, uint8_t* qt, float* st,
+                                    int pow2_scales, void* stream);
+
+/* RMSNorm. x: bf16 [M][K]; gamma: bf16 [K]; eps: positive, finite (FP8RL_ERR_VALUE).
+ * r[m] = fl32(1 / sqrt(mean_k x[m][k]^2 + eps)) (rounded once from the exact value, up to
+ * fp64 evaluation error), written to rstd fp32 [M] (required: the backward pass keeps it);
+ * y[m][k] = bf16(fl32(gamma[k] * bf16(fl32(x[m][k] * r[m])))).
+ * fp8_rmsnorm_bf16 writes y: bf16 [M][K]. fp8_rmsnorm_quant_1x128 quantizes y: q,s / qt,st
+ * as in fp8_quant_act_1x128.
+ * Rules: K % 128 == 0, K <= 65536; M % 128 == 0 when qt is requested; at least one output
+ * pair for the quantizing form. gamma[k] * sqrt(K) beyond the bf16 range is outside the
+ * contract. */
+fp8rl_status fp8_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                              uint16_t* y, float* rstd, void* stream);
+fp8rl_status fp8_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                                     float* rstd, uint8_t* q, float* s, uint8_t* qt, float* st,
+                                     int pow2_scales, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Block-scaled GEMMs (FP8 operands, fp32 accumulation). Each is the product of the

@@ -40,7 +40,6 @@ from __future__ import annotations
 
 import decimal
 import math
-from fractions import Fraction
 from functools import lru_cache
 
 import numpy as np
@@ -49,6 +48,7 @@ from .fp8_formats import round_to_bf16
 from .quantize import (quant_act_1x128, quant_act_128x1, quant_act_1x128_pow2, quant_act_128x1_pow2)
 
 _CTX = decimal.Context(prec=60, Emin=-10 ** 6, Emax=10 ** 6, traps=[])
+_WIDE = decimal.Context(prec=400, Emin=-10 ** 6, Emax=10 ** 6, traps=[decimal.Inexact])
 
 
 def _bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -57,8 +57,8 @@ def _bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 def _round_decimal_to_bf16(v: decimal.Decimal, negative: bool) -> float:
-    """Round a 60-digit value to bf16, ties to even, by an exact (rational) comparison with
-    the midpoint of its two bf16 neighbours. `negative` gives the sign of a value that
+    """Round a 60-digit value to bf16, ties to even, by an exact comparison with the
+    midpoint of its two bf16 neighbours. `negative` gives the sign of a value that
     underflowed to zero."""
     if v == 0:
         return -0.0 if negative else 0.0
@@ -75,13 +75,14 @@ def _round_decimal_to_bf16(v: decimal.Decimal, negative: bool) -> float:
     hi = nxt(lo, True)
     while decimal.Decimal(hi) <= a:
         lo, hi = hi, nxt(hi, True)
-    fa = Fraction(a)                                           # exact
     if math.isinf(hi):                                         # |silu(g)| <= |g| <= the bf16 maximum
         return -lo if v < 0 else lo
-    mid = (Fraction(lo) + Fraction(hi)) / 2                    # exact
-    if fa < mid:
+    # bf16 values are short binary fractions (at most ~100 significant decimal digits), so
+    # their midpoint is exact in 400 digits; the comparison with a is exact.
+    mid = _WIDE.divide(_WIDE.add(decimal.Decimal(lo), decimal.Decimal(hi)), 2)
+    if a < mid:
         r = lo
-    elif fa > mid:
+    elif a > mid:
         r = hi
     else:                                                      # a tie (silu of 0 only gives 0 above)
         r = lo if (np.array([lo], np.float32).view(np.uint32)[0] >> 16) % 2 == 0 else hi

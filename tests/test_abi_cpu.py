@@ -16,7 +16,7 @@ import fp8_block_scaled_quant_amd as F
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8rl.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_RECIPE, ERR_DEVICE, ERR_LAUNCH, ERR_WORKSPACE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_RECIPE, ERR_DEVICE, ERR_LAUNCH, ERR_WORKSPACE, ERR_VALUE = range(9)
 P = 0x10000          # an aligned, never-dereferenced fake device address
 P2 = 0x20000
 MIS = 0x10008        # 8-byte aligned only
@@ -39,7 +39,10 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["fp8_quant_act_1x128", "fp8_quant_w_128x128", "mxfp8_quant_1x32", "fp8_gemm_blockscaled_fwd",
               "fp8_gemm_blockscaled_dgrad", "fp8_gemm_blockscaled_wgrad", "fp8_grouped_gemm", "fp8_weight_install",
-              "fp8rl_abi_version", "fp8rl_status_str", "fp8rl_fwd_workspace_bytes"]:
+              "fp8rl_abi_version", "fp8rl_status_str", "fp8rl_fwd_workspace_bytes", "fp8_quant_act_1x128_pow2",
+              "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd", "fp8_gemm_blockscaled_pow2_dgrad",
+              "fp8_gemm_blockscaled_pow2_wgrad", "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16",
+              "fp8_rmsnorm_quant_1x128"]:
         assert n in names
 
 
@@ -54,8 +57,8 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8rl_abi_version() == 2
-    for code in range(8):
+    assert lib.fp8rl_abi_version() == 3
+    for code in range(9):
         assert len(lib.fp8rl_status_str(code)) > 0
     assert lib.fp8rl_status_str(99) == b"unknown status"
 
@@ -117,6 +120,35 @@ def test_gemm_validation(lib):
     assert wg(P, P, P, P, 128, 128, 128, None, 0, None) == ERR_NULL
     assert wg(P, P, P, P, 128, 128, 128, MIS, 0, None) == ERR_ALIGN
     assert wg(P, P, P, P, 128, 0, 128, P, 0, None) == OK
+
+
+def test_producer_validation(lib):
+    sb = lib.fp8_swiglu_bf16
+    assert sb(P, 4, 100, P, None) == ERR_SHAPE                          # F % 128
+    assert sb(None, 4, 128, P, None) == ERR_NULL
+    assert sb(P, 4, 128, None, None) == ERR_NULL
+    assert sb(MIS, 4, 128, P, None) == ERR_ALIGN
+    assert sb(P, 0, 128, None, None) == OK
+    sq = lib.fp8_swiglu_quant_1x128
+    assert sq(P, 4, 128, P, None, None, None, 0, None) == ERR_NULL      # half a pair
+    assert sq(P, 4, 128, None, None, None, None, 0, None) == ERR_NULL   # nothing requested
+    assert sq(P, 100, 128, None, None, P, P, 0, None) == ERR_SHAPE      # column groups need M % 128
+    assert sq(P, 4, 128, P, P + 2, None, None, 1, None) == ERR_ALIGN
+    assert sq(P, -1, 128, P, P, None, None, 0, None) == ERR_SHAPE
+    rb = lib.fp8_rmsnorm_bf16
+    assert rb(P, P, 4, 128, 0.0, P, P, None) == ERR_VALUE               # eps must be positive
+    assert rb(P, P, 4, 128, float("nan"), P, P, None) == ERR_VALUE
+    assert rb(P, P, 4, 128, float("inf"), P, P, None) == ERR_VALUE
+    assert rb(P, P, 4, 100, 1e-6, P, P, None) == ERR_SHAPE
+    assert rb(P, P, 4, 65536 + 128, 1e-6, P, P, None) == ERR_SHAPE      # K <= 65536
+    assert rb(P, None, 4, 128, 1e-6, P, P, None) == ERR_NULL
+    assert rb(P, P, 4, 128, 1e-6, P, None, None) == ERR_NULL            # rstd required
+    assert rb(P, P, 4, 128, 1e-6, MIS, P, None) == ERR_ALIGN
+    rq = lib.fp8_rmsnorm_quant_1x128
+    assert rq(P, P, 4, 128, 1e-6, P, None, None, P, P, 0, None) == ERR_SHAPE     # qt needs M % 128
+    assert rq(P, P, 4, 128, 1e-6, P, None, None, None, None, 0, None) == ERR_NULL
+    assert rq(P, P, 4, 128, -1.0, P, P, P, None, None, 0, None) == ERR_VALUE
+    assert rq(P, P, 0, 128, 1e-6, None, P, P, None, None, 0, None) == OK
 
 
 def test_grouped_validation(lib):
