@@ -63,6 +63,7 @@ MEASURED_TRAFFIC = {
     "decode_n24576": {"sha": "f0ab91830ef18133", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
     "grouped_gu": {"sha": "91547e59995d80c3", "gb": 0.5539},     # read 0.4868 + write 0.0672
     "install_gu": {"sha": "c4b1fdd282a2ee0f", "gb": 0.2014},     # read 0.1007 + write 0.1007
+    "swiglu_fp8": {"sha": "f498596b7d6a231f", "gb": 0.6476},     # read 0.4034 + write 0.2442
 }
 
 

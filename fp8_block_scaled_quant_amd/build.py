@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -45,8 +46,17 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _generate_tables():
+    """Regenerate the generated sources (silu_lut.inc) from their scripts."""
+    spec = importlib.util.spec_from_file_location("gen_silu_lut", os.path.join(CSRC, "gen_silu_lut.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.main(os.path.join(CSRC, "silu_lut.inc"))
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _generate_tables()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))

@@ -10,11 +10,16 @@
 // bf16(silu(g)) is the correctly rounded bf16 of the exact silu(g): an fp32 evaluation
 // with a rounding-ambiguity test, an fp64 fallback for the inputs it cannot settle, and
 // the series g/2 + g^2/4 for tiny g (where g/2 can sit exactly on a bf16 tie).
+#include <algorithm>
+
 #include "device.hpp"
 #include "internal.hpp"
 #include "quant_kernels.hpp"
 
 namespace fp8rl {
+
+// bf16(silu(g)) for 2^-16 <= |g| < 64, generated at build time by gen_silu_lut.py.
+#include "silu_lut.inc"
 
 // bf16 bits of the nearest-even rounding of an fp64 value: round to odd at fp32 precision
 // (16 bits more than bf16, also in the subnormal range), then to nearest even.
@@ -36,55 +41,103 @@ __device__ __noinline__ uint32_t silu_bf16_bits_f64(float g) {
   return f64_to_bf16_bits(v);
 }
 
-// bf16 bits of silu(g) for a bf16 value g.
-__device__ __forceinline__ uint32_t silu_bf16_bits(float g) {
+// bf16 bits of silu(g) for a bf16 value g, fast path. `slow` is set when the fp32 value
+// cannot settle the rounding (then silu_bf16_bits_f64 must be used).
+//  - |g| < 2^-100: silu(g) = g/2 + g^2/4 + O(g^3). g/2 is exact in fp32; it is a bf16 tie
+//    only below 2^-125, where the g^2/4 term decides: up in magnitude for g > 0, down for
+//    g < 0.
+//  - otherwise, with e = exp(-|g|) in (0, 1]: v = g / (1 + e) for g >= 0, g e / (1 + e)
+//    for g < 0. exp(-|g|) = 2^(-|g| Lh) 2^(-|g| Ll) with log2(e) = Lh + Ll and Lh of 15
+//    significant bits, so |g| Lh is exact for a bf16 g; v_exp_f32 gives the first factor
+//    and one FMA the second (1 - |g| Ll ln2). The quotient uses v_rcp_f32 and a Newton
+//    step. v is then within a few fp32 ulps of silu(g); when it lies within 16 ulps of a
+//    bf16 rounding midpoint, or g < -80 (exp(g) near the fp32 subnormal range), the fp64
+//    path decides.
+__device__ __forceinline__ uint32_t silu_bf16_bits_fast(float g, bool& slow) {
+  constexpr float kLog2eHi = 1.44268798828125f;           // log2(e) to 15 significant bits
+  constexpr float kNegLn2Log2eLo = -4.888495368504664e-06f; // -ln(2) * (log2(e) - kLog2eHi)
   const float ag = fabsf(g);
-  if (ag < 0x1p-100f) {
-    // silu(g) = g/2 + g^2/4 + O(g^3). g/2 is exact in fp32; it is a bf16 tie only below
-    // 2^-125, where the g^2/4 term decides: up in magnitude for g > 0, down for g < 0.
-    const uint32_t u = __float_as_uint(g * 0.5f);
-    const uint32_t low = u & 0xffffu;
-    const uint32_t up = (low > 0x8000u || (low == 0x8000u && g > 0.0f)) ? 1u : 0u;
-    return (u >> 16) + up;
-  }
-  if (g < -80.0f) return silu_bf16_bits_f64(g);       // exp(g) is an fp32 subnormal or near it
-  // fp32: v = g / (1 + e) or g * e / (1 + e) with e = exp(-|g|) in (0, 1]; a few ulps of
-  // error in all. When v lies within 16 ulps of a bf16 rounding midpoint the rounding is
-  // settled in fp64.
-  const float e = expf(-ag);
-  const float v = (g >= 0.0f ? g : g * e) / (1.0f + e);
+  const uint32_t ut = __float_as_uint(g * 0.5f);
+  const uint32_t lowt = ut & 0xffffu;
+  const uint32_t tiny_bits = (ut >> 16) + ((lowt > 0x8000u || (lowt == 0x8000u && g > 0.0f)) ? 1u : 0u);
+  const float e0 = __builtin_amdgcn_exp2f(-(ag * kLog2eHi));
+  const float e = __builtin_fmaf(e0, ag * kNegLn2Log2eLo, e0);
+  const float d = 1.0f + e;
+  const float num = g >= 0.0f ? g : g * e;
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float v0 = num * r;
+  const float v = __builtin_fmaf(__builtin_fmaf(-d, v0, num), r, v0);
   const uint32_t bits = __float_as_uint(v);
-  const uint32_t low = bits & 0xffffu;
-  if (low - 0x7ff0u <= 0x20u) return silu_bf16_bits_f64(g);
-  return f32_to_bf16_bits(v);
+  const bool tiny = ag < 0x1p-100f;
+  slow = !tiny && ((((bits & 0xffffu) - 0x7ff0u) <= 0x20u) || g < -80.0f);
+  return tiny ? tiny_bits : f32_to_bf16_bits(v);
 }
 
-// Eight SwiGLU outputs from eight gate and eight up values (bf16 pairs in words).
-__device__ __forceinline__ uint32_t swiglu2(uint32_t gw, uint32_t uw) {
-  const float s0 = __uint_as_float(silu_bf16_bits(bf16_lo(gw)) << 16);
-  const float s1 = __uint_as_float(silu_bf16_bits(bf16_hi(gw)) << 16);
-  const uint32_t h0 = f32_to_bf16_bits(s0 * bf16_lo(uw));
-  const uint32_t h1 = f32_to_bf16_bits(s1 * bf16_hi(uw));
-  return h0 | (h1 << 16);
+// bf16 bits of silu(g) computed (for the bf16 values outside the table).
+__device__ __forceinline__ uint32_t silu_bf16_bits_computed(float g) {
+  bool slow;
+  const uint32_t b = silu_bf16_bits_fast(g, slow);
+  return slow ? silu_bf16_bits_f64(g) : b;
 }
-__device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
-  return make_uint4(swiglu2(g.x, u.x), swiglu2(g.y, u.y), swiglu2(g.z, u.z), swiglu2(g.w, u.w));
+
+// Eight SwiGLU outputs h = bf16(fl32(bf16(silu(g)) * u)) from eight gate and eight up values
+// (bf16 pairs in words). bf16(silu(g)) comes from the LDS table for 2^-16 <= |g| < 64
+// (almost every gate value); the others are computed after the table lookups.
+__device__ __forceinline__ uint4 swiglu8(uint4 gw, uint4 uw, const uint16_t* lut) {
+  const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, us[4] = {uw.x, uw.y, uw.z, uw.w};
+  uint32_t sb[8];
+  uint32_t miss = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t p = (j & 1) ? (gs[j >> 1] >> 16) : (gs[j >> 1] & 0xffffu);
+    const uint32_t off = (p & 0x7fffu) - FP8RL_SILU_LUT_LO;
+    const bool in = off < FP8RL_SILU_LUT_N;
+    sb[j] = lut[in ? off + (p >> 15) * FP8RL_SILU_LUT_N : 0u];
+    miss |= (in ? 0u : 1u) << j;
+  }
+  if (miss != 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((miss >> j) & 1u) {
+        const uint32_t w = gs[j >> 1];
+        sb[j] = silu_bf16_bits_computed((j & 1) ? bf16_hi(w) : bf16_lo(w));
+      }
+  }
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = us[j >> 1];
+    h[j] = f32_to_bf16_bits(__uint_as_float(sb[j] << 16) * ((j & 1) ? bf16_hi(w) : bf16_lo(w)));
+  }
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
 // SwiGLU of GU[M][2F], presented as h[M][F].
 struct SwigluSrc {
+  struct Raw {
+    uint4 g, u;
+  };
+  static constexpr int kLdsBytes = (int)(2 * FP8RL_SILU_LUT_N * sizeof(uint16_t));
   const uint16_t* gu;
   int64_t F;
   uint32_t gpr;   // 1x128 groups per row = F / 128
-  __device__ __forceinline__ uint4 load8(int64_t row, int64_t col) const {
+  __device__ __forceinline__ Raw fetch8(int64_t row, int64_t col) const {
     const uint16_t* p = gu + row * 2 * F + col;
-    return swiglu8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + F));
+    return Raw{*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + F)};
   }
-  __device__ __forceinline__ void load16(int64_t g, int part, uint4& a, uint4& b) const {
+  __device__ __forceinline__ void fetch16(int64_t g, int part, Raw& a, Raw& b) const {
     const int64_t row = (int64_t)((uint64_t)g / gpr);
     const int64_t col = (g - row * gpr) * 128 + part * 16;
-    a = load8(row, col);
-    b = load8(row, col + 8);
+    a = fetch8(row, col);
+    b = fetch8(row, col + 8);
+  }
+  __device__ __forceinline__ void prepare(void* lds, int tid, int nt) const {
+    const uint4* src = reinterpret_cast<const uint4*>(kSiluLut);
+    uint4* dst = reinterpret_cast<uint4*>(lds);
+    for (int i = tid; i < kLdsBytes / 16; i += nt) dst[i] = src[i];
+  }
+  __device__ __forceinline__ uint4 make(const Raw& r, const void* lds) const {
+    return swiglu8(r.g, r.u, reinterpret_cast<const uint16_t*>(lds));
   }
 };
 
@@ -100,32 +153,46 @@ __device__ __forceinline__ uint4 rms8(uint4 x, uint4 g, float r) {
 
 // RMSNorm of X[M][K] with per-row r (already computed), presented as y[M][K].
 struct RmsSrc {
+  struct Raw {
+    uint4 x, g;
+    float r;
+  };
+  static constexpr int kLdsBytes = 0;
   const uint16_t* x;
   const uint16_t* gamma;
   const float* rstd;
   int64_t C;
   uint32_t gpr;
-  __device__ __forceinline__ uint4 load8(int64_t row, int64_t col) const {
-    return rms8(*reinterpret_cast<const uint4*>(x + row * C + col), *reinterpret_cast<const uint4*>(gamma + col),
-                rstd[row]);
+  __device__ __forceinline__ Raw fetch8(int64_t row, int64_t col) const {
+    return Raw{*reinterpret_cast<const uint4*>(x + row * C + col), *reinterpret_cast<const uint4*>(gamma + col),
+               rstd[row]};
   }
-  __device__ __forceinline__ void load16(int64_t g, int part, uint4& a, uint4& b) const {
+  __device__ __forceinline__ void fetch16(int64_t g, int part, Raw& a, Raw& b) const {
     const int64_t row = (int64_t)((uint64_t)g / gpr);
     const int64_t col = (g - row * gpr) * 128 + part * 16;
-    a = load8(row, col);
-    b = load8(row, col + 8);
+    a = fetch8(row, col);
+    b = fetch8(row, col + 8);
   }
+  __device__ __forceinline__ void prepare(void*, int, int) const {}
+  __device__ __forceinline__ uint4 make(const Raw& r, const void*) const { return rms8(r.x, r.g, r.r); }
 };
 
-// h[M][F] in bf16 (the unfused SwiGLU): 8 outputs per thread.
+// h[M][F] in bf16 (the unfused SwiGLU): 8 outputs per thread and step, grid-stride.
 __global__ __launch_bounds__(256) void k_swiglu_bf16(SwigluSrc src, uint16_t* __restrict__ h, int64_t n8) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n8) return;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SwigluSrc::kLdsBytes];
+  src.prepare(lds, threadIdx.x, 256);
+  __syncthreads();
   const int64_t per_row = src.F / 8;
-  const int64_t row = t / per_row;
-  const int64_t col = (t - row * per_row) * 8;
-  *reinterpret_cast<uint4*>(h + row * src.F + col) = src.load8(row, col);
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n8; t += (int64_t)gridDim.x * 256) {
+    const int64_t row = t / per_row;
+    const int64_t col = (t - row * per_row) * 8;
+    *reinterpret_cast<uint4*>(h + row * src.F + col) = src.make(src.fetch8(row, col), lds);
+  }
 }
+
+// Workgroups for the grid-stride kernels that fill an LDS table first: enough to fill the
+// chip several times over, few enough that the table copies stay small.
+constexpr int64_t kTableGrid = 256 * 8;
 
 // One workgroup (256 threads) per row of X[M][K]; thread t holds the 16-value chunks
 // t, t + 256, ... (NCH of them, K <= NCH * 4096). The sum of squares is exact per element
@@ -209,7 +276,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t* __restrict
 hipError_t launch_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, hipStream_t stream) {
   const SwigluSrc src{gu, F, (uint32_t)(F / 128)};
   const int64_t n8 = M * F / 8;
-  hipLaunchKernelGGL(k_swiglu_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, src, h, n8);
+  const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, kTableGrid);
+  hipLaunchKernelGGL(k_swiglu_bf16, dim3((unsigned)blocks), dim3(256), 0, stream, src, h, n8);
   return hipGetLastError();
 }
 
@@ -218,7 +286,7 @@ hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t M, int64_t F, uint8_t
   const SwigluSrc src{gu, F, (uint32_t)(F / 128)};
   if (qt == nullptr) {
     const int64_t ngroups = M * (F / 128);
-    const dim3 grid((unsigned)((ngroups * 8 + 255) / 256));
+    const dim3 grid((unsigned)std::min<int64_t>((ngroups * 8 + 255) / 256, kTableGrid));
     if (pow2)
       hipLaunchKernelGGL((k_quant_rows_1x128<SwigluSrc, true>), grid, dim3(256), 0, stream, src, q, s, ngroups);
     else

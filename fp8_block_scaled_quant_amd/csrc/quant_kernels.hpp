@@ -1,8 +1,13 @@
 // The 1x128 row and 128x128 tile quantizer kernels, generic over where their bf16 input
-// comes from. A source presents a virtual bf16 matrix [R][C] (C % 128 == 0):
-//   load8(row, col)         -> the 8 bf16 values at (row, col .. col+7), col % 8 == 0;
-//   load16(g, part, a, b)   -> the 16 values of 1x128 group g, part `part` (0..7), i.e.
-//                              row g / (C/128), columns (g % (C/128)) * 128 + 16 * part ...
+// comes from. A source presents a virtual bf16 matrix [R][C] (C % 128 == 0) in two steps,
+// so that a thread issues all of its loads before any of the arithmetic:
+//   fetch8(row, col)        -> the raw inputs (Src::Raw) of the 8 values at (row, col .. col+7),
+//                              col % 8 == 0;
+//   fetch16(g, part, a, b)  -> those of the 16 values of 1x128 group g, part `part` (0..7),
+//                              i.e. row g / (C/128), columns (g % (C/128)) * 128 + 16 * part ...;
+//   make(raw, lds)          -> the 8 bf16 values (4 words) from their raw inputs.
+// A source may keep a table in LDS: Src::kLdsBytes bytes, filled by prepare(lds, tid, nt)
+// (all threads of the workgroup, then a barrier) before the first make().
 // Plain quantization reads the matrix from memory; the fused producers compute it from
 // their own inputs (SwiGLU of the gate/up output, RMSNorm of the residual stream), so the
 // bf16 values never go through memory. Method: [AIS] symmetric quantizer equation on the
@@ -15,17 +20,27 @@ namespace fp8rl {
 
 // bf16 matrix [R][C] in memory, row-major.
 struct PlainSrc {
+  typedef uint4 Raw;
+  static constexpr int kLdsBytes = 0;
   const uint16_t* x;
   int64_t C;
-  __device__ __forceinline__ uint4 load8(int64_t row, int64_t col) const {
+  __device__ __forceinline__ Raw fetch8(int64_t row, int64_t col) const {
     return *reinterpret_cast<const uint4*>(x + row * C + col);
   }
   // Groups tile the rows exactly, so group g starts at element g * 128.
-  __device__ __forceinline__ void load16(int64_t g, int part, uint4& a, uint4& b) const {
+  __device__ __forceinline__ void fetch16(int64_t g, int part, Raw& a, Raw& b) const {
     const uint4* p = reinterpret_cast<const uint4*>(x + g * 128 + part * 16);
     a = p[0];
     b = p[1];
   }
+  __device__ __forceinline__ void prepare(void*, int, int) const {}
+  __device__ __forceinline__ uint4 make(const Raw& r, const void*) const { return r; }
+};
+
+// LDS for a source's table (at least 16 bytes so that the declaration is valid).
+template <class Src>
+struct SrcLds {
+  static constexpr int kBytes = Src::kLdsBytes > 0 ? Src::kLdsBytes : 16;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -36,23 +51,36 @@ struct PlainSrc {
 template <class Src, bool kPow2>
 __global__ __launch_bounds__(256) void k_quant_rows_1x128(Src src, uint8_t* __restrict__ q, float* __restrict__ s,
                                                           int64_t ngroups) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t g = t >> 3;
-  const int part = (int)(t & 7);
-  const bool valid = g < ngroups;
-  uint4 a = make_uint4(0, 0, 0, 0), b = a;
-  if (valid) src.load16(g, part, a, b);
-  float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
-                     fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-  const BlockScale bs = group_scale<kPow2>(amax);
-  if (valid) {
-    const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
-    const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
-    *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    if (part == 0) s[g] = bs.s;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SrcLds<Src>::kBytes];
+  if constexpr (Src::kLdsBytes > 0) {
+    src.prepare(lds, threadIdx.x, 256);
+    __syncthreads();
+  }
+  const int part = (int)(threadIdx.x & 7);
+  // Each workgroup takes 32 consecutive groups per step (one step when the grid covers
+  // all groups, as for plain quantization).
+  for (int64_t g0 = (int64_t)blockIdx.x * 32; g0 < ngroups; g0 += (int64_t)gridDim.x * 32) {
+    const int64_t g = g0 + (threadIdx.x >> 3);
+    const bool valid = g < ngroups;
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (valid) {
+      typename Src::Raw ra, rb;
+      src.fetch16(g, part, ra, rb);
+      a = src.make(ra, lds);
+      b = src.make(rb, lds);
+    }
+    float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
+                       fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const BlockScale bs = group_scale<kPow2>(amax);
+    if (valid) {
+      const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
+      const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
+      *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      if (part == 0) s[g] = bs.s;
+    }
   }
 }
 
@@ -78,15 +106,23 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
                                                     float* __restrict__ st) {
   __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];   // [column][row pair]
   __shared__ float red[8];
+  __shared__ __attribute__((aligned(16))) uint8_t src_lds[SrcLds<Src>::kBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid & 15, rg = tid >> 4;                               // rg: 0..31
   const int64_t ncb = C / 128;
   const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
   const bool want_rows = q != nullptr, want_cols = qt != nullptr;
 
+  typename Src::Raw raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = src.fetch8(rb * 128 + 4 * rg + i, cb * 128 + c * 8);
+  if constexpr (Src::kLdsBytes > 0) {
+    src.prepare(src_lds, tid, 512);
+    __syncthreads();
+  }
   uint4 v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = src.load8(rb * 128 + 4 * rg + i, cb * 128 + c * 8);
+  for (int i = 0; i < 4; ++i) v[i] = src.make(raw[i], src_lds);
 
   double rblk = 0.0;
   if (kBlock) {
