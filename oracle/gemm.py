@@ -16,13 +16,20 @@ below any tolerance used against the GPU.
   i.e. the column-wise (transposed) quantized copies
   ([Jet-RL] "Quantization scheme", backward pass: DGrad and WGrad run in FP8,
   WGrad with 1x128 and 128x1 groups).
+* MXFP8 dense linear ([SkyRL-FP8]: the MXFP8 recipe for the linear layers; 1x32
+  blocks along each GEMM's contraction dimension):
+    forward  Y  = X . W^T    X [M][K], W [N][K], 1x32 groups along K;
+    DGrad    dX = dY . W     dY [M][N] 1x32 along N; W quantized 32x1 along N,
+                             i.e. the transposed copy Wt [K][N] with 1x32 groups;
+    WGrad    dW = dY^T . X   both 32x1 along the tokens: dYt [N][M], Xt [K][M].
 * grouped   per expert e, rows [off[e], off[e+1]) of the routed activations
   times expert e's weight, MXFP8 1x32 scales on both operands
   ([SkyRL-FP8] MoE experts hold most parameters; MXFP8 recipe).
 
 Pinned by tests/test_oracle_gemm.py: an exact-rational (fractions.Fraction)
 triple loop on small non-square shapes with per-element scale lookup; the
-grouped GEMM equals the dense GEMM per expert and for a single expert.
+grouped GEMM equals the dense GEMM per expert and for a single expert; the MXFP8 dense
+GEMMs by the same exact-rational loop with E8M0 scales looked up per 32-element block.
 """
 
 from __future__ import annotations
@@ -68,6 +75,23 @@ def gemm_wgrad(dyqt, sdyt, xqt, sxt) -> np.ndarray:
     """dW[N][K] = deq(dY)^T . deq(X), from the column-wise copies
     dYt[N][M] (st [N][M/128]) and Xt[K][M] (st [K][M/128]) (fp64)."""
     return dequant_1x128(dyqt, sdyt) @ dequant_1x128(xqt, sxt).T
+
+
+def gemm_mx_fwd(xq, ex, wq, ew) -> np.ndarray:
+    """Y[M][N] = deq(X) . deq(W)^T with 1x32 E8M0 groups along K on both (fp64)."""
+    return dequant_mx(xq, ex) @ dequant_mx(wq, ew).T
+
+
+def gemm_mx_dgrad(dyq, edy, wqt, ewt) -> np.ndarray:
+    """dX[M][K] = deq(dY) . deq(W), dY[M][N] with 1x32 groups along N and W given as its
+    32x1-quantized transposed copy Wt[K][N] (1x32 groups along N) (fp64)."""
+    return dequant_mx(dyq, edy) @ dequant_mx(wqt, ewt).T
+
+
+def gemm_mx_wgrad(dyqt, edyt, xqt, ext) -> np.ndarray:
+    """dW[N][K] = deq(dY)^T . deq(X) from the 32x1 (token-group) copies dYt[N][M] and
+    Xt[K][M] (fp64)."""
+    return dequant_mx(dyqt, edyt) @ dequant_mx(xqt, ext).T
 
 
 def grouped_gemm_mx(xq, ex, wq, ew, offsets) -> np.ndarray:

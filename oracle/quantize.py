@@ -15,7 +15,9 @@ qmax = 448 for E4M3, and Q = E4M3(X / s). Granularities:
   "Quantization scheme", backward pass);
 * MXFP8: one power-of-two scale per 1x32 group ([SkyRL-FP8] "When independent
   quantization breaks policy consistency" and the "Deep dive" section:
-  exponent-only scales, up to 2x coarser).
+  exponent-only scales, up to 2x coarser); for the backward operands of a dense
+  MXFP8 linear layer, 32x1 groups along the token (or output-feature) dimension,
+  written transposed.
 
 Readings where the pages are silent:
 
@@ -42,7 +44,8 @@ fractions and a nearest-in-table encoder on small groups, the invariants that
 the amax element of every group encodes to +-448 and that a group scaled by
 2**j keeps its codes with the scale scaled by 2**j, the half-ulp error bound,
 group locality (changing one element changes only its own group), and the MX
-invariant 224 < amax * 2**-e <= 448. The power-of-two block quantizers: the same
+invariant 224 < amax * 2**-e <= 448; the MX 32x1 (transposed) layout by a
+brute force over columns. The power-of-two block quantizers: the same
 brute force with exponent-only scales for all three layouts, 224 < amax / s <= 448,
 2**j equivariance, and fl32(amax / 448) <= s < 2 fl32(amax / 448).
 """
@@ -196,3 +199,18 @@ def quant_mx_1x32(x):
     e = mx_exponent(amax)
     q = encode_e4m3(np.ldexp(g, -e[:, :, None]))     # exact power-of-two scaling in fp64
     return q.reshape(R, K), (e + 127).astype(np.uint8)
+
+
+def quant_mx_32x1(x):
+    """MXFP8 quantization with 32x1 groups along the rows of X[R][K] (R % 32 == 0), written
+    transposed: the operand layout of a GEMM that contracts over R (the MXFP8 recipe's
+    backward operands, [SkyRL-FP8] "When independent quantization breaks policy
+    consistency": 1x32 blocks along the contraction dimension). Element (r, k) is quantized
+    with the group of rows 32 * (r // 32) .. +31 of column k.
+
+    Returns (qt uint8 [K][R], e8m0t uint8 [K][R/32])."""
+    x = _as_f32(x)
+    if x.shape[0] % MX_GROUP:
+        raise ValueError("R must be a multiple of 32 for 32x1 groups")
+    return quant_mx_1x32(np.ascontiguousarray(x.T))
+

@@ -124,3 +124,38 @@ def test_unit_scale_reduces_to_plain_product_of_codes():
     a = torch.from_numpy(xq).view(torch.float8_e4m3fn).to(torch.float64)
     b = torch.from_numpy(wq).view(torch.float8_e4m3fn).to(torch.float64)
     assert np.allclose(y, (a @ b.T).numpy(), rtol=0, atol=1e-9)
+
+
+def _e8(rng, shape):
+    return rng.integers(100, 150, size=shape, dtype=np.uint8)
+
+
+def _p2(b):
+    return Fraction(2) ** (int(b) - 127)
+
+
+def test_mx_dense_fwd_dgrad_wgrad_exact_rational():
+    rng = np.random.default_rng(34)
+    M, N, K = 5, 6, 96
+    xq, ex = _codes(rng, (M, K)), _e8(rng, (M, K // 32))
+    wq, ew = _codes(rng, (N, K)), _e8(rng, (N, K // 32))
+    y = G.gemm_mx_fwd(xq, ex, wq, ew)
+    assert y.shape == (M, N)
+    _check([(m, n) for m in range(M) for n in range(N)],
+           lambda m, n, k: _DEC_FR[xq[m, k]] * _p2(ex[m, k // 32]) * _DEC_FR[wq[n, k]] * _p2(ew[n, k // 32]), y, K)
+    # DGrad: dY [M][Nr] (groups along Nr), Wt [K][Nr] (W's 32x1 copy) -> dX [M][K]
+    Nr = 64
+    dyq, edy = _codes(rng, (M, Nr)), _e8(rng, (M, Nr // 32))
+    wqt, ewt = _codes(rng, (K, Nr)), _e8(rng, (K, Nr // 32))
+    dx = G.gemm_mx_dgrad(dyq, edy, wqt, ewt)
+    assert dx.shape == (M, K)
+    _check([(0, 0), (4, 95), (2, 33)],
+           lambda m, k, n: _DEC_FR[dyq[m, n]] * _p2(edy[m, n // 32]) * _DEC_FR[wqt[k, n]] * _p2(ewt[k, n // 32]), dx, Nr)
+    # WGrad: dYt [N][T], Xt [K][T] -> dW [N][K]
+    T = 64
+    dyqt, edyt = _codes(rng, (N, T)), _e8(rng, (N, T // 32))
+    xqt, ext = _codes(rng, (K, T)), _e8(rng, (K, T // 32))
+    dw = G.gemm_mx_wgrad(dyqt, edyt, xqt, ext)
+    assert dw.shape == (N, K)
+    _check([(0, 0), (5, 95), (3, 40)],
+           lambda n, k, t: _DEC_FR[dyqt[n, t]] * _p2(edyt[n, t // 32]) * _DEC_FR[xqt[k, t]] * _p2(ext[k, t // 32]), dw, T)

@@ -299,3 +299,23 @@ def test_pow2_equivariance(j):
     q2, s2 = Q.quant_act_1x128_pow2(bf16_round(x * np.float32(2.0 ** j)))
     assert np.array_equal(q1, q2)
     assert np.array_equal(s2.astype(np.float64), s1.astype(np.float64) * 2.0 ** j)
+
+
+def test_mx_32x1_brute_force_and_layout():
+    x = _sample((96, 64), 14)
+    x[0:32, 3] = 0.0                        # an all-zero column group
+    x[40, 7] = 448.0 * 8                    # amax exactly 448 * 2**3
+    x[70, 9] = -1e-39                       # a subnormal bf16 value (after rounding)
+    x = bf16_round(x)
+    qt, et = Q.quant_mx_32x1(x)
+    assert qt.shape == (64, 96) and et.shape == (64, 3)
+    for k in (0, 3, 7, 9, 63):
+        for rg in range(3):
+            vals = x[rg * 32:(rg + 1) * 32, k]
+            e = _brute_mx_exponent(float(np.max(np.abs(vals))))
+            assert int(et[k, rg]) == e + 127
+            for i, v in enumerate(vals):
+                assert qt[k, rg * 32 + i] == _enc_fraction(Fraction(float(v)) / Fraction(2) ** e, np.signbit(v))
+    assert et[3, 0] == 127 and et[7, 1] == 127 + 3
+    with pytest.raises(ValueError):
+        Q.quant_mx_32x1(x[:40])
