@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install|producers] [--no-cpu-baseline]
+                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install|producers|mx_dense] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
 HBM. The default workload is the dense layer shaped like a ~9B model's MLP
@@ -56,14 +56,10 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "47d9ca8caad91577", "gb": 1.6281},        # read 1.2257 + write 0.4024
-    "gemm_gu_pow2": {"sha": "47d9ca8caad91577", "gb": 1.6279},   # read 1.2255 + write 0.4024
-    "dgrad": {"sha": "47d9ca8caad91577", "gb": 1.3004},          # read 1.2333 + write 0.0671
-    "dgrad_pow2": {"sha": "47d9ca8caad91577", "gb": 1.3004},     # read 1.2333 + write 0.0671
-    "decode_n24576": {"sha": "f0ab91830ef18133", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
-    "grouped_gu": {"sha": "91547e59995d80c3", "gb": 0.5539},     # read 0.4868 + write 0.0672
-    "install_gu": {"sha": "c4b1fdd282a2ee0f", "gb": 0.2014},     # read 0.1007 + write 0.1007
-    "swiglu_fp8": {"sha": "f498596b7d6a231f", "gb": 0.6476},     # read 0.4034 + write 0.2442
+    "gemm_gu": {"sha": "2937a39ef29013ef", "gb": 1.6281},        # read 1.2258 + write 0.4024
+    "dgrad": {"sha": "2937a39ef29013ef", "gb": 1.3005},          # read 1.2335 + write 0.0671
+    "mx_fwd": {"sha": "2937a39ef29013ef", "gb": 1.6408},         # read 1.2385 + write 0.4024
+    "decode_n24576": {"sha": "6e30ff2362398afe", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
 }
 
 
@@ -76,14 +72,15 @@ def _sources_sha(files):
 
 
 KERNEL_SOURCES = {
-    "gemm_gu": ("gemm.hip", "device.hpp", "internal.hpp"),
-    "gemm_gu_pow2": ("gemm.hip", "device.hpp", "internal.hpp"),
-    "dgrad": ("gemm.hip", "device.hpp", "internal.hpp"),
-    "dgrad_pow2": ("gemm.hip", "device.hpp", "internal.hpp"),
-    "decode_n24576": ("skinny.hip", "gemm.hip", "quant.hip", "device.hpp", "internal.hpp"),
-    "grouped_gu": ("grouped.hip", "device.hpp", "internal.hpp"),
-    "install_gu": ("install.hip", "device.hpp", "internal.hpp"),
-    "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp", "internal.hpp"),
+    "gemm_gu": ("gemm.hip", "device.hpp"),
+    "gemm_gu_pow2": ("gemm.hip", "device.hpp"),
+    "dgrad": ("gemm.hip", "device.hpp"),
+    "dgrad_pow2": ("gemm.hip", "device.hpp"),
+    "mx_fwd": ("gemm.hip", "device.hpp"),
+    "decode_n24576": ("skinny.hip", "device.hpp"),
+    "grouped_gu": ("grouped.hip", "device.hpp"),
+    "install_gu": ("install.hip", "device.hpp"),
+    "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp"),
 }
 
 
@@ -102,7 +99,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense", choices=["dense", "dense_pow2", "decode", "backward", "backward_pow2", "moe",
-                                                         "install", "producers"])
+                                                         "install", "producers", "mx_dense"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -274,6 +271,60 @@ def backward_setup(torch, F, W, dev, pow2=False):
                "bf16 read 2 B + row and column E4M3 payloads + fp32 scales per element"),
         gemm_keys=("dgrad", "wgrad"),
         traffic_key="dgrad_pow2" if pow2 else "dgrad",
+    )
+    return step, timers, info
+
+
+def mx_dense_setup(torch, F, W, dev):
+    """The dense gate/up layer (X 8192x4096, W 24576x4096, dY 8192x24576) forward and backward
+    in the MXFP8 recipe: 1x32 E8M0 groups along each GEMM's contraction dimension, so X, W and
+    dY are each quantized row-wise and column-wise (32x1, transposed) from bf16; then the
+    forward, DGrad and WGrad GEMMs on the scaled MFMA."""
+    d = W.dense_forward(with_down=False)
+    x = W.to_bf16_tensor(d["x"]).to(dev)
+    w = W.to_bf16_tensor(d["w_gu"]).to(dev)
+    del d
+    dy = W.to_bf16_tensor(W.dense_backward()["dy"]).to(dev)
+    M, K = x.shape
+    N = w.shape[0]
+    u8 = torch.uint8
+
+    def qbufs(R, C):
+        return (torch.empty((R, C), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
+                torch.empty((C, R), dtype=u8, device=dev), torch.empty((C, R // 32), dtype=u8, device=dev))
+    bx, bw, bdy = qbufs(M, K), qbufs(N, K), qbufs(M, N)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    timers = {k: EventTimer(torch) for k in ("quant_x", "quant_w", "fwd", "quant_dy", "dgrad", "wgrad")}
+
+    def step(timed):
+        tm = timers if timed else None
+        if tm: tm["quant_x"].start()
+        F.mxfp8_quant_act_1x32(x, *bx, colwise=True)
+        if tm: tm["quant_x"].stop(); tm["quant_w"].start()
+        F.mxfp8_quant_act_1x32(w, *bw, colwise=True)
+        if tm: tm["quant_w"].stop(); tm["fwd"].start()
+        F.fp8_gemm_mxfp8_fwd(bx[0], bx[1], bw[0], bw[1], y=y)
+        if tm: tm["fwd"].stop(); tm["quant_dy"].start()
+        F.mxfp8_quant_act_1x32(dy, *bdy, colwise=True)
+        if tm: tm["quant_dy"].stop(); tm["dgrad"].start()
+        F.fp8_gemm_mxfp8_dgrad(bdy[0], bdy[1], bw[2], bw[3], dx=dx)
+        if tm: tm["dgrad"].stop(); tm["wgrad"].start()
+        F.fp8_gemm_mxfp8_wgrad(bdy[2], bdy[3], bx[2], bx[3], dw=dw)
+        if tm: tm["wgrad"].stop()
+
+    fl = 2.0 * M * N * K
+    info = dict(
+        config={"workload": "dense_layer_fwd_bwd_mxfp8_9b", "tokens_M": M, "gate_up_N": N, "hidden_K": K,
+                "recipe": "MXFP8: E4M3 + E8M0 per 1x32 along each contraction (32x1 transposed copies)",
+                "out": "Y, dX bf16; dW fp32"},
+        flops=3 * fl,
+        dominant=("fwd", "mfma", fl / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS, f"2*M*N*K = {fl:.4g} FLOP per launch"),
+        quant=("quant_dy", (M * N * 4 + 2 * M * N // 32) / 1e9,
+               "bf16 read 2 B + row and column E4M3 payloads + E8M0 scales per element"),
+        gemm_keys=("fwd", "dgrad", "wgrad"),
+        traffic_key="mx_fwd",
     )
     return step, timers, info
 
@@ -480,6 +531,19 @@ def cpu_baseline(workload: str, budget_s: float = 12.0):
         return {"value": reps * nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"{reps} x oracle SwiGLU -> FP8 (rows + cols) of GU {m}x{2 * f} and RMSNorm -> FP8 "
                           f"(rows + cols) of X {m}x{k}, 128 token rows of the dense layer", "seconds": round(dt, 2)}
+    if workload == "mx_dense":
+        m, n, k = 256, 2048, 4096
+        x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        w = W.bf16_round(rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02))
+
+        def chunk():
+            xq, ex = OQ.quant_mx_1x32(x)
+            wq, ew = OQ.quant_mx_1x32(w)
+            OG.gemm_mx_fwd(xq, ex, wq, ew)
+        reps, dt = _repeat(chunk, budget_s)
+        return {"value": reps * 2.0 * m * n * k / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+                "kind": "oracle", "sample": f"{reps} x oracle MXFP8 quantization of both operands + fp64 dequantized "
+                f"forward GEMM, {m}x{n}x{k} chunk of the gate/up layer", "seconds": round(dt, 2)}
     if workload == "moe":
         m, n, k = 512, 1024, 2048
         x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
@@ -526,7 +590,7 @@ def main():
     F.load_library()
     setup = {"dense": dense_setup, "dense_pow2": lambda *args: dense_setup(*args, pow2=True), "decode": decode_setup,
              "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup,
-             "install": install_setup, "producers": producers_setup}[a.workload]
+             "install": install_setup, "producers": producers_setup, "mx_dense": mx_dense_setup}[a.workload]
     step, timers, info = setup(torch, F, W, dev)
 
     for _ in range(a.warmup):

@@ -29,6 +29,7 @@ __all__ = [
     "fp8_quant_act_1x128_pow2", "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd",
     "fp8_gemm_blockscaled_pow2_dgrad", "fp8_gemm_blockscaled_pow2_wgrad",
     "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16", "fp8_rmsnorm_quant_1x128",
+    "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad", "fp8_gemm_mxfp8_wgrad",
 ]
 
 RECIPE_BLOCK128 = 0
@@ -68,6 +69,10 @@ _SIGNATURES = {
     "fp8_gemm_blockscaled_pow2_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_blockscaled_pow2_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_swiglu_bf16": ([_vp, _i64, _i64, _vp, _vp], _int),
+    "mxfp8_quant_act_1x32": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
+    "fp8_gemm_mxfp8_fwd": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_gemm_mxfp8_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
+    "fp8_gemm_mxfp8_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_swiglu_quant_1x128": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _int, _vp], _int),
     "fp8_rmsnorm_bf16": ([_vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _vp], _int),
     "fp8_rmsnorm_quant_1x128": ([_vp, _vp, _i64, _i64, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _int, _vp], _int),
@@ -275,6 +280,75 @@ def mxfp8_quant_1x32(x, q=None, e8m0=None):
     e8m0 = _out(e8m0, torch.uint8, tuple(x.shape[:-1]) + (K // 32,), dev, "e8m0")
     _check(lib.mxfp8_quant_1x32(_ptr(x), R, K, _ptr(q), _ptr(e8m0), _stream(dev)), "mxfp8_quant_1x32")
     return q, e8m0
+
+
+def mxfp8_quant_act_1x32(x, q=None, e8m0=None, qt=None, e8m0t=None, *, rowwise=True, colwise=False):
+    """MXFP8 1x32 row groups and/or 32x1 column groups written transposed, of x [R][K] bf16.
+    Returns (q [R][K], e8m0 [R][K/32], qt [K][R], e8m0t [K][R/32]); outputs not requested are None."""
+    lib = load_library()
+    R, K = x.shape
+    _need(x, torch.bfloat16, (R, K), "x")
+    dev = x.device
+    if rowwise:
+        q = _out(q, torch.uint8, (R, K), dev, "q")
+        e8m0 = _out(e8m0, torch.uint8, (R, K // 32), dev, "e8m0")
+    else:
+        q = e8m0 = None
+    if colwise:
+        qt = _out(qt, torch.uint8, (K, R), dev, "qt")
+        e8m0t = _out(e8m0t, torch.uint8, (K, R // 32), dev, "e8m0t")
+    else:
+        qt = e8m0t = None
+    _check(lib.mxfp8_quant_act_1x32(_ptr(x), R, K, _ptr(q), _ptr(e8m0), _ptr(qt), _ptr(e8m0t), _stream(dev)),
+           "mxfp8_quant_act_1x32")
+    return q, e8m0, qt, e8m0t
+
+
+def fp8_gemm_mxfp8_fwd(xq, ex, wq, ew, *, out_dtype=torch.bfloat16, y=None):
+    """Y[M][N] = deq(X) deq(W)^T, MXFP8 operands (1x32 E8M0 scales along K)."""
+    lib = load_library()
+    M, K = xq.shape
+    N = wq.shape[0]
+    _need(xq, torch.uint8, (M, K), "xq")
+    _need(ex, torch.uint8, (M, K // 32), "ex")
+    _need(wq, torch.uint8, (N, K), "wq")
+    _need(ew, torch.uint8, (N, K // 32), "ew")
+    y = _out(y, out_dtype, (M, N), xq.device, "y")
+    _check(lib.fp8_gemm_mxfp8_fwd(_ptr(xq), _ptr(ex), _ptr(wq), _ptr(ew), M, N, K, _ptr(y), _odt(out_dtype),
+                                  _stream(xq.device)), "fp8_gemm_mxfp8_fwd")
+    return y
+
+
+def fp8_gemm_mxfp8_dgrad(dyq, edy, wqt, ewt, *, out_dtype=torch.bfloat16, dx=None):
+    """dX[M][K] = deq(dY) deq(W); dyq [M][N]; W as its 32x1 copy wqt [K][N], ewt [K][N/32]."""
+    lib = load_library()
+    M, N = dyq.shape
+    K = wqt.shape[0]
+    _need(dyq, torch.uint8, (M, N), "dyq")
+    _need(edy, torch.uint8, (M, N // 32), "edy")
+    _need(wqt, torch.uint8, (K, N), "wqt")
+    _need(ewt, torch.uint8, (K, N // 32), "ewt")
+    dx = _out(dx, out_dtype, (M, K), dyq.device, "dx")
+    _check(lib.fp8_gemm_mxfp8_dgrad(_ptr(dyq), _ptr(edy), _ptr(wqt), _ptr(ewt), M, N, K, _ptr(dx), _odt(out_dtype),
+                                    _stream(dyq.device)), "fp8_gemm_mxfp8_dgrad")
+    return dx
+
+
+def fp8_gemm_mxfp8_wgrad(dyqt, edyt, xqt, ext, *, dw=None, accumulate=False):
+    """dW[N][K] (fp32) = deq(dY)^T deq(X) from the 32x1 copies dyqt [N][M], xqt [K][M]."""
+    lib = load_library()
+    N, M = dyqt.shape
+    K = xqt.shape[0]
+    _need(dyqt, torch.uint8, (N, M), "dyqt")
+    _need(edyt, torch.uint8, (N, M // 32), "edyt")
+    _need(xqt, torch.uint8, (K, M), "xqt")
+    _need(ext, torch.uint8, (K, M // 32), "ext")
+    if dw is None:
+        dw = (torch.zeros if accumulate else torch.empty)((N, K), dtype=torch.float32, device=dyqt.device)
+    _need(dw, torch.float32, (N, K), "dw")
+    _check(lib.fp8_gemm_mxfp8_wgrad(_ptr(dyqt), _ptr(edyt), _ptr(xqt), _ptr(ext), M, N, K, _ptr(dw),
+                                    1 if accumulate else 0, _stream(dyqt.device)), "fp8_gemm_mxfp8_wgrad")
+    return dw
 
 
 def fp8rl_fwd_workspace_bytes(M: int, K: int) -> int:

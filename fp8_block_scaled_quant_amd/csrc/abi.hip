@@ -203,6 +203,21 @@ fp8rl_status mxfp8_quant_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* 
   return launched(launch_quant_mx_1x32(x, R, K, q, e8m0, as_stream(stream)));
 }
 
+fp8rl_status mxfp8_quant_act_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0, uint8_t* qt,
+                                  uint8_t* e8m0t, void* stream) {
+  if (fp8rl_status e = check_dims(R, K)) return e;
+  if (K % 32 != 0) return FP8RL_ERR_SHAPE;
+  if (R == 0 || K == 0) return FP8RL_OK;
+  if ((q == nullptr) != (e8m0 == nullptr) || (qt == nullptr) != (e8m0t == nullptr)) return FP8RL_ERR_NULL;
+  if (q == nullptr && qt == nullptr) return FP8RL_ERR_NULL;
+  if (qt != nullptr && (R % 128 != 0 || K % 128 != 0)) return FP8RL_ERR_SHAPE;
+  if (x == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(x, 16) || (q && !aligned(q, 16)) || (qt && !aligned(qt, 16))) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  if (qt == nullptr) return launched(launch_quant_mx_1x32(x, R, K, q, e8m0, as_stream(stream)));
+  return launched(launch_quant_mx_tile(x, R, K, q, e8m0, qt, e8m0t, as_stream(stream)));
+}
+
 size_t fp8rl_fwd_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % 128 != 0 || check_dims(M, K) != FP8RL_OK) return 0;
   const size_t qbytes = (size_t)(M * K);
@@ -292,6 +307,36 @@ fp8rl_status fp8_gemm_blockscaled_pow2_fwd(const uint8_t* xq, const float* sx, c
 
 namespace {
 
+// MXFP8 TN GEMM C[ra][rb] = sum_k deq(A)[ra][k] deq(B)[rb][k], E8M0 bytes [rows][kred/32].
+fp8rl_status mx_gemm_impl(const uint8_t* a, const uint8_t* ea, const uint8_t* b, const uint8_t* eb, int64_t ra,
+                          int64_t rb, int64_t kred, void* c, bool f32, int accumulate, void* stream) {
+  if (a == nullptr || ea == nullptr || b == nullptr || eb == nullptr || c == nullptr) return FP8RL_ERR_NULL;
+  if (fp8rl_status e = check_dims(ra, kred)) return e;
+  if (fp8rl_status e = check_dims(rb, kred)) return e;
+  if (fp8rl_status e = check_dims(ra, rb)) return e;
+  if (kred % 128 != 0 || rb % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (ra == 0 || rb == 0) return FP8RL_OK;
+  if (kred == 0) return FP8RL_ERR_SHAPE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(ea, 4) || !aligned(eb, 4) || !aligned(c, 16))
+    return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  GemmParams p{};
+  p.A = a;
+  p.B = b;
+  p.sA = reinterpret_cast<const float*>(ea);     // read as dwords: 4 E8M0 bytes per 128 K
+  p.sB = reinterpret_cast<const float*>(eb);
+  p.C = c;
+  p.M = ra;
+  p.N = rb;
+  p.K = kred;
+  p.sa_ld = kred / 128;
+  p.sb_ld_n = kred / 128;
+  p.sb_ld_k = 1;
+  p.ldc = rb;
+  p.accumulate = accumulate;
+  return launched(launch_gemm_mx(p, f32, as_stream(stream)));
+}
+
 fp8rl_status dgrad_impl(const uint8_t* dyq, const float* sdy, const uint8_t* wqt, const float* sw, int64_t M,
                         int64_t N, int64_t K, void* dx, int dx_dtype, bool pow2, void* stream) {
   if (dyq == nullptr || sdy == nullptr || wqt == nullptr || sw == nullptr || dx == nullptr) return FP8RL_ERR_NULL;
@@ -375,6 +420,25 @@ fp8rl_status fp8_gemm_blockscaled_pow2_wgrad(const uint8_t* dyqt, const float* s
                                              const float* sxt, int64_t M, int64_t N, int64_t K, float* dw,
                                              int accumulate, void* stream) {
   return wgrad_impl(dyqt, sdyt, xqt, sxt, M, N, K, dw, accumulate, true, stream);
+}
+
+fp8rl_status fp8_gemm_mxfp8_fwd(const uint8_t* xq, const uint8_t* ex, const uint8_t* wq, const uint8_t* ew, int64_t M,
+                                int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
+  if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
+  return mx_gemm_impl(xq, ex, wq, ew, M, N, K, y, y_dtype == FP8RL_OUT_F32, 0, stream);
+}
+
+fp8rl_status fp8_gemm_mxfp8_dgrad(const uint8_t* dyq, const uint8_t* edy, const uint8_t* wqt, const uint8_t* ewt,
+                                  int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* stream) {
+  if (dx_dtype != FP8RL_OUT_BF16 && dx_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
+  return mx_gemm_impl(dyq, edy, wqt, ewt, M, K, N, dx, dx_dtype == FP8RL_OUT_F32, 0, stream);
+}
+
+fp8rl_status fp8_gemm_mxfp8_wgrad(const uint8_t* dyqt, const uint8_t* edyt, const uint8_t* xqt, const uint8_t* ext,
+                                  int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream) {
+  if (M % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (N > 0 && K > 0 && M == 0) return FP8RL_ERR_SHAPE;
+  return mx_gemm_impl(dyqt, edyt, xqt, ext, N, K, M, dw, true, accumulate ? 1 : 0, stream);
 }
 
 fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, const uint8_t* wq, const void* sw,

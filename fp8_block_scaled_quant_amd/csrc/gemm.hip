@@ -33,7 +33,11 @@ namespace fp8rl {
 // Distance, in MFMA tiles, between an MFMA and the FMAs that fold its result.
 constexpr int kLag = 3;
 
-template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, bool kPow2>
+// kScale: 0 = fp32 scales (each 128-K block product folded in with one FMA),
+//         1 = power-of-two fp32 scales (their exponent fields go to the scaled MFMA),
+//         2 = MXFP8: each scale dword holds the 4 E8M0 bytes of a row's 128-K block, one per
+//             32-wide part; lane l hands the MFMA the byte of part l >> 4.
+template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, int kScale>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -177,14 +181,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     hold(sbv);
     hold(blo);
     hold(bhi);
-    if constexpr (kPow2) {
+    if constexpr (kScale != 0) {
       // Power-of-two scales: the scaled MFMA applies 2^(e_a + e_b) itself (E8M0 bytes are
       // the scales' fp32 exponent fields; 2^-127, an fp32 subnormal, gives byte 0), so the
       // products accumulate directly. Lane l supplies the scale of row l & 15 for all four
-      // 32-wide parts of the K block.
+      // 32-wide parts of the K block. MXFP8: lane l supplies the E8M0 byte of row l & 15
+      // for 32-wide part l >> 4 (the MFMA reads the low byte of the operand).
+      const int esh = kScale == 2 ? 8 * (lane >> 4) : 23;
       int ua[FM];
 #pragma unroll
-      for (int j = 0; j < FM; ++j) ua[j] = (int)(__float_as_uint(sa[j]) >> 23);
+      for (int j = 0; j < FM; ++j) ua[j] = (int)(__float_as_uint(sa[j]) >> esh);
       int ubr[FN];
       if constexpr (kRowB) {
         // The LDS reads land only at the wait: take the exponents after it.
@@ -197,10 +203,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
           hold(sbr[i]);
-          ubr[i] = (int)(__float_as_uint(sbr[i]) >> 23);
+          ubr[i] = (int)(__float_as_uint(sbr[i]) >> esh);
         }
       }
-      const int ub = kRowB ? 0 : (int)(__float_as_uint(sb) >> 23);
+      const int ub = kRowB ? 0 : (int)(__float_as_uint(sb) >> esh);
       static_for<0, FN>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         v4i nlo, nhi;
@@ -380,14 +386,14 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool kRowB, bool kPow2>
+template <int BM, int BN, int WM, int WN, bool kRowB, int kScale>
 static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles), block(WM * WN * 64);
   if (f32)
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kPow2>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kScale>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kPow2>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kScale>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -400,12 +406,19 @@ hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f
   const bool big = big_tiles >= 256;
   if (pow2) {
     if (row_scale_b)
-      return big ? launch_cfg<256, 256, 4, 2, true, true>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, true>(p, f32, stream);
-    return big ? launch_cfg<256, 256, 4, 2, false, true>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false, true>(p, f32, stream);
+      return big ? launch_cfg<256, 256, 4, 2, true, 1>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, 1>(p, f32, stream);
+    return big ? launch_cfg<256, 256, 4, 2, false, 1>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false, 1>(p, f32, stream);
   }
   if (row_scale_b)
-    return big ? launch_cfg<256, 256, 4, 2, true, false>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, false>(p, f32, stream);
-  return big ? launch_cfg<256, 256, 4, 2, false, false>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false, false>(p, f32, stream);
+    return big ? launch_cfg<256, 256, 4, 2, true, 0>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, 0>(p, f32, stream);
+  return big ? launch_cfg<256, 256, 4, 2, false, 0>(p, f32, stream) : launch_cfg<128, 128, 2, 2, false, 0>(p, f32, stream);
+}
+
+// MXFP8: both operands carry one E8M0 byte per row per 32 K (sA / sB point at those bytes,
+// sa_ld = sb_ld_n = K / 128 dwords per row).
+hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream) {
+  const bool big = ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
+  return big ? launch_cfg<256, 256, 4, 2, true, 2>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, 2>(p, f32, stream);
 }
 
 }  // namespace fp8rl

@@ -23,6 +23,9 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, int64_t
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
                                 float* rstd, uint8_t* q, float* s, uint8_t* qt, float* st, bool pow2,
                                 hipStream_t stream);
+// MXFP8 1x32 rows and/or 32x1 columns (written transposed) of X[R][K], R % 128 == K % 128 == 0.
+hipError_t launch_quant_mx_tile(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0, uint8_t* qt,
+                                uint8_t* e8m0t, hipStream_t stream);
 hipError_t launch_quant_mx_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0,
                                 hipStream_t stream);
 
@@ -42,6 +45,8 @@ struct GemmParams {
 // pow2: every scale is a power of two (the pow2 quantizers' output); the scaled MFMA then
 // applies them (their fp32 exponent fields) and no rescale step is needed.
 hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, bool pow2, hipStream_t stream);
+// MXFP8 TN GEMM: sA / sB are E8M0 bytes [rows][K/32] (passed as float* to dwords of 4 bytes).
+hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream);
 // Few-row form (M <= 256, block-scaled B only): all rows per workgroup, one workgroup per CU.
 hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream);
 

@@ -87,6 +87,15 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8
   return hipGetLastError();
 }
 
+hipError_t launch_quant_mx_tile(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0, uint8_t* qt,
+                                uint8_t* e8m0t, hipStream_t stream) {
+  const dim3 grid((unsigned)((K / 128) * (R / 128)));
+  const PlainSrc src{x, K};
+  hipLaunchKernelGGL((k_quant_tile<PlainSrc, false, true, 32>), grid, dim3(512), 0, stream, src, R, K, q, e8m0, qt,
+                     e8m0t);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_mx_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0,
                                 hipStream_t stream) {
   const int64_t ngroups = R * (K / 32);

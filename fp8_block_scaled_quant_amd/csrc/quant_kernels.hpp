@@ -90,6 +90,9 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(Src src, uint8_t* __re
 //                   column output = 128x1 groups written transposed (qt [C][R], st [C][R/128]).
 //   kBlock = true : weight mode. One scale for the whole 128x128 block (s [R/128][C/128]);
 //                   qt, if requested, is the byte transpose of q (same scale, same bytes).
+//   kG = 32 (with kPow2): MXFP8 mode. Row output = 1x32 groups, column output = 32x1
+//                   groups written transposed; the scales are E8M0 bytes (e + 127, the
+//                   exponent field of the power-of-two scale) [R][C/32] and [C][R/32].
 // Grid: blockIdx.x = rb * (C/128) + cb.
 // Thread t owns the 4x8 sub-block rows 4*(t/16) .. +3, columns 8*(t%16) .. +7. Each wave
 // load instruction then reads 4 whole 256-byte row segments, and each row-output store
@@ -100,10 +103,20 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(Src src, uint8_t* __re
 // then own one column (16 rows each): column amax over those 8 lanes, and each store
 // instruction writes 8 whole 128-byte lines of qt.
 // ---------------------------------------------------------------------------------------
-template <class Src, bool kBlock, bool kPow2>
+// Store a group scale: fp32 for 128-wide groups, the E8M0 byte for 32-wide (MX) groups.
+template <int kG>
+__device__ __forceinline__ void store_scale(void* p, int64_t i, const BlockScale& bs) {
+  if constexpr (kG == 32)
+    reinterpret_cast<uint8_t*>(p)[i] = (uint8_t)(__float_as_uint(bs.s) >> 23);
+  else
+    reinterpret_cast<float*>(p)[i] = bs.s;
+}
+
+template <class Src, bool kBlock, bool kPow2, int kG = 128>
 __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t C, uint8_t* __restrict__ q,
-                                                    float* __restrict__ s, uint8_t* __restrict__ qt,
-                                                    float* __restrict__ st) {
+                                                    void* __restrict__ s, uint8_t* __restrict__ qt,
+                                                    void* __restrict__ st) {
+  static_assert(kG == 128 || (kG == 32 && kPow2 && !kBlock), "MX groups take power-of-two scales");
   __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];   // [column][row pair]
   __shared__ float red[8];
   __shared__ __attribute__((aligned(16))) uint8_t src_lds[SrcLds<Src>::kBytes];
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
     __syncthreads();
     a = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
     const BlockScale bs = group_scale<kPow2>(a);
-    if (tid == 0) s[rb * ncb + cb] = bs.s;
+    if (tid == 0) store_scale<128>(s, rb * ncb + cb, bs);
     rblk = bs.r;
     if (want_rows) {
 #pragma unroll
@@ -150,10 +163,14 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
       float a = fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w)));
       a = fmaxf(a, __shfl_xor(a, 1));
       a = fmaxf(a, __shfl_xor(a, 2));
-      a = fmaxf(a, __shfl_xor(a, 4));
-      a = fmaxf(a, __shfl_xor(a, 8));
+      if constexpr (kG == 128) {
+        a = fmaxf(a, __shfl_xor(a, 4));
+        a = fmaxf(a, __shfl_xor(a, 8));
+      }
       const BlockScale bs = group_scale<kPow2>(a);
-      if (c == 0) s[(rb * 128 + 4 * rg + i) * ncb + cb] = bs.s;
+      constexpr int kLanes = kG / 8;                               // lanes of one row group
+      if ((c & (kLanes - 1)) == 0)
+        store_scale<kG>(s, (rb * 128 + 4 * rg + i) * (C / kG) + cb * (128 / kG) + c / kLanes, bs);
       *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
           quant8(v[i].x, v[i].y, v[i].z, v[i].w, bs.r);
     }
@@ -195,11 +212,15 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
       float m = fmaxf(fmaxf(fmaxf(absmax2(lo.x), absmax2(lo.y)), fmaxf(absmax2(lo.z), absmax2(lo.w))),
                       fmaxf(fmaxf(absmax2(hi.x), absmax2(hi.y)), fmaxf(absmax2(hi.z), absmax2(hi.w))));
       m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
+      if constexpr (kG == 128) {
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+      }
       const BlockScale bs = group_scale<kPow2>(m);
       r = bs.r;
-      if (k == 0) st[(cb * 128 + col) * (R / 128) + rb] = bs.s;
+      constexpr int kLanes = kG / 16;                              // lanes of one column group
+      if ((k & (kLanes - 1)) == 0)
+        store_scale<kG>(st, (cb * 128 + col) * (R / kG) + rb * (128 / kG) + k / kLanes, bs);
     }
     const uint2 o0 = quant8(lo.x, lo.y, lo.z, lo.w, r);
     const uint2 o1 = quant8(hi.x, hi.y, hi.z, hi.w, r);

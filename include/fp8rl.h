@@ -65,7 +65,7 @@ typedef enum {
 } fp8rl_out;
 
 /* ABI version of this header. */
-#define FP8RL_ABI_VERSION 3
+#define FP8RL_ABI_VERSION 4
 int fp8rl_abi_version(void);
 const char* fp8rl_status_str(fp8rl_status status);
 
@@ -117,6 +117,19 @@ fp8rl_status fp8_quant_w_128x128_pow2(const uint16_t* w, int64_t N, int64_t K,
  *   x : bf16 [R][K];  q uint8 [R][K];  e8m0 uint8 [R][K/32].   Rules: K % 32 == 0. */
 fp8rl_status mxfp8_quant_1x32(const uint16_t* x, int64_t R, int64_t K,
                               uint8_t* q, uint8_t* e8m0, void* stream);
+
+/* MXFP8 activation quantization with 1x32 row groups and/or 32x1 column groups written
+ * transposed: the operands of an MXFP8 linear layer's backward, whose GEMMs contract over
+ * the token (or output-feature) dimension ([SkyRL-FP8] "When independent quantization
+ * breaks policy consistency": 1x32 blocks; the MXFP8 recipe for the linear layers). Same
+ * scale rule and encoding as mxfp8_quant_1x32.
+ *   x : bf16 [R][K]
+ *   q, e8m0   : rows: uint8 [R][K], E8M0 uint8 [R][K/32]             (both NULL: not produced)
+ *   qt, e8m0t : columns, transposed: uint8 [K][R], E8M0 uint8 [K][R/32]; qt[k][r] quantizes
+ *               x[r][k] within the group of 32 consecutive rows r     (both NULL: not produced)
+ * Rules: K % 32 == 0; R % 128 == 0 and K % 128 == 0 when qt is requested; at least one pair. */
+fp8rl_status mxfp8_quant_act_1x32(const uint16_t* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e8m0,
+                                  uint8_t* qt, uint8_t* e8m0t, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Fused producers ([Jet-RL] "Quantization scheme": the FP8 activations a linear layer
@@ -220,6 +233,25 @@ fp8rl_status fp8_gemm_blockscaled_pow2_wgrad(const uint8_t* dyqt, const float* s
                                              const uint8_t* xqt, const float* sxt,
                                              int64_t M, int64_t N, int64_t K,
                                              float* dw, int accumulate, void* stream);
+
+/* MXFP8 dense linear layer ([SkyRL-FP8]: the MXFP8 recipe for the linear layers, one E8M0
+ * scale per 1x32 block along each GEMM's contraction dimension). The scaled MFMA applies
+ * the E8M0 scales; fp32 accumulation.
+ *   forward: Y[M][N] = deq(X) . deq(W)^T; xq [M][K], ex [M][K/32]; wq [N][K], ew [N][K/32];
+ *            y bf16 or fp32 [M][N].                Rules: K % 128 == 0, N % 128 == 0, any M.
+ *   DGrad  : dX[M][K] = deq(dY) . deq(W); dyq [M][N], edy [M][N/32]; W as its 32x1 copy
+ *            (mxfp8_quant_act_1x32's qt of W): wqt [K][N], ewt [K][N/32];
+ *            dx bf16 or fp32 [M][K].               Rules: N % 128 == 0, K % 128 == 0, any M.
+ *   WGrad  : dW[N][K] = deq(dY)^T . deq(X) from the 32x1 copies dyqt [N][M], edyt [N][M/32],
+ *            xqt [K][M], ext [K][M/32]; dw fp32 [N][K]; accumulate != 0 adds to dw.
+ *                                                  Rules: M, N, K % 128 == 0.
+ * E8M0 arrays must be 4-byte aligned (their rows are read as dwords of 4 bytes). */
+fp8rl_status fp8_gemm_mxfp8_fwd(const uint8_t* xq, const uint8_t* ex, const uint8_t* wq, const uint8_t* ew,
+                                int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* stream);
+fp8rl_status fp8_gemm_mxfp8_dgrad(const uint8_t* dyq, const uint8_t* edy, const uint8_t* wqt, const uint8_t* ewt,
+                                  int64_t M, int64_t N, int64_t K, void* dx, int dx_dtype, void* stream);
+fp8rl_status fp8_gemm_mxfp8_wgrad(const uint8_t* dyqt, const uint8_t* edyt, const uint8_t* xqt, const uint8_t* ext,
+                                  int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream);
 
 /* Grouped GEMM for mixture-of-experts ([SkyRL-FP8] MoE: routed experts hold most
  * parameters; MXFP8 recipe). Routed rows are grouped by expert; rows

@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
               "fp8rl_abi_version", "fp8rl_status_str", "fp8rl_fwd_workspace_bytes", "fp8_quant_act_1x128_pow2",
               "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd", "fp8_gemm_blockscaled_pow2_dgrad",
               "fp8_gemm_blockscaled_pow2_wgrad", "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16",
-              "fp8_rmsnorm_quant_1x128"]:
+              "fp8_rmsnorm_quant_1x128", "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad",
+              "fp8_gemm_mxfp8_wgrad"]:
         assert n in names
 
 
@@ -57,7 +58,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8rl_abi_version() == 3
+    assert lib.fp8rl_abi_version() == 4
     for code in range(9):
         assert len(lib.fp8rl_status_str(code)) > 0
     assert lib.fp8rl_status_str(99) == b"unknown status"
@@ -149,6 +150,31 @@ def test_producer_validation(lib):
     assert rq(P, P, 4, 128, 1e-6, P, None, None, None, None, 0, None) == ERR_NULL
     assert rq(P, P, 4, 128, -1.0, P, P, P, None, None, 0, None) == ERR_VALUE
     assert rq(P, P, 0, 128, 1e-6, None, P, P, None, None, 0, None) == OK
+
+
+def test_mx_dense_validation(lib):
+    qa = lib.mxfp8_quant_act_1x32
+    assert qa(P, 4, 48, P, P, None, None, None) == ERR_SHAPE               # K % 32
+    assert qa(P, 4, 64, P, None, None, None, None) == ERR_NULL             # half a pair
+    assert qa(P, 4, 64, None, None, None, None, None) == ERR_NULL          # nothing requested
+    assert qa(P, 100, 128, None, None, P, P, None) == ERR_SHAPE            # columns need R % 128
+    assert qa(P, 128, 96, None, None, P, P, None) == ERR_SHAPE             # ... and K % 128
+    assert qa(MIS, 4, 64, P, P, None, None, None) == ERR_ALIGN
+    assert qa(P, 0, 64, None, None, None, None, None) == OK
+    f = lib.fp8_gemm_mxfp8_fwd
+    assert f(P, P, P, P, 4, 128, 128, P, 7, None) == ERR_RECIPE
+    assert f(P, P, P, P, 4, 128, 96, P, 0, None) == ERR_SHAPE              # K % 128
+    assert f(P, P, P, P, 4, 100, 128, P, 0, None) == ERR_SHAPE             # N % 128
+    assert f(P, None, P, P, 4, 128, 128, P, 0, None) == ERR_NULL
+    assert f(P, P + 2, P, P, 4, 128, 128, P, 0, None) == ERR_ALIGN         # E8M0 rows read as dwords
+    assert f(P, P, P, P, 0, 128, 128, P, 0, None) == OK
+    d = lib.fp8_gemm_mxfp8_dgrad
+    assert d(P, P, P, P, 4, 100, 128, P, 0, None) == ERR_SHAPE             # N % 128 (contraction)
+    assert d(P, P, P, P, 4, 128, 100, P, 0, None) == ERR_SHAPE             # K % 128 (output columns)
+    w = lib.fp8_gemm_mxfp8_wgrad
+    assert w(P, P, P, P, 100, 128, 128, P, 0, None) == ERR_SHAPE           # tokens % 128
+    assert w(P, P, P, P, 128, 128, 128, None, 0, None) == ERR_NULL
+    assert w(P, P, P, P, 128, 0, 128, P, 0, None) == OK
 
 
 def test_grouped_validation(lib):
