@@ -27,4 +27,4 @@ Parity status of each function is stated in its docstring ("pinned by ..." or
 "parity unpinned").
 """
 
-from . import fp8_formats, quantize, gemm, weight_sync, producers  # noqa: F401
+from . import fp8_formats, quantize, gemm, weight_sync, producers, fp8_param  # noqa: F401
