@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install|producers|mx_dense] [--no-cpu-baseline]
+                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install|producers|mx_dense|fp8_param] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
 HBM. The default workload is the dense layer shaped like a ~9B model's MLP
@@ -57,9 +57,15 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # last-level cache are included.
 MEASURED_TRAFFIC = {
     "gemm_gu": {"sha": "2937a39ef29013ef", "gb": 1.6281},        # read 1.2258 + write 0.4024
+    "gemm_gu_pow2": {"sha": "2937a39ef29013ef", "gb": 1.6280},   # read 1.2257 + write 0.4024
     "dgrad": {"sha": "2937a39ef29013ef", "gb": 1.3005},          # read 1.2335 + write 0.0671
+    "dgrad_pow2": {"sha": "2937a39ef29013ef", "gb": 1.3005},     # read 1.2334 + write 0.0671
     "mx_fwd": {"sha": "2937a39ef29013ef", "gb": 1.6408},         # read 1.2385 + write 0.4024
     "decode_n24576": {"sha": "6e30ff2362398afe", "gb": 0.1221},  # read 0.1095 + write 0.0126 (GEMM launch)
+    "grouped_gu": {"sha": "507c9c7b91309811", "gb": 0.5539},     # read 0.4868 + write 0.0672
+    "install_gu": {"sha": "977959b7e9590927", "gb": 0.2014},     # read 0.1007 + write 0.1007
+    "swiglu_fp8": {"sha": "f71e26464895891b", "gb": 0.6477},     # read 0.4034 + write 0.2443
+    "requant_gu": {"sha": "af0cd780a8ce2f48", "gb": 0.6040},     # read 0.4026 + write 0.2014
 }
 
 
@@ -81,6 +87,7 @@ KERNEL_SOURCES = {
     "grouped_gu": ("grouped.hip", "device.hpp"),
     "install_gu": ("install.hip", "device.hpp"),
     "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp"),
+    "requant_gu": ("fp8_param.hip", "device.hpp"),
 }
 
 
@@ -99,7 +106,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense", choices=["dense", "dense_pow2", "decode", "backward", "backward_pow2", "moe",
-                                                         "install", "producers", "mx_dense"])
+                                                         "install", "producers", "mx_dense", "fp8_param"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -325,6 +332,47 @@ def mx_dense_setup(torch, F, W, dev):
                "bf16 read 2 B + row and column E4M3 payloads + E8M0 scales per element"),
         gemm_keys=("fwd", "dgrad", "wgrad"),
         traffic_key="mx_fwd",
+    )
+    return step, timers, info
+
+
+def fp8_param_setup(torch, F, W, dev):
+    """fp8_param requantization after an optimizer step: the FP32 masters of the dense layer's
+    gate/up (24576x4096) and down (4096x12288) weights quantized per 128x128 block into FP8
+    storage, with the byte-transposed copy DGrad reads. The masters are the dense workload's
+    weights in fp32 plus a small fp32 perturbation (all 24 significand bits in use)."""
+    d = W.dense_forward(with_down=True)
+    rng = np.random.default_rng(7)
+    masters = []
+    for k in ("w_gu", "w_dn"):
+        m32 = d[k] + (rng.standard_normal(d[k].shape, dtype=np.float32) * np.float32(1e-6))
+        masters.append(torch.from_numpy(m32.astype(np.float32)).to(dev))
+    del d
+    outs = []
+    for m in masters:
+        N, K = m.shape
+        outs.append((torch.empty((N, K), dtype=torch.uint8, device=dev),
+                     torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
+                     torch.empty((K, N), dtype=torch.uint8, device=dev)))
+    timers = {k: EventTimer(torch) for k in ("requant_gu", "requant_dn")}
+
+    def step(timed):
+        for name, m, (q, s_, qt) in zip(("requant_gu", "requant_dn"), masters, outs):
+            if timed: timers[name].start()
+            F.fp8_quant_w_128x128_f32(m, q=q, s=s_, qt=qt, transpose=True)
+            if timed: timers[name].stop()
+
+    per = [m.numel() * (4 + 2) + (m.numel() // (128 * 128)) * 4 for m in masters]
+    info = dict(
+        config={"workload": "fp8_param_requant_dense_layer_9b", "masters": ["gate_up 24576x4096 fp32",
+                                                                          "down 4096x12288 fp32"],
+                "recipe": "128x128 blocks, fp32 scales, row + byte-transposed E4M3"},
+        flops=None,
+        bytes=sum(per),
+        dominant=("requant_gu", "hbm", per[0] / 1e9, "GB/s", PEAK_HBM_GBS,
+                  f"fp32 read 4 B + E4M3 row and transposed copies 2 B per element + scales = {per[0]} B"),
+        quant=None,
+        gemm_keys=(),
     )
     return step, timers, info
 
@@ -590,7 +638,8 @@ def main():
     F.load_library()
     setup = {"dense": dense_setup, "dense_pow2": lambda *args: dense_setup(*args, pow2=True), "decode": decode_setup,
              "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup,
-             "install": install_setup, "producers": producers_setup, "mx_dense": mx_dense_setup}[a.workload]
+             "install": install_setup, "producers": producers_setup, "mx_dense": mx_dense_setup,
+             "fp8_param": fp8_param_setup}[a.workload]
     step, timers, info = setup(torch, F, W, dev)
 
     for _ in range(a.warmup):
@@ -642,7 +691,7 @@ def main():
                                  "per_launch": qdesc}
     if "extra" in info:
         out["unfused_kernel_us"] = info["extra"]()
-    if not a.no_cpu_baseline and a.workload != "install":
+    if not a.no_cpu_baseline and a.workload not in ("install", "fp8_param"):
         out["cpu_baseline"] = cpu_baseline(a.workload)
     print(json.dumps(out))
 

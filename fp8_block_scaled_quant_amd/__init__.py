@@ -30,6 +30,7 @@ __all__ = [
     "fp8_gemm_blockscaled_pow2_dgrad", "fp8_gemm_blockscaled_pow2_wgrad",
     "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16", "fp8_rmsnorm_quant_1x128",
     "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad", "fp8_gemm_mxfp8_wgrad",
+    "fp8_quant_w_128x128_f32",
 ]
 
 RECIPE_BLOCK128 = 0
@@ -70,6 +71,7 @@ _SIGNATURES = {
     "fp8_gemm_blockscaled_pow2_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_swiglu_bf16": ([_vp, _i64, _i64, _vp, _vp], _int),
     "mxfp8_quant_act_1x32": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
+    "fp8_quant_w_128x128_f32": ([_vp, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
     "fp8_gemm_mxfp8_fwd": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_mxfp8_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_mxfp8_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
@@ -280,6 +282,21 @@ def mxfp8_quant_1x32(x, q=None, e8m0=None):
     e8m0 = _out(e8m0, torch.uint8, tuple(x.shape[:-1]) + (K // 32,), dev, "e8m0")
     _check(lib.mxfp8_quant_1x32(_ptr(x), R, K, _ptr(q), _ptr(e8m0), _stream(dev)), "mxfp8_quant_1x32")
     return q, e8m0
+
+
+def fp8_quant_w_128x128_f32(w, q=None, s=None, qt=None, *, transpose=False, pow2_scales=False):
+    """fp8_param requantization: 128x128-block quantization of an fp32 master W [N][K].
+    Returns (q [N][K] u8, s [N/128][K/128] f32, qt [K][N] u8 or None)."""
+    lib = load_library()
+    N, K = w.shape
+    _need(w, torch.float32, (N, K), "w")
+    dev = w.device
+    q = _out(q, torch.uint8, (N, K), dev, "q")
+    s = _out(s, torch.float32, (N // 128, K // 128), dev, "s")
+    qt = _out(qt, torch.uint8, (K, N), dev, "qt") if transpose else None
+    _check(lib.fp8_quant_w_128x128_f32(_ptr(w), N, K, _ptr(q), _ptr(s), _ptr(qt), 1 if pow2_scales else 0,
+                                       _stream(dev)), "fp8_quant_w_128x128_f32")
+    return q, s, qt
 
 
 def mxfp8_quant_act_1x32(x, q=None, e8m0=None, qt=None, e8m0t=None, *, rowwise=True, colwise=False):

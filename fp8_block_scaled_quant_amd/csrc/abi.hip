@@ -141,6 +141,18 @@ fp8rl_status fp8_quant_act_1x128_pow2(const uint16_t* x, int64_t M, int64_t K, u
   return quant_act_impl(x, M, K, q, s, qt, st, true, stream);
 }
 
+fp8rl_status fp8_quant_w_128x128_f32(const float* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                     int pow2_scales, void* stream) {
+  if (q == nullptr || s == nullptr) return FP8RL_ERR_NULL;
+  if (fp8rl_status e = check_dims(N, K)) return e;
+  if (N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8RL_OK;
+  if (w == nullptr) return FP8RL_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || (qt && !aligned(qt, 16))) return FP8RL_ERR_ALIGN;
+  if (fp8rl_status e = check_device()) return e;
+  return launched(launch_quant_w_f32(w, N, K, q, s, qt, pow2_scales != 0, as_stream(stream)));
+}
+
 fp8rl_status fp8_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, void* stream) {
   if (fp8rl_status e = swiglu_check(gu, M, F)) return e;
   if (M == 0 || F == 0) return FP8RL_OK;

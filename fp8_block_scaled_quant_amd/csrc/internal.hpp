@@ -14,6 +14,9 @@ hipError_t launch_quant_act_tile(const uint16_t* x, int64_t M, int64_t K, uint8_
                                  float* st, bool pow2, hipStream_t stream);
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
                                   bool pow2, hipStream_t stream);
+// fp8_param: 128x128-block quantization of an fp32 master W[N][K] (fp8_param.hip).
+hipError_t launch_quant_w_f32(const float* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt, bool pow2,
+                              hipStream_t stream);
 // Fused producers (producers.hip). gu is [M][2F] = [gate | up]; rstd [M].
 hipError_t launch_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s, uint8_t* qt,

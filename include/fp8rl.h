@@ -65,7 +65,7 @@ typedef enum {
 } fp8rl_out;
 
 /* ABI version of this header. */
-#define FP8RL_ABI_VERSION 4
+#define FP8RL_ABI_VERSION 5
 int fp8rl_abi_version(void);
 const char* fp8rl_status_str(fp8rl_status status);
 
@@ -108,6 +108,18 @@ fp8rl_status fp8_quant_act_1x128_pow2(const uint16_t* x, int64_t M, int64_t K,
                                       uint8_t* q, float* s, uint8_t* qt, float* st, void* stream);
 fp8rl_status fp8_quant_w_128x128_pow2(const uint16_t* w, int64_t N, int64_t K,
                                       uint8_t* q, float* s, uint8_t* qt, void* stream);
+
+/* fp8_param requantization ([SkyRL-FP8] "Deep dive: FP8 quantization with FP32 and
+ * power-of-two block scales": the optimizer updates an FP32 master copy and the FP8
+ * parameter storage is recomputed from it after each step). 128x128 blocks quantized from
+ * fp32 values: s = fl32(amax / 448) (pow2_scales == 0) or the power-of-two rule of
+ * fp8_quant_w_128x128_pow2 (pow2_scales != 0); q = E4M3(fl32(w / s)) with an IEEE fp32
+ * division (exact scaling for power-of-two scales).
+ *   w  : fp32 [N][K], finite;  q uint8 [N][K];  s fp32 [N/128][K/128]
+ *   qt : optional (NULL allowed) byte transpose of q, uint8 [K][N] (the DGrad operand).
+ * Rules: N % 128 == 0, K % 128 == 0. Bytes and scales are bit-identical to the CPU oracle. */
+fp8rl_status fp8_quant_w_128x128_f32(const float* w, int64_t N, int64_t K, uint8_t* q, float* s, uint8_t* qt,
+                                     int pow2_scales, void* stream);
 
 /* MXFP8 quantization, one E8M0 scale per 1x32 group along K ([SkyRL-FP8] "When
  * independent quantization breaks policy consistency": one scale per 1x32 block; "Deep

@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
               "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd", "fp8_gemm_blockscaled_pow2_dgrad",
               "fp8_gemm_blockscaled_pow2_wgrad", "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16",
               "fp8_rmsnorm_quant_1x128", "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad",
-              "fp8_gemm_mxfp8_wgrad"]:
+              "fp8_gemm_mxfp8_wgrad", "fp8_quant_w_128x128_f32"]:
         assert n in names
 
 
@@ -58,7 +58,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8rl_abi_version() == 4
+    assert lib.fp8rl_abi_version() == 5
     for code in range(9):
         assert len(lib.fp8rl_status_str(code)) > 0
     assert lib.fp8rl_status_str(99) == b"unknown status"
@@ -150,6 +150,17 @@ def test_producer_validation(lib):
     assert rq(P, P, 4, 128, 1e-6, P, None, None, None, None, 0, None) == ERR_NULL
     assert rq(P, P, 4, 128, -1.0, P, P, P, None, None, 0, None) == ERR_VALUE
     assert rq(P, P, 0, 128, 1e-6, None, P, P, None, None, 0, None) == OK
+
+
+def test_fp8_param_validation(lib):
+    f = lib.fp8_quant_w_128x128_f32
+    assert f(P, 128, 128, None, P, None, 0, None) == ERR_NULL
+    assert f(P, 100, 128, P, P, None, 0, None) == ERR_SHAPE
+    assert f(P, 128, 64, P, P, None, 1, None) == ERR_SHAPE
+    assert f(MIS, 128, 128, P, P, None, 0, None) == ERR_ALIGN
+    assert f(P, 128, 128, P, P, MIS, 0, None) == ERR_ALIGN
+    assert f(None, 128, 128, P, P, None, 0, None) == ERR_NULL
+    assert f(None, 0, 128, P, P, None, 0, None) == OK
 
 
 def test_mx_dense_validation(lib):
