@@ -182,3 +182,82 @@ def test_moe_mxfp8_full_size():
             else:
                 half_ulp = np.ldexp(1.0, np.frexp(np.abs(got.astype(np.float64)))[1] - 9)
                 assert np.all(np.abs(got - ref) <= 2e-3 * rms + half_ulp), f"{name} expert {e} outside tolerance"
+
+
+def test_producers_full_size():
+    """Fused SwiGLU -> FP8 (GU 8192x24576, rows + cols) and RMSNorm -> FP8 (X 8192x4096, rows
+    + cols) as the producers workload runs them; sampled rows (1x128 groups, r) and sampled
+    columns (128x1 groups over all rows) against the oracle."""
+    from oracle import producers as OP
+    d = W.fused_producers()
+    gu = W.to_bf16_tensor(d["gu"]).to(dev())
+    x = W.to_bf16_tensor(d["x"]).to(dev())
+    gamma = W.to_bf16_tensor(d["gamma"]).to(dev())
+    M = d["gu"].shape[0]
+    hq, hs, hqt, hst = F.fp8_swiglu_quant_1x128(gu, colwise=True)
+    xq, xs, xqt, xst, rstd = F.fp8_rmsnorm_quant_1x128(x, gamma, d["eps"], colwise=True)
+    rows = _sample(M, 16, 40)
+    rq, rs = OP.swiglu_quant_1x128(d["gu"][rows])
+    assert_bytes_equal(_rows_of(hq, rows), rq, "swiglu q rows")
+    assert_bytes_equal(_rows_of(hs, rows), rs, "swiglu s rows")
+    Fh = d["gu"].shape[1] // 2
+    cols = _sample(Fh, 6, 41)
+    h_cols = OP.swiglu_bf16(np.concatenate([d["gu"][:, cols], d["gu"][:, Fh + cols]], axis=1))
+    rqt, rst = OQ.quant_act_128x1(h_cols)
+    assert_bytes_equal(_rows_of(hqt, cols), rqt, "swiglu qt columns")
+    assert_bytes_equal(_rows_of(hst, cols), rst, "swiglu st columns")
+    ry, rr, amb = OP.rmsnorm_bf16(d["x"][rows], d["gamma"], d["eps"])
+    assert not amb.any()
+    assert_bytes_equal(_rows_of(rstd, rows), rr, "rstd rows")
+    rq2, rs2 = OQ.quant_act_1x128(ry)
+    assert_bytes_equal(_rows_of(xq, rows), rq2, "rmsnorm q rows")
+    assert_bytes_equal(_rows_of(xs, rows), rs2, "rmsnorm s rows")
+
+
+def test_mx_dense_full_size(dense):
+    """The MXFP8 dense gate/up layer as the mx_dense workload runs it: quantized bytes of
+    sampled rows / columns and sampled outputs of the forward, DGrad and WGrad GEMMs."""
+    d, t = dense
+    dy_np = W.dense_backward()["dy"]
+    dy = W.to_bf16_tensor(dy_np).to(dev())
+    M, K = d["x"].shape
+    N = d["w_gu"].shape[0]
+    xq, ex, xqt, ext = F.mxfp8_quant_act_1x32(t["x"], colwise=True)
+    wq, ew, wqt, ewt = F.mxfp8_quant_act_1x32(t["w_gu"], colwise=True)
+    dyq, edy, dyqt, edyt = F.mxfp8_quant_act_1x32(dy, colwise=True)
+    y = F.fp8_gemm_mxfp8_fwd(xq, ex, wq, ew, out_dtype=torch.float32)
+    dx = F.fp8_gemm_mxfp8_dgrad(dyq, edy, wqt, ewt, out_dtype=torch.float32)
+    dw = F.fp8_gemm_mxfp8_wgrad(dyqt, edyt, xqt, ext)
+    rows, ns, ks = _sample(M, 8, 42), _sample(N, 8, 43), _sample(K, 8, 44)
+    rxq, rex = OQ.quant_mx_1x32(d["x"][rows])
+    rwq, rew = OQ.quant_mx_1x32(d["w_gu"][ns])
+    assert_bytes_equal(_rows_of(xq, rows), rxq, "mx xq rows")
+    assert_bytes_equal(_rows_of(wq, ns), rwq, "mx wq rows")
+    assert_gemm_close(host(_rows_of(y, rows))[:, ns], OG.gemm_mx_fwd(rxq, rex, rwq, rew), "mx fwd")
+    rdyq, redy = OQ.quant_mx_1x32(dy_np[rows])
+    rwqt, rewt = OQ.quant_mx_1x32(np.ascontiguousarray(d["w_gu"][:, ks].T))
+    assert_bytes_equal(_rows_of(wqt, ks), rwqt, "mx wqt columns")
+    assert_bytes_equal(_rows_of(ewt, ks), rewt, "mx ewt columns")
+    assert_gemm_close(host(_rows_of(dx, rows))[:, ks], OG.gemm_mx_dgrad(rdyq, redy, rwqt, rewt), "mx dgrad")
+    rdyqt, redyt = OQ.quant_mx_1x32(np.ascontiguousarray(dy_np[:, ns].T))
+    rxqt, rext = OQ.quant_mx_1x32(np.ascontiguousarray(d["x"][:, ks].T))
+    assert_bytes_equal(_rows_of(dyqt, ns), rdyqt, "mx dyqt columns")
+    assert_gemm_close(host(_rows_of(dw, ns))[:, ks], OG.gemm_mx_wgrad(rdyqt, redyt, rxqt, rext), "mx wgrad")
+
+
+def test_fp8_param_full_size():
+    """fp8_param requantization of the gate/up fp32 master (24576x4096, as the fp8_param
+    workload builds it): sampled 128x128 blocks, their scales and transposed bytes."""
+    from oracle import fp8_param as OP8
+    d = W.dense_forward(with_down=False)
+    rng = np.random.default_rng(7)
+    m32 = (d["w_gu"] + rng.standard_normal(d["w_gu"].shape, dtype=np.float32) * np.float32(1e-6)).astype(np.float32)
+    q, s, qt = F.fp8_quant_w_128x128_f32(torch.from_numpy(m32).to(dev()), transpose=True)
+    N, K = m32.shape
+    for bi in _sample(N // 128, 3, 45):
+        rows = np.arange(bi * 128, (bi + 1) * 128)
+        rq, rs = OP8.quant_w_128x128_f32(m32[rows])
+        assert_bytes_equal(_rows_of(q, rows), rq, f"q block row {bi}")
+        assert_bytes_equal(_rows_of(s, np.array([bi])), rs, f"s block row {bi}")
+        got_t = host(qt)[:, rows]
+        assert np.array_equal(got_t, rq.T), f"qt block row {bi}"
