@@ -19,6 +19,11 @@
 //   the loads of block kb+1 overlap the MFMAs of block kb; one barrier per K block.
 //   The two stages are distinct LDS objects and the K loop is unrolled by two, so each
 //   compute phase reads a statically known stage.
+// * Row scales (1x128 / 128x1 groups: one fp32 or E8M0 dword per row per K block) come SK
+//   K blocks at a time (SK = 8, or 4 when B's row scales come too) into a double-buffered
+//   LDS ring: one cache-line request per row per SK K blocks instead of one per row per K
+//   block. Those 4-byte loads were a third of the kernel's L2 read requests, and the
+//   number of requests in flight per CU is what limits the operand copies.
 // * Rows are 128 bytes with a 16-byte-chunk XOR swizzle to keep fragment reads
 //   bank-conflict free.
 // * Workgroups are mapped to tiles XCD-aware (contiguous tile ranges per XCD) and in
@@ -37,7 +42,10 @@ constexpr int kLag = 3;
 //         1 = power-of-two fp32 scales (their exponent fields go to the scaled MFMA),
 //         2 = MXFP8: each scale dword holds the 4 E8M0 bytes of a row's 128-K block, one per
 //             32-wide part; lane l hands the MFMA the byte of part l >> 4.
-template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, int kScale>
+// SK: 1 = every scale is loaded per K block into the stage; otherwise A's row scales (and
+//     B's, when they are row scales applied by the MFMA: SK = 4) come SK K blocks at a time
+//     through the ring, and K / 128 must be a multiple of SK.
+template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, int kScale, int SK>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -53,8 +61,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   static_assert(OFF_SB + NSB * 4 <= STAGE, "scale slots");
   static_assert(kRowB || TN <= 128, "a wave's n range must sit inside one 128-row scale block");
   static_assert(kLag < FM, "a folded tile is at most one B fragment behind");
+  constexpr bool kChunkB = SK > 1 && kRowB && kScale != 0;   // B's row scales come through the ring
+  constexpr int CROWS = BM + (kChunkB ? BN : 0);               // ring rows: A's, then B's
+  constexpr int CBUF = CROWS * SK * 4;                         // bytes per ring buffer
+  constexpr int LPR = SK > 4 ? SK / 4 : 1;                     // ring lanes per row, 16 bytes each
+  static_assert(LPR >= 1, "LPR divides lane indices");
+  static_assert(SK == 1 || (SK == (kChunkB ? 4 : 8) && CROWS * LPR == NT), "every lane loads one ring piece");
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t scr[SK > 1 ? 2 * CBUF : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,10 +105,26 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   const uint32_t off0 = (uint32_t)(lr * K) + (uint32_t)(swz(lr, tid & 7) << 4);
   const uint32_t bytesA = (uint32_t)((rows_a - 1) * K + 128), bytesB = (uint32_t)((rows_b - 1) * K + 128);
   // Scale loads: waves [0, BM/64) fetch sA of the tile rows, the next NSB/64 waves fetch
-  // sB; every other wave issues the same instruction through an empty descriptor (no
-  // memory access) into its own unused slot, which keeps the K step branch-free.
+  // sB; every other wave issues the same per-K-block instruction through an empty
+  // descriptor (no memory access) into its own unused slot, which keeps that part of the K
+  // step branch-free. With SK > 1 only B's scales that do not go through the ring are
+  // loaded per K block.
   const bool sa_wave = wave < BM / 64;
   const bool sb_wave = !sa_wave && wave < BM / 64 + NSB / 64;
+  const bool pb_wave = SK == 1 || (sb_wave && !kChunkB);         // per-K-block scale load
+  // Ring loads: lane idx = wave * 64 + lane loads 16 bytes (4 K blocks) of ring row
+  // idx / LPR (A's rows, then B's), piece idx % LPR; the ring row r, K block kb % SK sits at
+  // byte (r * SK + kb % SK) * 4 of a buffer, which is where the lane-ordered LDS write puts it.
+  const int cidx = wave * 64 + lane;
+  const int crow = cidx / LPR;
+  const bool c_a = crow < BM;                                    // wave-uniform
+  const float* cbase = c_a ? p.sA + m0 * p.sa_ld : p.sB + n0 * p.sb_ld_n;
+  const int64_t cld = c_a ? p.sa_ld : p.sb_ld_n;
+  const uint32_t coff = (uint32_t)(((c_a ? crow : crow - BM) * cld + (cidx % LPR) * 4) * 4);
+  // Rows past the tile's last valid row read as zero; nkb % SK == 0 keeps every load of a
+  // valid row inside that row's scales.
+  const uint32_t cbytes = (uint32_t)(((c_a ? rows_a : rows_b) - 1) * cld * 4 + nkb * 4);
+  const uint32_t scr0 = lds_addr(scr);
   const float* baseS;
   uint32_t offS, bytesS;
   int64_t sstep;  // floats per K block
@@ -131,7 +162,14 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
       const uint32_t nb = (live && bytesB > r0 * K) ? (uint32_t)(bytesB - r0 * K) : 0u;
       dma16(make_rsrc(p.B + (n0 + r0) * K + kbc * 128, nb), off0, st + OFF_B + (it * NT + wave * 64) * 16);
     }
-    dma4(make_rsrc(baseS + kbc * sstep, live ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
+    dma4(make_rsrc(baseS + kbc * sstep, (live && pb_wave) ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
+    if constexpr (SK > 1) {
+      // At kb % SK == 0: row scales of K blocks kb .. kb + SK - 1 into ring buffer
+      // (kb / SK) & 1, whose previous contents were read by K blocks that every wave
+      // finished before the barrier preceding this issue. Otherwise nothing moves.
+      dma16_if(make_rsrc(cbase, cbytes), coff + (uint32_t)(kbc * 4), scr0 + ((kb / SK) & 1) * CBUF + wave * 1024,
+               (uint32_t)(live && kb % SK == 0));
+    }
   };
 
   v4f acc[FN][FM];
@@ -150,22 +188,25 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   // fragments are double-buffered (fragment i+1 is read while fragment i feeds the MFMAs);
   // the FMAs that fold tile t-1 into the accumulators follow the MFMA of tile t
   // (t = i * FM + j), so one MFMA result is in flight while the previous one is folded.
-  auto compute = [&](uint32_t st) __attribute__((always_inline)) {
+  auto compute = [&](uint32_t st, int kb) __attribute__((always_inline)) {
     const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi;
     const uint32_t b_lo = st + OFF_B + fb.lo, b_hi = st + OFF_B + fb.hi;
-    const uint32_t sa_ad = st + o_sa, sb_ad = st + o_sb;
+    // Ring slot of K block kb: row r's scale sits at byte (r * SK + kb % SK) * 4 of the buffer.
+    const uint32_t cb = scr0 + ((kb / SK) & 1) * CBUF + (kb % SK) * 4;
+    const uint32_t sa_ad = SK > 1 ? cb + (wm0 + (lane & 15)) * SK * 4 : st + o_sa;
+    const uint32_t sb_ad = st + o_sb;
     v4i alo[FM], ahi[FM];
     float sa[FM];
     static_for<0, FM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       alo[j] = ds_read16<j * 2048>(a_lo);
       ahi[j] = ds_read16<j * 2048>(a_hi);
-      sa[j] = ds_read4f<j * 64>(sa_ad);
+      sa[j] = ds_read4f<j * 16 * SK * 4>(sa_ad);
     });
     float sb = 0.f;
     v4i sbv;
     if (!kRowB) sb = ds_read4f<0>(sb_ad);
-    else sbv = ds_read16<0>(sb_ad);
+    else if (kScale == 0) sbv = ds_read16<0>(sb_ad);
     v4i blo = ds_read16<0>(b_lo), bhi = ds_read16<0>(b_hi);
     lds_wait<0>();
     v8i af[FM];
@@ -195,9 +236,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
       if constexpr (kRowB) {
         // The LDS reads land only at the wait: take the exponents after it.
         float sbr[FN];
+        const uint32_t sbr_ad = kChunkB ? cb + (BM + wn0 + (lane & 15)) * SK * 4 : st + o_sbr;
         static_for<0, FN>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          sbr[i] = ds_read4f<i * 64>(st + o_sbr);
+          sbr[i] = ds_read4f<i * 16 * (kChunkB ? SK : 1) * 4>(sbr_ad);
         });
         lds_wait<0>();
 #pragma unroll
@@ -294,16 +336,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     wait_vmem();
     __syncthreads();
     issue(kb + 1, st1);
-    compute(st0);
+    compute(st0, kb);
     wait_vmem();
     __syncthreads();
     issue(kb + 2, st0);
-    compute(st1);
+    compute(st1, kb + 1);
   }
   if (kb < nkb) {
     wait_vmem();
     __syncthreads();
-    compute(st0);
+    compute(st0, kb);
   }
 
   // Epilogue. The tile goes out through LDS (the stages are free after the K loop), so that
@@ -386,15 +428,24 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool kRowB, int kScale>
-static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, bool kRowB, int kScale, int SK>
+static hipError_t launch_sk(const GemmParams& p, bool f32, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles), block(WM * WN * 64);
   if (f32)
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kScale>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kScale, SK>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kScale>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kScale, SK>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+// 256x256 tiles take their row scales through the ring whenever K / 128 is a multiple of SK.
+template <int BM, int BN, int WM, int WN, bool kRowB, int kScale>
+static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
+  constexpr int SK = (kRowB && kScale != 0) ? 4 : 8;
+  if constexpr (BM == 256)
+    if ((p.K / 128) % SK == 0) return launch_sk<BM, BN, WM, WN, kRowB, kScale, SK>(p, f32, stream);
+  return launch_sk<BM, BN, WM, WN, kRowB, kScale, 1>(p, f32, stream);
 }
 
 // Tile choice: at most 256 rows with block-scaled fp32 scales go to the few-row kernel (skinny.hip);
