@@ -135,20 +135,30 @@ __device__ __forceinline__ void dma4(v4i rsrc, uint32_t voff, uint32_t lds) {
                : "memory", "m0");
 }
 
-// dma16 when `on` (wave-uniform) is non-zero; otherwise the same instruction runs with
-// exec = 0 and moves nothing. exec is saved and restored inside the one asm statement, so
-// the compiler sees no control flow (a branch around the copy in an unrolled K loop made
-// it keep ~40 more VGPRs live).
+// dma16 / dma4 when `on` (wave-uniform) is non-zero; otherwise the copy is skipped. The
+// branch sits inside the one asm statement, so the compiler sees straight-line code (a
+// branch around the copy in the K loop costs the register allocator ~40 VGPRs), and a
+// skipped copy costs the texture unit nothing (unlike one issued with exec = 0 or an empty
+// descriptor, which it processes like a real one).
 __device__ __forceinline__ void dma16_if(v4i rsrc, uint32_t voff, uint32_t lds, uint32_t on) {
-  uint64_t saved;
   asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "s_mov_b64 %0, exec\n\t"
-      "s_cmp_eq_u32 %4, 0\n\t"
-      "s_cmov_b64 exec, 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_mov_b64 exec, %0"
-      : "=&s"(saved)
+      "s_cmp_eq_u32 %3, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds\n"
+      "1:"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds), "s"(__builtin_amdgcn_readfirstlane(on))
+      : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void dma4_if(v4i rsrc, uint32_t voff, uint32_t lds, uint32_t on) {
+  asm volatile(
+      "s_cmp_eq_u32 %3, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds\n"
+      "1:"
+      :
       : "v"(voff), "s"(rsrc), "s"(lds), "s"(__builtin_amdgcn_readfirstlane(on))
       : "memory", "m0", "scc");
 }

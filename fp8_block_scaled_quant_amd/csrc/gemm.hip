@@ -37,6 +37,8 @@ namespace fp8rl {
 
 // Distance, in MFMA tiles, between an MFMA and the FMAs that fold its result.
 constexpr int kLag = 3;
+// Largest K / 128 of the ring configuration (its B block-scale table holds 2 x kMaxKb floats).
+constexpr int kMaxKb = 1024;
 
 // kScale: 0 = fp32 scales (each 128-K block product folded in with one FMA),
 //         1 = power-of-two fp32 scales (their exponent fields go to the scaled MFMA),
@@ -65,11 +67,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   constexpr int CROWS = BM + (kChunkB ? BN : 0);               // ring rows: A's, then B's
   constexpr int CBUF = CROWS * SK * 4;                         // bytes per ring buffer
   constexpr int LPR = SK > 4 ? SK / 4 : 1;                     // ring lanes per row, 16 bytes each
+  // With SK > 1 and 128x128 block scales on B, the tile's B scales (2 block rows x K / 128)
+  // are loaded into an LDS table once, before the K loop (at most kMaxKb K blocks).
+  constexpr bool kPreB = SK > 1 && !kRowB;
+  constexpr int kPreFloats = kPreB ? 2 * kMaxKb : 1;
   static_assert(LPR >= 1, "LPR divides lane indices");
   static_assert(SK == 1 || (SK == (kChunkB ? 4 : 8) && CROWS * LPR == NT), "every lane loads one ring piece");
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t scr[SK > 1 ? 2 * CBUF : 16];
+  __shared__ __attribute__((aligned(16))) float sbk[kPreFloats];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,11 +101,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
 
   // Staged loads go through raw buffer descriptors whose range ends at the last valid row
   // of the tile, so rows past the end of A / B (and their scales) read as zero without a
-  // memory access; their results are never stored.
+  // memory access; their results are never stored. One descriptor per operand and K block
+  // (base: the tile's first row at column kb * 128) serves all of the operand's loads.
   constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;
-  // Load `it` covers tile rows it * NT/8 .. : the same per-lane offset works for every
-  // `it` once the descriptor base moves by it * (NT/8) * K bytes, because NT/8 is a
-  // multiple of 16 and so leaves the row swizzle phase ((r >> 1) & 7) unchanged.
+  // Load `it` covers tile rows it * NT/8 .. : its lane offset is the first load's plus
+  // it * (NT/8) * K bytes, and NT/8 is a multiple of 16, so the row swizzle phase
+  // ((r >> 1) & 7) is the same for every load.
   static_assert((NT / 8) % 16 == 0, "swizzle phase must repeat across loads");
   const int64_t rows_a = min((int64_t)BM, M - m0), rows_b = min((int64_t)BN, N - n0);
   const int lr = tid >> 3;
@@ -111,7 +119,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   // loaded per K block.
   const bool sa_wave = wave < BM / 64;
   const bool sb_wave = !sa_wave && wave < BM / 64 + NSB / 64;
-  const bool pb_wave = SK == 1 || (sb_wave && !kChunkB);         // per-K-block scale load
+  // Per-K-block scale loads: every wave when SK == 1 (empty descriptors for waves without
+  // scales); with SK > 1 only the waves holding B's row scales when they are folded in fp32.
+  const bool pb_wave = SK == 1 || (kRowB && !kChunkB && sb_wave);
   // Ring loads: lane idx = wave * 64 + lane loads 16 bytes (4 K blocks) of ring row
   // idx / LPR (A's rows, then B's), piece idx % LPR; the ring row r, K block kb % SK sits at
   // byte (r * SK + kb % SK) * 4 of a buffer, which is where the lane-ordered LDS write puts it.
@@ -145,33 +155,43 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     sstep = p.sb_ld_k;
   }
 
-  // Stage the operands of K block kb into the stage at LDS address st. For kb >= nkb every
-  // descriptor is empty: the loads write zeros without touching memory.
-  auto issue = [&](int kb, uint32_t st) __attribute__((always_inline)) {
+  // Stage the operands of K block kb into the stage at LDS address st: operand copy `part`
+  // (A's loads, then B's), and the scale copies. For kb >= nkb every descriptor is empty:
+  // the loads write zeros without touching memory.
+  constexpr int NPART = LA + LB;
+  auto issue_part = [&](int kb, uint32_t st, auto partc) __attribute__((always_inline)) {
+    constexpr int part = decltype(partc)::value;
     const bool live = kb < nkb;
     const int kbc = live ? kb : 0;
-#pragma unroll
-    for (int it = 0; it < LA; ++it) {
-      const int64_t r0 = (int64_t)it * (NT / 8);
-      const uint32_t nb = (live && bytesA > r0 * K) ? (uint32_t)(bytesA - r0 * K) : 0u;
-      dma16(make_rsrc(p.A + (m0 + r0) * K + kbc * 128, nb), off0, st + (it * NT + wave * 64) * 16);
+    if constexpr (part < LA) {
+      dma16(make_rsrc(p.A + m0 * K + kbc * 128, live ? bytesA : 0u), off0 + (uint32_t)(part * (NT / 8)) * (uint32_t)K,
+            st + (part * NT + wave * 64) * 16);
+    } else {
+      dma16(make_rsrc(p.B + n0 * K + kbc * 128, live ? bytesB : 0u), off0 + (uint32_t)((part - LA) * (NT / 8)) * (uint32_t)K,
+            st + OFF_B + ((part - LA) * NT + wave * 64) * 16);
     }
-#pragma unroll
-    for (int it = 0; it < LB; ++it) {
-      const int64_t r0 = (int64_t)it * (NT / 8);
-      const uint32_t nb = (live && bytesB > r0 * K) ? (uint32_t)(bytesB - r0 * K) : 0u;
-      dma16(make_rsrc(p.B + (n0 + r0) * K + kbc * 128, nb), off0, st + OFF_B + (it * NT + wave * 64) * 16);
-    }
-    dma4(make_rsrc(baseS + kbc * sstep, (live && pb_wave) ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
-    if constexpr (SK > 1) {
+  };
+  auto issue_scales = [&](int kb, uint32_t st) __attribute__((always_inline)) {
+    const bool live = kb < nkb;
+    const int kbc = live ? kb : 0;
+    if constexpr (SK == 1) {
+      dma4(make_rsrc(baseS + kbc * sstep, live ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
+    } else {
+      // Only the waves and K blocks that own scale copies issue one: an instruction with an
+      // empty descriptor or exec = 0 still costs the texture unit the time of a real one.
+      if constexpr (kRowB && !kChunkB)
+        dma4_if(make_rsrc(baseS + kbc * sstep, bytesS), offS, st + OFF_SA + wave * 256, (uint32_t)(pb_wave && live));
       // At kb % SK == 0: row scales of K blocks kb .. kb + SK - 1 into ring buffer
       // (kb / SK) & 1, whose previous contents were read by K blocks that every wave
-      // finished before the barrier preceding this issue. Otherwise nothing moves.
+      // finished before the barrier preceding this issue.
       dma16_if(make_rsrc(cbase, cbytes), coff + (uint32_t)(kbc * 4), scr0 + ((kb / SK) & 1) * CBUF + wave * 1024,
                (uint32_t)(live && kb % SK == 0));
     }
   };
-
+  auto issue = [&](int kb, uint32_t st) __attribute__((always_inline)) {
+    static_for<0, NPART>([&](auto pc) { issue_part(kb, st, pc); });
+    issue_scales(kb, st);
+  };
   v4f acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -183,6 +203,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   const uint32_t o_sa = OFF_SA + (wm0 + (lane & 15)) * 4;
   const uint32_t o_sb = kRowB ? OFF_SB + (wn0 + 4 * (lane >> 4)) * 4 : OFF_SB + (uint32_t)(((n0 + wn0) >> 7) - nb0) * 4;
   const uint32_t o_sbr = OFF_SB + (wn0 + (lane & 15)) * 4;     // row (lane & 15) of each B fragment
+  const uint32_t sbk_w = lds_addr(sbk) + (uint32_t)((((n0 + wn0) >> 7) - nb0) * nkb) * 4;
 
   // One K block from the stage at st. A fragments stay in registers for the whole block; B
   // fragments are double-buffered (fragment i+1 is read while fragment i feeds the MFMAs);
@@ -194,7 +215,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     // Ring slot of K block kb: row r's scale sits at byte (r * SK + kb % SK) * 4 of the buffer.
     const uint32_t cb = scr0 + ((kb / SK) & 1) * CBUF + (kb % SK) * 4;
     const uint32_t sa_ad = SK > 1 ? cb + (wm0 + (lane & 15)) * SK * 4 : st + o_sa;
-    const uint32_t sb_ad = st + o_sb;
+    // B's block scale of this wave's 128 columns: its table entry, or the stage slot.
+    const uint32_t sb_ad = kPreB ? sbk_w + kb * 4 : st + o_sb;
     v4i alo[FM], ahi[FM];
     float sa[FM];
     static_for<0, FM>([&](auto jc) {
@@ -330,6 +352,22 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   // barrier (all waves' copies landed, and everyone is done reading the other stage),
   // start copying K block kb+1 into the other stage, then compute on the current one.
   const uint32_t st0 = lds_addr(sm0), st1 = lds_addr(sm1);
+  const uint32_t sbk0 = lds_addr(sbk);
+  if constexpr (kPreB) {
+    // Entry e of the table is B block row e / nkb (of the tile's two), K block e % nkb; the
+    // descriptor's range ends at the last valid entry, so entries of a block row past the
+    // end of B read as zero or as other scales of B (never used). Entries past 2 * nkb read
+    // as zero. The K loop's first wait and barrier cover these copies.
+    const int ne = 2 * nkb;
+    const v4i rs = make_rsrc(p.sB + nb0 * p.sb_ld_n,
+                             (uint32_t)(((nbl - nb0) * p.sb_ld_n + (int64_t)(nkb - 1) * p.sb_ld_k + 1) * 4));
+    for (int e0 = 0; e0 < ne; e0 += NT) {
+      const int e = e0 + wave * 64 + lane;
+      const int r = e / nkb, k = e - r * nkb;
+      const uint32_t off = e < ne ? (uint32_t)((r * p.sb_ld_n + (int64_t)k * p.sb_ld_k) * 4) : 0xfffffff0u;
+      dma4(rs, off, sbk0 + (e0 + wave * 64) * 4);
+    }
+  }
   issue(0, st0);
   int kb = 0;
   for (; kb + 2 <= nkb; kb += 2) {
@@ -444,7 +482,7 @@ template <int BM, int BN, int WM, int WN, bool kRowB, int kScale>
 static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
   constexpr int SK = (kRowB && kScale != 0) ? 4 : 8;
   if constexpr (BM == 256)
-    if ((p.K / 128) % SK == 0) return launch_sk<BM, BN, WM, WN, kRowB, kScale, SK>(p, f32, stream);
+    if ((p.K / 128) % SK == 0 && p.K / 128 <= kMaxKb) return launch_sk<BM, BN, WM, WN, kRowB, kScale, SK>(p, f32, stream);
   return launch_sk<BM, BN, WM, WN, kRowB, kScale, 1>(p, f32, stream);
 }
 
