@@ -106,6 +106,7 @@ __device__ __forceinline__ float absmax2(uint32_t w) {
 // offsets >= bytes return zero instead of touching memory (the hardware range check of
 // raw buffers, stride 0). The last word is the gfx9 buffer format word.
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   v4i r;
@@ -135,7 +136,7 @@ __device__ __forceinline__ void dma4(v4i rsrc, uint32_t voff, uint32_t lds) {
                : "memory", "m0");
 }
 
-// dma16 / dma4 when `on` (wave-uniform) is non-zero; otherwise the copy is skipped. The
+// dma16 when `on` (wave-uniform) is non-zero; otherwise the copy is skipped. The
 // branch sits inside the one asm statement, so the compiler sees straight-line code (a
 // branch around the copy in the K loop costs the register allocator ~40 VGPRs), and a
 // skipped copy costs the texture unit nothing (unlike one issued with exec = 0 or an empty
@@ -146,17 +147,6 @@ __device__ __forceinline__ void dma16_if(v4i rsrc, uint32_t voff, uint32_t lds, 
       "s_cbranch_scc1 1f\n\t"
       "s_mov_b32 m0, %2\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds\n"
-      "1:"
-      :
-      : "v"(voff), "s"(rsrc), "s"(lds), "s"(__builtin_amdgcn_readfirstlane(on))
-      : "memory", "m0", "scc");
-}
-__device__ __forceinline__ void dma4_if(v4i rsrc, uint32_t voff, uint32_t lds, uint32_t on) {
-  asm volatile(
-      "s_cmp_eq_u32 %3, 0\n\t"
-      "s_cbranch_scc1 1f\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "buffer_load_dword %0, %1, 0 offen lds\n"
       "1:"
       :
       : "v"(voff), "s"(rsrc), "s"(lds), "s"(__builtin_amdgcn_readfirstlane(on))
@@ -208,6 +198,14 @@ template <int OFF>
 __device__ __forceinline__ float ds_read4f(uint32_t addr) {
   float r;
   asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Two dwords at addr + 4 * O0 and addr + 4 * O1 (offsets in dwords, at most 255).
+template <int O0, int O1>
+__device__ __forceinline__ v2i ds_read2_b32(uint32_t addr) {
+  static_assert(O0 >= 0 && O0 <= 255 && O1 >= 0 && O1 <= 255, "ds_read2_b32 offsets");
+  v2i r;
+  asm volatile("ds_read2_b32 %0, %1 offset0:%2 offset1:%3" : "=v"(r) : "v"(addr), "i"(O0), "i"(O1));
   return r;
 }
 template <int N>

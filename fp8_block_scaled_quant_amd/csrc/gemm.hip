@@ -63,7 +63,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   static_assert(OFF_SB + NSB * 4 <= STAGE, "scale slots");
   static_assert(kRowB || TN <= 128, "a wave's n range must sit inside one 128-row scale block");
   static_assert(kLag < FM, "a folded tile is at most one B fragment behind");
-  constexpr bool kChunkB = SK > 1 && kRowB && kScale != 0;   // B's row scales come through the ring
+  constexpr bool kChunkB = SK > 1 && kRowB;                  // B's row scales come through the ring
   constexpr int CROWS = BM + (kChunkB ? BN : 0);               // ring rows: A's, then B's
   constexpr int CBUF = CROWS * SK * 4;                         // bytes per ring buffer
   constexpr int LPR = SK > 4 ? SK / 4 : 1;                     // ring lanes per row, 16 bytes each
@@ -119,9 +119,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   // loaded per K block.
   const bool sa_wave = wave < BM / 64;
   const bool sb_wave = !sa_wave && wave < BM / 64 + NSB / 64;
-  // Per-K-block scale loads: every wave when SK == 1 (empty descriptors for waves without
-  // scales); with SK > 1 only the waves holding B's row scales when they are folded in fp32.
-  const bool pb_wave = SK == 1 || (kRowB && !kChunkB && sb_wave);
+  // Per-K-block scale loads (SK == 1 only): every wave, with empty descriptors for waves
+  // without scales.
   // Ring loads: lane idx = wave * 64 + lane loads 16 bytes (4 K blocks) of ring row
   // idx / LPR (A's rows, then B's), piece idx % LPR; the ring row r, K block kb % SK sits at
   // byte (r * SK + kb % SK) * 4 of a buffer, which is where the lane-ordered LDS write puts it.
@@ -177,10 +176,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     if constexpr (SK == 1) {
       dma4(make_rsrc(baseS + kbc * sstep, live ? bytesS : 0u), offS, st + OFF_SA + wave * 256);
     } else {
-      // Only the waves and K blocks that own scale copies issue one: an instruction with an
+      // Only the K blocks that start a ring chunk issue a scale copy: an instruction with an
       // empty descriptor or exec = 0 still costs the texture unit the time of a real one.
-      if constexpr (kRowB && !kChunkB)
-        dma4_if(make_rsrc(baseS + kbc * sstep, bytesS), offS, st + OFF_SA + wave * 256, (uint32_t)(pb_wave && live));
       // At kb % SK == 0: row scales of K blocks kb .. kb + SK - 1 into ring buffer
       // (kb / SK) & 1, whose previous contents were read by K blocks that every wave
       // finished before the barrier preceding this issue.
@@ -227,8 +224,21 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     });
     float sb = 0.f;
     v4i sbv;
+    // The fold's B row scales of B-fragment step i: rows wn0 + 16 i + 4 (lane >> 4) .. + 3,
+    // contiguous in the stage slot; 16 bytes apart in the ring.
+    const uint32_t sbv_ad = kChunkB ? cb + (BM + wn0 + 4 * (lane >> 4)) * SK * 4 : sb_ad;
+    auto read_sbv = [&](auto ic) __attribute__((always_inline)) -> v4i {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (kChunkB) {
+        const uint32_t a = sbv_ad + i * 16 * SK * 4;
+        const v2i lo = ds_read2_b32<0, SK>(a), hi = ds_read2_b32<2 * SK, 3 * SK>(a);
+        return v4i{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        return ds_read16<i * 64>(sb_ad);
+      }
+    };
     if (!kRowB) sb = ds_read4f<0>(sb_ad);
-    else if (kScale == 0) sbv = ds_read16<0>(sb_ad);
+    else if (kScale == 0) sbv = read_sbv(std::integral_constant<int, 0>{});
     v4i blo = ds_read16<0>(b_lo), bhi = ds_read16<0>(b_hi);
     lds_wait<0>();
     v8i af[FM];
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
         if constexpr (i + 1 < FN) {
           nlo = ds_read16<(i + 1) * 2048>(b_lo);
           nhi = ds_read16<(i + 1) * 2048>(b_hi);
-          if (kRowB) nsb = ds_read16<(i + 1) * 64>(sb_ad);
+          if (kRowB) nsb = read_sbv(std::integral_constant<int, i + 1>{});
         }
         const v8i bf = join(blo, bhi);
 #pragma unroll
@@ -480,7 +490,7 @@ static hipError_t launch_sk(const GemmParams& p, bool f32, hipStream_t stream) {
 // 256x256 tiles take their row scales through the ring whenever K / 128 is a multiple of SK.
 template <int BM, int BN, int WM, int WN, bool kRowB, int kScale>
 static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
-  constexpr int SK = (kRowB && kScale != 0) ? 4 : 8;
+  constexpr int SK = kRowB ? 4 : 8;
   if constexpr (BM == 256)
     if ((p.K / 128) % SK == 0 && p.K / 128 <= kMaxKb) return launch_sk<BM, BN, WM, WN, kRowB, kScale, SK>(p, f32, stream);
   return launch_sk<BM, BN, WM, WN, kRowB, kScale, 1>(p, f32, stream);
