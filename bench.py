@@ -84,7 +84,7 @@ KERNEL_SOURCES = {
     "dgrad_pow2": ("gemm.hip", "device.hpp"),
     "mx_fwd": ("gemm.hip", "device.hpp"),
     "decode_n24576": ("skinny.hip", "device.hpp"),
-    "grouped_gu": ("grouped.hip", "device.hpp"),
+    "grouped_gu": ("gemm.hip", "device.hpp"),
     "install_gu": ("install.hip", "device.hpp"),
     "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp"),
     "requant_gu": ("fp8_param.hip", "device.hpp"),

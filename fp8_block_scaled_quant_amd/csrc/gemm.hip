@@ -47,7 +47,9 @@ constexpr int kMaxKb = 1024;
 // SK: 1 = every scale is loaded per K block into the stage; otherwise A's row scales (and
 //     B's, when they are row scales applied by the MFMA: SK = 4) come SK K blocks at a time
 //     through the ring, and K / 128 must be a multiple of SK.
-template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, int kScale, int SK>
+// kGroup: the grouped (MoE) form; each workgroup resolves its expert, row range and the
+//     expert's B and sB from the device offsets (see below); everything else is shared.
+template <int BM, int BN, int WM, int WN, bool kRowB, bool kF32, int kScale, int SK, bool kGroup = false>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -85,16 +87,78 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   const int wn0 = (wave / WM) * TN;
 
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  constexpr int GM = 8;
-  const int group = L / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int in_group = L - group * GM * tiles_n;
-  const int64_t m0 = (int64_t)(first_m + in_group % gsz) * BM;
-  const int64_t n0 = (int64_t)(in_group / gsz) * BN;
+  int64_t m0, n0, m_end;                 // tile origin; A rows of this tile end before m_end
+  const uint8_t* Bp = p.B;
+  const float* sBp = p.sB;
+  if constexpr (kGroup) {
+    // Expert e owns ceil(count_e / BM) m-tiles. A wave-level prefix sum over the experts
+    // (64 per step) gives the total, then the expert owning m-tile mt. Offsets are clamped
+    // into [0, M] and a decreasing step is an empty expert, so no access leaves the
+    // buffers whatever they hold. Only the real tiles are mapped (XCD-aware, n fastest, so
+    // an XCD's concurrent tiles share A rows and the expert's B); the grid's spare
+    // workgroups exit here.
+    auto rows_of = [&](int64_t e, int64_t& beg) __attribute__((always_inline)) -> int64_t {
+      const int64_t a = min(max((int64_t)p.offsets[e], (int64_t)0), M);
+      const int64_t b = min(max((int64_t)p.offsets[e + 1], (int64_t)0), M);
+      beg = a;
+      return b > a ? b - a : 0;
+    };
+    int64_t total = 0;
+    for (int64_t c0 = 0; c0 < p.E; c0 += 64) {
+      int64_t beg, t = 0;
+      if (c0 + lane < p.E) t = (rows_of(c0 + lane, beg) + BM - 1) / BM;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+      total += t;
+    }
+    // Offsets that do not partition [0, M] can give more tiles than the grid holds: only the
+    // first gridDim.x of them are computed, and every index stays in range.
+    const int64_t G = min(total * tiles_n, (int64_t)gridDim.x);
+    if ((int64_t)blockIdx.x >= G) return;   // uniform across the workgroup
+    const int L = xcd_remap(blockIdx.x, (int)G);
+    const int64_t mt = L / tiles_n;
+    n0 = (int64_t)(L % tiles_n) * BN;
+    int64_t base = 0, expert = -1, row_beg = 0, row_cnt = 0;
+    m0 = 0;
+    for (int64_t c0 = 0; c0 < p.E && expert < 0; c0 += 64) {
+      const int64_t e = c0 + lane;
+      int64_t beg = 0, cnt = 0;
+      if (e < p.E) cnt = rows_of(e, beg);
+      const int64_t tiles = (cnt + BM - 1) / BM;
+      int64_t incl = tiles;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      const int64_t excl = incl - tiles;
+      const uint64_t hit = __ballot(e < p.E && mt >= base + excl && mt < base + incl);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        expert = c0 + src;
+        row_beg = __shfl(beg, src);
+        row_cnt = __shfl(cnt, src);
+        m0 = row_beg + (mt - base - __shfl(excl, src)) * BM;
+      }
+      base += __shfl(incl, 63);
+    }
+    if (expert < 0) return;                 // not reached for mt < total; uniform
+    m_end = row_beg + row_cnt;
+    Bp += expert * p.b_stride;
+    sBp += expert * p.sb_stride;
+  } else {
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    constexpr int GM = 8;
+    const int group = L / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int in_group = L - group * GM * tiles_n;
+    m0 = (int64_t)(first_m + in_group % gsz) * BM;
+    n0 = (int64_t)(in_group / gsz) * BN;
+    m_end = M;
+  }
   const int nkb = (int)(K / 128);
   const int64_t nb0 = n0 >> 7;                                  // first 128-row B block of the tile
   const int64_t nbl = (N - 1) >> 7;                             // last B block
@@ -108,7 +172,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   // it * (NT/8) * K bytes, and NT/8 is a multiple of 16, so the row swizzle phase
   // ((r >> 1) & 7) is the same for every load.
   static_assert((NT / 8) % 16 == 0, "swizzle phase must repeat across loads");
-  const int64_t rows_a = min((int64_t)BM, M - m0), rows_b = min((int64_t)BN, N - n0);
+  const int64_t rows_a = min((int64_t)BM, m_end - m0), rows_b = min((int64_t)BN, N - n0);
   const int lr = tid >> 3;
   const uint32_t off0 = (uint32_t)(lr * K) + (uint32_t)(swz(lr, tid & 7) << 4);
   const uint32_t bytesA = (uint32_t)((rows_a - 1) * K + 128), bytesB = (uint32_t)((rows_b - 1) * K + 128);
@@ -127,7 +191,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   const int cidx = wave * 64 + lane;
   const int crow = cidx / LPR;
   const bool c_a = crow < BM;                                    // wave-uniform
-  const float* cbase = c_a ? p.sA + m0 * p.sa_ld : p.sB + n0 * p.sb_ld_n;
+  const float* cbase = c_a ? p.sA + m0 * p.sa_ld : sBp + n0 * p.sb_ld_n;
   const int64_t cld = c_a ? p.sa_ld : p.sb_ld_n;
   const uint32_t coff = (uint32_t)(((c_a ? crow : crow - BM) * cld + (cidx % LPR) * 4) * 4);
   // Rows past the tile's last valid row read as zero; nkb % SK == 0 keeps every load of a
@@ -143,12 +207,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     bytesS = (uint32_t)((rows_a - 1) * p.sa_ld * 4 + 4);
     sstep = 1;
   } else if (kRowB) {
-    baseS = p.sB + n0 * p.sb_ld_n;
+    baseS = sBp + n0 * p.sb_ld_n;
     offS = (uint32_t)(((wave - BM / 64) * 64 + lane) * p.sb_ld_n * 4);
     bytesS = sb_wave ? (uint32_t)((rows_b - 1) * p.sb_ld_n * 4 + 4) : 0u;
     sstep = 1;
   } else {
-    baseS = p.sB + nb0 * p.sb_ld_n;
+    baseS = sBp + nb0 * p.sb_ld_n;
     offS = (uint32_t)(lane * p.sb_ld_n * 4);
     bytesS = sb_wave ? (uint32_t)((nbl - nb0) * p.sb_ld_n * 4 + 4) : 0u;
     sstep = p.sb_ld_k;
@@ -166,7 +230,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
       dma16(make_rsrc(p.A + m0 * K + kbc * 128, live ? bytesA : 0u), off0 + (uint32_t)(part * (NT / 8)) * (uint32_t)K,
             st + (part * NT + wave * 64) * 16);
     } else {
-      dma16(make_rsrc(p.B + n0 * K + kbc * 128, live ? bytesB : 0u), off0 + (uint32_t)((part - LA) * (NT / 8)) * (uint32_t)K,
+      dma16(make_rsrc(Bp + n0 * K + kbc * 128, live ? bytesB : 0u), off0 + (uint32_t)((part - LA) * (NT / 8)) * (uint32_t)K,
             st + OFF_B + ((part - LA) * NT + wave * 64) * 16);
     }
   };
@@ -369,7 +433,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     // end of B read as zero or as other scales of B (never used). Entries past 2 * nkb read
     // as zero. The K loop's first wait and barrier cover these copies.
     const int ne = 2 * nkb;
-    const v4i rs = make_rsrc(p.sB + nb0 * p.sb_ld_n,
+    const v4i rs = make_rsrc(sBp + nb0 * p.sb_ld_n,
                              (uint32_t)(((nbl - nb0) * p.sb_ld_n + (int64_t)(nkb - 1) * p.sb_ld_k + 1) * 4));
     for (int e0 = 0; e0 < ne; e0 += NT) {
       const int e = e0 + wave * 64 + lane;
@@ -429,7 +493,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
         const int r = r0 + cr;
         const int64_t m = m0 + q * TM + r;
         float4 v = *reinterpret_cast<const float4*>(buf + r * ROWF + cc * 16);
-        if (m < M && n < N) {
+        if (m < m_end && n < N) {
           float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + m * p.ldc + n);
           if (p.accumulate) {
             const float4 o = *dst;
@@ -471,19 +535,18 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
       const int r = r0 + cr;
       const int64_t m = m0 + r;
       const uint4 v = *reinterpret_cast<const uint4*>((r < HALF ? sm0 : sm1) + (r % HALF) * ROW + cc * 16);
-      if (m < M && n < N) *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n) = v;
+      if (m < m_end && n < N) *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n) = v;
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool kRowB, int kScale, int SK>
-static hipError_t launch_sk(const GemmParams& p, bool f32, hipStream_t stream) {
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+template <int BM, int BN, int WM, int WN, bool kRowB, int kScale, int SK, bool kGroup = false>
+static hipError_t launch_sk(const GemmParams& p, bool f32, int64_t tiles, hipStream_t stream) {
   const dim3 grid((unsigned)tiles), block(WM * WN * 64);
   if (f32)
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kScale, SK>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, true, kScale, SK, kGroup>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kScale, SK>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_blockscaled<BM, BN, WM, WN, kRowB, false, kScale, SK, kGroup>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -491,9 +554,11 @@ static hipError_t launch_sk(const GemmParams& p, bool f32, hipStream_t stream) {
 template <int BM, int BN, int WM, int WN, bool kRowB, int kScale>
 static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) {
   constexpr int SK = kRowB ? 4 : 8;
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if constexpr (BM == 256)
-    if ((p.K / 128) % SK == 0 && p.K / 128 <= kMaxKb) return launch_sk<BM, BN, WM, WN, kRowB, kScale, SK>(p, f32, stream);
-  return launch_sk<BM, BN, WM, WN, kRowB, kScale, 1>(p, f32, stream);
+    if ((p.K / 128) % SK == 0 && p.K / 128 <= kMaxKb)
+      return launch_sk<BM, BN, WM, WN, kRowB, kScale, SK>(p, f32, tiles, stream);
+  return launch_sk<BM, BN, WM, WN, kRowB, kScale, 1>(p, f32, tiles, stream);
 }
 
 // Tile choice: at most 256 rows with block-scaled fp32 scales go to the few-row kernel (skinny.hip);
@@ -518,6 +583,35 @@ hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f
 hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream) {
   const bool big = ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
   return big ? launch_cfg<256, 256, 4, 2, true, 2>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, 2>(p, f32, stream);
+}
+
+// MXFP8 grouped GEMM (MoE): the MX kernel above with grouped tile resolution, 256x256 tiles
+// (measured faster than 128x128 / 128x256 / 256x128 tiles on the routed-MoE shapes even
+// though ragged experts leave more of their last m-tile empty). X rows are grouped by
+// expert; W and its E8M0 scales are [E][N][K] and [E][N][K/32]. The grid is an upper bound
+// on the tiles (sum_e ceil(c_e / 256) <= T / 256 + E for offsets that partition [0, T]);
+// its spare workgroups exit at once.
+hipError_t launch_grouped_mx(const GroupedParams& g, bool f32, hipStream_t stream) {
+  GemmParams p{};
+  p.A = g.X;
+  p.B = g.W;
+  p.sA = reinterpret_cast<const float*>(g.Xs);
+  p.sB = reinterpret_cast<const float*>(g.Ws);
+  p.C = g.Y;
+  p.M = g.T;
+  p.N = g.N;
+  p.K = g.K;
+  p.sa_ld = p.sb_ld_n = g.K / 128;   // dwords of 4 E8M0 bytes per row
+  p.sb_ld_k = 1;
+  p.ldc = g.N;
+  p.offsets = g.offsets;
+  p.E = g.E;
+  p.b_stride = g.N * g.K;
+  p.sb_stride = g.N * (g.K / 128);
+  const int64_t tiles = ((g.T + 255) / 256 + g.E) * ((g.N + 255) / 256);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if ((g.K / 128) % 4 == 0 && g.K / 128 <= kMaxKb) return launch_sk<256, 256, 4, 2, true, 2, 4, true>(p, f32, tiles, stream);
+  return launch_sk<256, 256, 4, 2, true, 2, 1, true>(p, f32, tiles, stream);
 }
 
 }  // namespace fp8rl

@@ -44,6 +44,11 @@ struct GemmParams {
   int64_t M, N, K;
   int64_t sa_ld, sb_ld_n, sb_ld_k, ldc;
   int accumulate;
+  // Grouped (MoE) form only: rows of A grouped by expert, expert e owning rows
+  // [offsets[e], offsets[e + 1]) of [0, M); B and sB advance by b_stride bytes and sb_stride
+  // dwords per expert.
+  const int32_t* offsets;
+  int64_t E, b_stride, sb_stride;
 };
 // pow2: every scale is a power of two (the pow2 quantizers' output); the scaled MFMA then
 // applies them (their fp32 exponent fields) and no rescale step is needed.

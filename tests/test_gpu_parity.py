@@ -230,7 +230,8 @@ def _routing(T_tokens, E, topk, seed):
     return perm, offsets
 
 
-@pytest.mark.parametrize("T_tokens,E,topk,N,K", [(200, 8, 2, 256, 256), (64, 16, 4, 128, 384), (300, 1, 1, 64, 128)])
+@pytest.mark.parametrize("T_tokens,E,topk,N,K", [(200, 8, 2, 256, 256), (64, 16, 4, 128, 384), (300, 1, 1, 64, 128),
+                                                 (256, 8, 4, 384, 1024)])
 def test_grouped_mx(T_tokens, E, topk, N, K):
     perm, offsets = _routing(T_tokens, E, topk, 9000 + E)
     x = _rand((T_tokens, K), 9001 + E)[perm]
