@@ -414,6 +414,8 @@ def moe_setup(torch, F, W, dev):
                   f"2*T*N*K = {fl_gu:.4g} FLOP per launch"),
         quant=("quant_x", T * K * (2 + 1 + 1 / 32) / 1e9, "bf16 read 2 B + E4M3 1 B + E8M0 1/32 B per element"),
         gemm_keys=("grouped_gu", "grouped_dn"),
+        # X_perm and the expert stack once (E4M3 + E8M0) and Y once (bf16)
+        algorithmic_gb=(T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + T * N * 2) / 1e9,
     )
     return step, timers, info
 
@@ -689,6 +691,14 @@ def main():
         out["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
                                  "per_launch": qdesc}
+    if "algorithmic_gb" in info:
+        # A GEMM whose arithmetic intensity sits below the ridge (flops per HBM byte under
+        # peak FLOP/s / peak B/s) cannot reach the MFMA peak: report the attainable rate too.
+        ai = info["dominant"][2] * 1e12 / (info["algorithmic_gb"] * 1e9)
+        attainable = min(peak, ai * PEAK_HBM_GBS / 1e3)
+        out["roofline"]["arithmetic_intensity"] = round(ai, 1)
+        out["roofline"]["attainable"] = round(attainable, 1)
+        out["roofline"]["frac_attainable"] = round(achieved / attainable, 4)
     if "extra" in info:
         out["unfused_kernel_us"] = info["extra"]()
     if not a.no_cpu_baseline and a.workload not in ("install", "fp8_param"):
