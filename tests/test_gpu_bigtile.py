@@ -61,6 +61,19 @@ def test_bigtile_blockscaled_forward(data, pow2):
     _check(y32, y16, OG.gemm_fwd(aq[ROWS], sa[ROWS], bq, sb), f"fwd pow2={pow2}")
 
 
+def test_bigtile_deterministic(data):
+    """Two launches of the ring-path kernel on the ragged big-tile shape give the same bits
+    (fixed K order, no atomics)."""
+    a, b, _ = data
+    aq, sa = OQ.quant_act_1x128(a)
+    bq, sb = OQ.quant_w_128x128(b)
+    args = (u8_dev(aq), f32_dev(sa), u8_dev(bq), f32_dev(sb))
+    y1 = F.fp8_gemm_blockscaled_fwd(*args, out_dtype=torch.float32)
+    y2 = F.fp8_gemm_blockscaled_fwd(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
 @pytest.mark.parametrize("pow2", [False, True])
 def test_bigtile_blockscaled_dgrad(data, pow2):
     a, _, wd = data

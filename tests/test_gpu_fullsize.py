@@ -70,6 +70,30 @@ def test_dense_forward_full_size(dense):
     assert_bytes_equal(_rows_of(sxt, cols), rst, "sxt columns")
 
 
+def test_dense_forward_pow2_full_size(dense):
+    """The gate/up layer with power-of-two block scales (the scaled MFMA applies them): the
+    pow2 quantizers' bytes and scales on sampled rows and weight blocks, and Y on those rows
+    against every column of the sampled weight blocks."""
+    d, t = dense
+    xq, sx, _, _ = F.fp8_quant_act_1x128_pow2(t["x"])
+    wq, sw, _ = F.fp8_quant_w_128x128_pow2(t["w_gu"])
+    y32 = F.fp8_gemm_blockscaled_pow2_fwd(xq, sx, wq, sw, out_dtype=torch.float32)
+    y16 = F.fp8_gemm_blockscaled_pow2_fwd(xq, sx, wq, sw, out_dtype=torch.bfloat16)
+    rows = _sample(d["x"].shape[0], 16, 11)
+    blocks = sorted(_sample(d["w_gu"].shape[0] // 128, 3, 12).tolist())
+    rxq, rsx = OQ.quant_act_1x128_pow2(d["x"][rows])
+    assert_bytes_equal(_rows_of(xq, rows), rxq, "pow2 xq rows")
+    assert_bytes_equal(_rows_of(sx, rows), rsx, "pow2 sx rows")
+    wrows = np.concatenate([np.arange(b * 128, (b + 1) * 128) for b in blocks])
+    rwq, rsw = OQ.quant_w_128x128_pow2(d["w_gu"][wrows])
+    assert_bytes_equal(_rows_of(wq, wrows), rwq, "pow2 wq blocks")
+    assert_bytes_equal(_rows_of(sw, np.array(blocks)), rsw, "pow2 sw blocks")
+    ref = OG.gemm_fwd(rxq, rsx, rwq, rsw)
+    assert_gemm_close(host(_rows_of(y32, rows))[:, wrows], ref, "pow2 gate/up f32")
+    torch.cuda.synchronize()
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
 def test_dense_down_projection_full_size(dense):
     d, t = dense
     x2q, sx2, _, _ = F.fp8_quant_act_1x128(t["x2"])
