@@ -274,7 +274,8 @@ fp8rl_status fp8_gemm_mxfp8_wgrad(const uint8_t* dyqt, const uint8_t* edyt, cons
  *   offsets: DEVICE int32 [E+1], expected 0 = offsets[0] <= ... <= offsets[E] = T. The
  *   kernel clamps every offset into [0, T] and treats a decreasing step as an empty
  *   expert, so malformed offsets never cause an out-of-bounds access; rows not covered by
- *   any expert are left unwritten.
+ *   any expert are left unwritten. If clamped ranges overlap, the experts' 256-row tiles
+ *   can outnumber the T/256 + E the launch provides for; the tiles past that are skipped.
  *   y: [T][N], bf16 or fp32.
  * Rules: K % 128 == 0, N % 16 == 0, E >= 1. FP8RL_RECIPE_BLOCK128 -> FP8RL_ERR_RECIPE. */
 fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx,
