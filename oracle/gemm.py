@@ -23,12 +23,15 @@ below any tolerance used against the GPU.
                              i.e. the transposed copy Wt [K][N] with 1x32 groups;
     WGrad    dW = dY^T . X   both 32x1 along the tokens: dYt [N][M], Xt [K][M].
 * grouped   per expert e, rows [off[e], off[e+1]) of the routed activations
-  times expert e's weight, MXFP8 1x32 scales on both operands
-  ([SkyRL-FP8] MoE experts hold most parameters; MXFP8 recipe).
+  times expert e's weight ([SkyRL-FP8] MoE experts hold most parameters), in either
+  recipe: MXFP8 1x32 scales on both operands, or the blockwise recipe (activation
+  rows in 1x128 groups, each expert's weight in 128x128 blocks, as for the dense
+  forward).
 
 Pinned by tests/test_oracle_gemm.py: an exact-rational (fractions.Fraction)
 triple loop on small non-square shapes with per-element scale lookup; the
-grouped GEMM equals the dense GEMM per expert and for a single expert; the MXFP8 dense
+grouped GEMMs (both recipes) equal the dense GEMM per expert and for a single expert, and
+the blockwise one also matches the exact-rational loop; the MXFP8 dense
 GEMMs by the same exact-rational loop with E8M0 scales looked up per 32-element block.
 """
 
@@ -94,6 +97,14 @@ def gemm_mx_wgrad(dyqt, edyt, xqt, ext) -> np.ndarray:
     return dequant_mx(dyqt, edyt) @ dequant_mx(xqt, ext).T
 
 
+def _expert_rows(offsets, E, T):
+    """Row ranges [lo, hi) of the E experts; offsets must run from 0 to T, non-decreasing."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    if offsets.shape != (E + 1,) or offsets[0] != 0 or offsets[-1] != T or np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must be non-decreasing from 0 to T with E+1 entries")
+    return [(int(offsets[e]), int(offsets[e + 1])) for e in range(E)]
+
+
 def grouped_gemm_mx(xq, ex, wq, ew, offsets) -> np.ndarray:
     """MXFP8 grouped GEMM.
 
@@ -102,15 +113,29 @@ def grouped_gemm_mx(xq, ex, wq, ew, offsets) -> np.ndarray:
     offsets[E+1]: rows of expert e are offsets[e] .. offsets[e+1]-1.
     Returns Y[T][N] (fp64).
     """
-    offsets = np.asarray(offsets, dtype=np.int64)
     wq = np.asarray(wq)
     E, N, _ = wq.shape
     T = np.asarray(xq).shape[0]
-    if offsets.shape != (E + 1,) or offsets[0] != 0 or offsets[-1] != T or np.any(np.diff(offsets) < 0):
-        raise ValueError("offsets must be non-decreasing from 0 to T with E+1 entries")
     y = np.zeros((T, N), dtype=np.float64)
-    for e in range(E):
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
+    for e, (lo, hi) in enumerate(_expert_rows(offsets, E, T)):
         if hi > lo:
             y[lo:hi] = dequant_mx(xq[lo:hi], ex[lo:hi]) @ dequant_mx(wq[e], ew[e]).T
+    return y
+
+
+def grouped_gemm_block(xq, sx, wq, sw, offsets) -> np.ndarray:
+    """Blockwise grouped GEMM.
+
+    xq[T][K], sx[T][K/128]: routed rows in 1x128 groups, grouped by expert;
+    wq[E][N][K], sw[E][N/128][K/128]: per-expert weights in 128x128 blocks;
+    offsets[E+1]: rows of expert e are offsets[e] .. offsets[e+1]-1.
+    Returns Y[T][N] (fp64).
+    """
+    wq = np.asarray(wq)
+    E, N, _ = wq.shape
+    T = np.asarray(xq).shape[0]
+    y = np.zeros((T, N), dtype=np.float64)
+    for e, (lo, hi) in enumerate(_expert_rows(offsets, E, T)):
+        if hi > lo:
+            y[lo:hi] = dequant_1x128(xq[lo:hi], sx[lo:hi]) @ dequant_128x128(wq[e], sw[e]).T
     return y

@@ -115,6 +115,40 @@ def test_grouped_equals_dense_per_expert_and_single_expert():
         G.grouped_gemm_mx(xq, ex, wq, ew, np.array([0, 10, 5, 33, 40], np.int32))
 
 
+def test_grouped_block_exact_rational():
+    """Blockwise grouped GEMM against the exact-rational loop: expert e's 128x128 weight
+    block scale is looked up as sw[e][n // 128][k // 128], the row scale as sx[t][k // 128]."""
+    rng = np.random.default_rng(36)
+    T, E, N, K = 6, 3, 256, 256
+    xq, sx = _codes(rng, (T, K)), _scales(rng, (T, K // 128))
+    wq, sw = _codes(rng, (E, N, K)), _scales(rng, (E, N // 128, K // 128))
+    offsets = np.array([0, 2, 2, 6], np.int32)          # expert 1 is empty
+    y = G.grouped_gemm_block(xq, sx, wq, sw, offsets)
+    expert = [0, 0, 2, 2, 2, 2]
+
+    def term(t, n, k):
+        e = expert[t]
+        return (_DEC_FR[xq[t, k]] * Fraction(float(sx[t, k // 128]))
+                * _DEC_FR[wq[e, n, k]] * Fraction(float(sw[e, n // 128, k // 128])))
+    _check([(0, 0), (1, 200), (2, 127), (3, 128), (5, 255), (4, 7)], term, y, K)
+
+
+def test_grouped_block_equals_dense_per_expert_and_single_expert():
+    rng = np.random.default_rng(37)
+    T, E, N, K = 40, 4, 256, 384
+    xq, sx = _codes(rng, (T, K)), _scales(rng, (T, K // 128))
+    wq, sw = _codes(rng, (E, N, K)), _scales(rng, (E, N // 128, K // 128))
+    offsets = np.array([0, 10, 10, 33, 40], np.int32)
+    y = G.grouped_gemm_block(xq, sx, wq, sw, offsets)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        assert np.array_equal(y[lo:hi], G.gemm_fwd(xq[lo:hi], sx[lo:hi], wq[e], sw[e]))
+    y1 = G.grouped_gemm_block(xq, sx, wq[:1], sw[:1], np.array([0, T], np.int32))
+    assert np.array_equal(y1, G.gemm_fwd(xq, sx, wq[0], sw[0]))
+    with pytest.raises(ValueError):
+        G.grouped_gemm_block(xq, sx, wq, sw, np.array([0, 10, 33, 40], np.int32))
+
+
 def test_unit_scale_reduces_to_plain_product_of_codes():
     """With every scale 1.0 the block-scaled GEMM is the plain product of decoded
     codes, here computed by torch in float64 from torch-decoded values."""
