@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|install|producers|mx_dense|fp8_param] [--no-cpu-baseline]
+                    [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|moe_block128|install|producers|mx_dense|fp8_param] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
 HBM. The default workload is the dense layer shaped like a ~9B model's MLP
@@ -18,7 +18,7 @@ peak; `quant_roofline` the X quantizer against 8 TB/s HBM.
 
 Other workloads (--workload) time the decode, backward, MoE and weight-install paths the
 same way; dense_pow2 and backward_pow2 run the dense layer with power-of-two block scales,
-which the scaled MFMA applies itself. HBM-bound workloads (decode, install) cycle through copies of their inputs that
+which the scaled MFMA applies itself; moe_block128 runs the MoE layer in the blockwise recipe. HBM-bound workloads (decode, install) cycle through copies of their inputs that
 together exceed 1 GiB, so the 256 MB last-level cache cannot serve a launch from the previous
 one. `roofline.traffic` is the dominant kernel's HBM bytes per launch from rocprofv3
 FETCH_SIZE + WRITE_SIZE counter runs (scaled by what the same counters read for the install
@@ -85,6 +85,7 @@ KERNEL_SOURCES = {
     "mx_fwd": ("gemm.hip", "device.hpp"),
     "decode_n24576": ("skinny.hip", "device.hpp"),
     "grouped_gu": ("gemm.hip", "device.hpp"),
+    "grouped_gu_block": ("gemm.hip", "device.hpp"),
     "install_gu": ("install.hip", "device.hpp"),
     "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp"),
     "requant_gu": ("fp8_param.hip", "device.hpp"),
@@ -106,7 +107,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense", choices=["dense", "dense_pow2", "decode", "backward", "backward_pow2", "moe",
-                                                         "install", "producers", "mx_dense", "fp8_param"])
+                                                         "moe_block128", "install", "producers", "mx_dense", "fp8_param"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -420,6 +421,56 @@ def moe_setup(torch, F, W, dev):
     return step, timers, info
 
 
+def moe_block128_setup(torch, F, W, dev):
+    """The MoE layer of the MXFP8 workload (same routed rows, experts and weights) in the
+    blockwise recipe: activations in 1x128 groups, each expert's weights in 128x128 blocks."""
+    d = W.moe_mxfp8()
+    xp = W.to_bf16_tensor(d["x_perm"]).to(dev)
+    h = W.to_bf16_tensor(d["h"]).to(dev)
+    E, N, K = d["w_gu"].shape
+    _, N2, K2 = d["w_dn"].shape
+    wq_gu, sw_gu, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d["w_gu"].reshape(E * N, K)).to(dev))
+    wq_dn, sw_dn, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d["w_dn"].reshape(E * N2, K2)).to(dev))
+    wq_gu, sw_gu = wq_gu.view(E, N, K), sw_gu.view(E, N // 128, K // 128)
+    wq_dn, sw_dn = wq_dn.view(E, N2, K2), sw_dn.view(E, N2 // 128, K2 // 128)
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    T = xp.shape[0]
+    u8, f32 = torch.uint8, torch.float32
+    b = dict(xq=torch.empty((T, K), dtype=u8, device=dev), sx=torch.empty((T, K // 128), dtype=f32, device=dev),
+             hq=torch.empty((T, K2), dtype=u8, device=dev), sh=torch.empty((T, K2 // 128), dtype=f32, device=dev),
+             y_gu=torch.empty((T, N), dtype=torch.bfloat16, device=dev),
+             y_dn=torch.empty((T, N2), dtype=torch.bfloat16, device=dev))
+    timers = {k: EventTimer(torch) for k in ("quant_x", "grouped_gu", "quant_h", "grouped_dn")}
+    blk = F.RECIPE_BLOCK128
+
+    def step(timed):
+        if timed: timers["quant_x"].start()
+        F.fp8_quant_act_1x128(xp, q=b["xq"], s=b["sx"])
+        if timed: timers["quant_x"].stop(); timers["grouped_gu"].start()
+        F.fp8_grouped_gemm(b["xq"], b["sx"], wq_gu, sw_gu, off, recipe=blk, y=b["y_gu"])
+        if timed: timers["grouped_gu"].stop(); timers["quant_h"].start()
+        F.fp8_quant_act_1x128(h, q=b["hq"], s=b["sh"])
+        if timed: timers["quant_h"].stop(); timers["grouped_dn"].start()
+        F.fp8_grouped_gemm(b["hq"], b["sh"], wq_dn, sw_dn, off, recipe=blk, y=b["y_dn"])
+        if timed: timers["grouped_dn"].stop()
+
+    fl_gu, fl_dn = 2.0 * T * N * K, 2.0 * T * N2 * K2
+    info = dict(
+        config={"workload": "moe_block128_grouped", "routed_rows_T": T, "experts": E, "gate_up": [N, K],
+                "down": [N2, K2], "routing": "Zipf(1.1) top-8"},
+        flops=fl_gu + fl_dn,
+        dominant=("grouped_gu", "mfma", fl_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
+                  f"2*T*N*K = {fl_gu:.4g} FLOP per launch"),
+        quant=("quant_x", T * K * (2 + 1 + 4 / 128) / 1e9, "bf16 read 2 B + E4M3 1 B + fp32 scale 4/128 B per element"),
+        gemm_keys=("grouped_gu", "grouped_dn"),
+        # X_perm once (E4M3 + fp32 1x128 scales), the expert stack once (E4M3 + fp32 128x128
+        # block scales) and Y once (bf16)
+        algorithmic_gb=(T * K * (1 + 4 / 128) + E * N * K * (1 + 4 / 128 ** 2) + T * N * 2) / 1e9,
+        traffic_key="grouped_gu_block",
+    )
+    return step, timers, info
+
+
 def install_setup(torch, F, W, dev):
     """Weight install of the dense layer's gate/up and down weights (payload + fp32 block scales),
     the rollout side's whole per-sync work for that layer. A plain copy of known size, so its
@@ -604,6 +655,16 @@ def cpu_baseline(workload: str, budget_s: float = 12.0):
             wq, ew = OQ.quant_mx_1x32(w)
             OG.grouped_gemm_mx(xq, ex, wq[None], ew[None], np.array([0, m], np.int64))
         what = f"oracle MXFP8 quantization of both operands + fp64 dequantized GEMM, {m}x{n}x{k} (one expert)"
+    elif workload == "moe_block128":
+        m, n, k = 512, 1024, 2048
+        x = W.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        w = W.bf16_round(rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02))
+
+        def chunk():
+            xq, sx = OQ.quant_act_1x128(x)
+            wq, sw = OQ.quant_w_128x128(w)
+            OG.grouped_gemm_block(xq, sx, wq[None], sw[None], np.array([0, m], np.int64))
+        what = f"oracle 1x128 / 128x128 quantization + fp64 dequantized GEMM, {m}x{n}x{k} (one expert)"
     else:
         # 256 token rows x 2048 output features of the dense gate/up projection, K = 4096
         m, n, k = 256, 2048, 4096
@@ -639,7 +700,7 @@ def main():
     dev = torch.device("cuda", 0)
     F.load_library()
     setup = {"dense": dense_setup, "dense_pow2": lambda *args: dense_setup(*args, pow2=True), "decode": decode_setup,
-             "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup,
+             "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup, "moe_block128": moe_block128_setup,
              "install": install_setup, "producers": producers_setup, "mx_dense": mx_dense_setup,
              "fp8_param": fp8_param_setup}[a.workload]
     step, timers, info = setup(torch, F, W, dev)

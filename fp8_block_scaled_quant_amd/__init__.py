@@ -475,15 +475,20 @@ def _wgrad(entry, dyqt, sdyt, xqt, sxt, dw, accumulate):
 
 
 def fp8_grouped_gemm(xq, sx, wq, sw, offsets, *, recipe=RECIPE_MXFP8, out_dtype=torch.bfloat16, y=None):
-    """MXFP8 grouped GEMM: xq [T][K] u8, sx [T][K/32] u8, wq [E][N][K] u8, sw [E][N][K/32] u8,
-    offsets int32 [E+1] on the GPU. Returns y [T][N]."""
+    """Grouped GEMM, offsets int32 [E+1] on the GPU. Returns y [T][N].
+    RECIPE_MXFP8:    xq [T][K] u8, sx [T][K/32] u8, wq [E][N][K] u8, sw [E][N][K/32] u8.
+    RECIPE_BLOCK128: xq [T][K] u8, sx [T][K/128] f32, wq [E][N][K] u8, sw [E][N/128][K/128] f32."""
     lib = load_library()
     T, K = xq.shape
     E, N, _ = wq.shape
     _need(xq, torch.uint8, (T, K), "xq")
-    _need(sx, torch.uint8, (T, K // 32), "sx")
     _need(wq, torch.uint8, (E, N, K), "wq")
-    _need(sw, torch.uint8, (E, N, K // 32), "sw")
+    if recipe == RECIPE_BLOCK128:
+        _need(sx, torch.float32, (T, K // 128), "sx")
+        _need(sw, torch.float32, (E, N // 128, K // 128), "sw")
+    else:
+        _need(sx, torch.uint8, (T, K // 32), "sx")
+        _need(sw, torch.uint8, (E, N, K // 32), "sw")
     _need(offsets, torch.int32, (E + 1,), "offsets")
     y = _out(y, out_dtype, (T, N), xq.device, "y")
     _check(lib.fp8_grouped_gemm(recipe, _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(offsets), T, E, N, K, _ptr(y),

@@ -456,7 +456,7 @@ fp8rl_status fp8_gemm_mxfp8_wgrad(const uint8_t* dyqt, const uint8_t* edyt, cons
 fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, const uint8_t* wq, const void* sw,
                               const int32_t* offsets, int64_t T, int64_t E, int64_t N, int64_t K, void* y,
                               int y_dtype, void* stream) {
-  if (recipe != FP8RL_RECIPE_MXFP8) return FP8RL_ERR_RECIPE;
+  if (recipe != FP8RL_RECIPE_MXFP8 && recipe != FP8RL_RECIPE_BLOCK128) return FP8RL_ERR_RECIPE;
   if (y_dtype != FP8RL_OUT_BF16 && y_dtype != FP8RL_OUT_F32) return FP8RL_ERR_RECIPE;
   if (xq == nullptr || sx == nullptr || wq == nullptr || sw == nullptr || offsets == nullptr || y == nullptr)
     return FP8RL_ERR_NULL;
@@ -465,6 +465,7 @@ fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, con
   if (fp8rl_status e = check_dims(E * N, K)) return e;
   if (fp8rl_status e = check_dims(T, N)) return e;
   if (K % 128 != 0 || N % 16 != 0 || E > ((int64_t)1 << 24)) return FP8RL_ERR_SHAPE;
+  if (recipe == FP8RL_RECIPE_BLOCK128 && N % 128 != 0) return FP8RL_ERR_SHAPE;   // whole 128-row weight blocks
   if (T == 0 || N == 0) return FP8RL_OK;
   if (K == 0) return FP8RL_ERR_SHAPE;
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(sx, 4) || !aligned(sw, 4) ||
@@ -482,7 +483,9 @@ fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, con
   p.E = E;
   p.N = N;
   p.K = K;
-  return launched(launch_grouped_mx(p, y_dtype == FP8RL_OUT_F32, as_stream(stream)));
+  const bool f32 = y_dtype == FP8RL_OUT_F32;
+  return launched(recipe == FP8RL_RECIPE_MXFP8 ? launch_grouped_mx(p, f32, as_stream(stream))
+                                               : launch_grouped_block(p, f32, as_stream(stream)));
 }
 
 fp8rl_status fp8_weight_install(const fp8rl_weight* src, const fp8rl_weight* dst, void* stream) {

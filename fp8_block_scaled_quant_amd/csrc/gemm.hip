@@ -585,13 +585,13 @@ hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream) {
   return big ? launch_cfg<256, 256, 4, 2, true, 2>(p, f32, stream) : launch_cfg<128, 128, 2, 2, true, 2>(p, f32, stream);
 }
 
-// MXFP8 grouped GEMM (MoE): the MX kernel above with grouped tile resolution, 256x256 tiles
+// Grouped GEMMs (MoE): the kernels above with grouped tile resolution, 256x256 tiles
 // (measured faster than 128x128 / 128x256 / 256x128 tiles on the routed-MoE shapes even
 // though ragged experts leave more of their last m-tile empty). X rows are grouped by
-// expert; W and its E8M0 scales are [E][N][K] and [E][N][K/32]. The grid is an upper bound
+// expert; W is [E][N][K]. The grid is an upper bound
 // on the tiles (sum_e ceil(c_e / 256) <= T / 256 + E for offsets that partition [0, T]);
 // its spare workgroups exit at once.
-hipError_t launch_grouped_mx(const GroupedParams& g, bool f32, hipStream_t stream) {
+static GemmParams grouped_params(const GroupedParams& g) {
   GemmParams p{};
   p.A = g.X;
   p.B = g.W;
@@ -601,17 +601,37 @@ hipError_t launch_grouped_mx(const GroupedParams& g, bool f32, hipStream_t strea
   p.M = g.T;
   p.N = g.N;
   p.K = g.K;
-  p.sa_ld = p.sb_ld_n = g.K / 128;   // dwords of 4 E8M0 bytes per row
+  p.sa_ld = p.sb_ld_n = g.K / 128;   // MXFP8: dwords of 4 E8M0 bytes per row; blockwise: K blocks
   p.sb_ld_k = 1;
   p.ldc = g.N;
   p.offsets = g.offsets;
   p.E = g.E;
   p.b_stride = g.N * g.K;
+  return p;
+}
+
+static int64_t grouped_tiles(const GroupedParams& g) { return ((g.T + 255) / 256 + g.E) * ((g.N + 255) / 256); }
+
+hipError_t launch_grouped_mx(const GroupedParams& g, bool f32, hipStream_t stream) {
+  GemmParams p = grouped_params(g);
   p.sb_stride = g.N * (g.K / 128);
-  const int64_t tiles = ((g.T + 255) / 256 + g.E) * ((g.N + 255) / 256);
+  const int64_t tiles = grouped_tiles(g);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   if ((g.K / 128) % 4 == 0 && g.K / 128 <= kMaxKb) return launch_sk<256, 256, 4, 2, true, 2, 4, true>(p, f32, tiles, stream);
   return launch_sk<256, 256, 4, 2, true, 2, 1, true>(p, f32, tiles, stream);
+}
+
+// Blockwise grouped GEMM: the fp32-scale forward kernel (1x128 row scales of X through the
+// ring, the expert's 128x128 block scales preloaded per tile) with grouped tile resolution;
+// expert e's block scales start sb_stride = (N/128)(K/128) floats after expert e-1's.
+hipError_t launch_grouped_block(const GroupedParams& g, bool f32, hipStream_t stream) {
+  GemmParams p = grouped_params(g);
+  p.sb_stride = (g.N / 128) * (g.K / 128);
+  const int64_t tiles = grouped_tiles(g);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if ((g.K / 128) % 8 == 0 && g.K / 128 <= kMaxKb)
+    return launch_sk<256, 256, 4, 2, false, 0, 8, true>(p, f32, tiles, stream);
+  return launch_sk<256, 256, 4, 2, false, 0, 1, true>(p, f32, tiles, stream);
 }
 
 }  // namespace fp8rl

@@ -58,16 +58,19 @@ hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream);
 // Few-row form (M <= 256, block-scaled B only): all rows per workgroup, one workgroup per CU.
 hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream);
 
+// Scales: MXFP8 = E8M0 bytes Xs [T][K/32], Ws [E][N][K/32]; blockwise = fp32
+// Xs [T][K/128] (1x128 groups), Ws [E][N/128][K/128] (128x128 blocks per expert).
 struct GroupedParams {
   const uint8_t* X;     // [T][K]
-  const uint8_t* Xs;    // E8M0 [T][K/32]
+  const uint8_t* Xs;
   const uint8_t* W;     // [E][N][K]
-  const uint8_t* Ws;    // E8M0 [E][N][K/32]
+  const uint8_t* Ws;
   const int32_t* offsets;
   void* Y;              // [T][N]
   int64_t T, E, N, K;
 };
 hipError_t launch_grouped_mx(const GroupedParams& p, bool f32, hipStream_t stream);
+hipError_t launch_grouped_block(const GroupedParams& p, bool f32, hipStream_t stream);
 
 hipError_t launch_copy(const uint8_t* src_q, uint8_t* dst_q, int64_t qbytes, const uint8_t* src_s, uint8_t* dst_s,
                        int64_t sbytes, hipStream_t stream);

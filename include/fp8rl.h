@@ -266,18 +266,23 @@ fp8rl_status fp8_gemm_mxfp8_wgrad(const uint8_t* dyqt, const uint8_t* edyt, cons
                                   int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream);
 
 /* Grouped GEMM for mixture-of-experts ([SkyRL-FP8] MoE: routed experts hold most
- * parameters; MXFP8 recipe). Routed rows are grouped by expert; rows
- * offsets[e] .. offsets[e+1]-1 belong to expert e:
+ * parameters; MXFP8 recipe, or the blockwise recipe of the dense layers). Routed rows are
+ * grouped by expert; rows offsets[e] .. offsets[e+1]-1 belong to expert e:
  *   Y[t][n] = sum_k deq(X)[t][k] * deq(W[e])[n][k].
- *   recipe FP8RL_RECIPE_MXFP8: xq uint8 [T][K], sx = E8M0 uint8 [T][K/32],
- *                              wq uint8 [E][N][K], sw = E8M0 uint8 [E][N][K/32].
+ *   recipe FP8RL_RECIPE_MXFP8:    xq uint8 [T][K], sx = E8M0 uint8 [T][K/32],
+ *                                 wq uint8 [E][N][K], sw = E8M0 uint8 [E][N][K/32].
+ *   recipe FP8RL_RECIPE_BLOCK128: xq uint8 [T][K], sx = fp32 [T][K/128] (1x128 groups, as
+ *                                 from fp8_quant_act_1x128), wq uint8 [E][N][K],
+ *                                 sw = fp32 [E][N/128][K/128] (each expert's 128x128
+ *                                 blocks, as from fp8_quant_w_128x128 of its [N][K] slice).
  *   offsets: DEVICE int32 [E+1], expected 0 = offsets[0] <= ... <= offsets[E] = T. The
  *   kernel clamps every offset into [0, T] and treats a decreasing step as an empty
  *   expert, so malformed offsets never cause an out-of-bounds access; rows not covered by
  *   any expert are left unwritten. If clamped ranges overlap, the experts' 256-row tiles
  *   can outnumber the T/256 + E the launch provides for; the tiles past that are skipped.
  *   y: [T][N], bf16 or fp32.
- * Rules: K % 128 == 0, N % 16 == 0, E >= 1. FP8RL_RECIPE_BLOCK128 -> FP8RL_ERR_RECIPE. */
+ * Rules: K % 128 == 0, N % 16 == 0 (MXFP8) or N % 128 == 0 (BLOCK128), E >= 1; pointers
+ * 16-byte aligned (scales and offsets 4-byte). Any other recipe -> FP8RL_ERR_RECIPE. */
 fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx,
                               const uint8_t* wq, const void* sw, const int32_t* offsets,
                               int64_t T, int64_t E, int64_t N, int64_t K,

@@ -190,7 +190,10 @@ def test_mx_dense_validation(lib):
 
 def test_grouped_validation(lib):
     g = lib.fp8_grouped_gemm
-    assert g(F.RECIPE_BLOCK128, P, P, P, P, P, 64, 2, 128, 128, P, 0, None) == ERR_RECIPE
+    assert g(7, P, P, P, P, P, 64, 2, 128, 128, P, 0, None) == ERR_RECIPE                # unknown recipe
+    assert g(F.RECIPE_BLOCK128, P, P, P, P, P, 64, 2, 144, 128, P, 0, None) == ERR_SHAPE  # N % 128 (blocks)
+    assert g(F.RECIPE_BLOCK128, P, P, P, P, P, 64, 2, 128, 128, P, 2, None) == ERR_RECIPE  # output dtype
+    assert g(F.RECIPE_BLOCK128, P, P, P, P, P, 0, 2, 128, 128, P, 0, None) == OK
     assert g(F.RECIPE_MXFP8, P, P, P, P, P, 64, 0, 128, 128, P, 0, None) == ERR_SHAPE
     assert g(F.RECIPE_MXFP8, P, P, P, P, P, 64, 2, 128, 96, P, 0, None) == ERR_SHAPE   # K % 128
     assert g(F.RECIPE_MXFP8, P, P, P, P, P, 64, 2, 120, 128, P, 0, None) == ERR_SHAPE  # N % 16

@@ -273,6 +273,44 @@ def test_grouped_mx_empty_experts_and_malformed_offsets():
     assert_gemm_close(got[60:], ref3, "grouped clamped expert 3")
 
 
+@pytest.mark.parametrize("T_tokens,E,topk,N,K", [(200, 8, 2, 256, 256), (64, 16, 4, 128, 384), (300, 1, 1, 128, 2048),
+                                                 (256, 8, 4, 384, 1024), (500, 4, 2, 640, 3072)])
+def test_grouped_block(T_tokens, E, topk, N, K):
+    """Blockwise grouped GEMM: 1x128 row scales (through the LDS ring when K / 128 is a
+    multiple of 8: K = 1024, 2048, 3072; per K block otherwise) and each expert's 128x128
+    block scales, on Zipf-routed ragged experts. Operands are the oracle's quantization."""
+    perm, offsets = _routing(T_tokens, E, topk, 9200 + E)
+    x = _rand((T_tokens, K), 9201 + E)[perm]
+    w = _rand((E, N, K), 9202 + E, 0.02)
+    rxq, rsx = OQ.quant_act_1x128(x)
+    rwq, rsw = OQ.quant_w_128x128(w.reshape(E * N, K))
+    rwq, rsw = rwq.reshape(E, N, K), rsw.reshape(E, N // 128, K // 128)
+    args = (u8_dev(rxq), f32_dev(rsx), u8_dev(rwq), f32_dev(rsw), torch.from_numpy(offsets).to(dev()))
+    y32 = F.fp8_grouped_gemm(*args, recipe=F.RECIPE_BLOCK128, out_dtype=torch.float32)
+    y16 = F.fp8_grouped_gemm(*args, recipe=F.RECIPE_BLOCK128, out_dtype=torch.bfloat16)
+    ref = OG.grouped_gemm_block(rxq, rsx, rwq, rsw, offsets)
+    assert_gemm_close(host(y32), ref, "grouped block f32")
+    assert_bf16_consistent(y16, y32, ref, "grouped block bf16")
+
+
+def test_grouped_block_empty_experts_and_gpu_quantizers():
+    """Empty experts, and operands from the library's own quantizers (whose bytes and scales
+    equal the oracle's): the weight stack [E][N][K] quantized as one [E*N][K] matrix gives
+    each expert's 128x128 blocks."""
+    E, N, K = 6, 256, 1024
+    x = _rand((100, K), 9300)
+    w = _rand((E, N, K), 9301, 0.02)
+    xq, sx, _, _ = F.fp8_quant_act_1x128(bf16_dev(x))
+    wq, sw, _ = F.fp8_quant_w_128x128(bf16_dev(w.reshape(E * N, K)))
+    good = np.array([0, 0, 40, 40, 41, 100, 100], np.int32)          # empty experts 0, 2, 5
+    y = F.fp8_grouped_gemm(xq, sx, wq.view(E, N, K), sw.view(E, N // 128, K // 128), torch.from_numpy(good).to(dev()),
+                           recipe=F.RECIPE_BLOCK128, out_dtype=torch.float32)
+    rxq, rsx = OQ.quant_act_1x128(x)
+    rwq, rsw = OQ.quant_w_128x128(w.reshape(E * N, K))
+    ref = OG.grouped_gemm_block(rxq, rsx, rwq.reshape(E, N, K), rsw.reshape(E, N // 128, K // 128), good)
+    assert_gemm_close(host(y), ref, "grouped block empty experts")
+
+
 # ------------------------------------------------------------------------------------- weight sync
 
 def test_install_bit_identity_and_naive_control():
