@@ -83,8 +83,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave % WM) * TM;
-  const int wn0 = (wave / WM) * TN;
+  // Wave grid position. The grouped form puts the wave rows across SIMDs (wave w runs on
+  // SIMD w % 4): wave row w / WN, so the two waves sharing a SIMD own rows TM * (w % 4 / WN)
+  // and 2 TM further. A wave whose rows all lie past the expert's last row skips its
+  // MFMAs, which then halves the SIMD time of an m-tile with at most 2 TM rows.
+  const int wmi = kGroup ? wave / WN : wave % WM;
+  const int wm0 = wmi * TM;
+  const int wn0 = (kGroup ? wave % WN : wave / WM) * TN;
 
   const int64_t M = p.M, N = p.N, K = p.K;
   const int tiles_n = (int)((N + BN - 1) / BN);
@@ -442,22 +447,24 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
       dma4(rs, off, sbk0 + (e0 + wave * 64) * 4);
     }
   }
+  // Grouped form: a wave with no rows of the expert computes nothing (wave-uniform).
+  const bool busy = !kGroup || m0 + wm0 < m_end;
   issue(0, st0);
   int kb = 0;
   for (; kb + 2 <= nkb; kb += 2) {
     wait_vmem();
     __syncthreads();
     issue(kb + 1, st1);
-    compute(st0, kb);
+    if (busy) compute(st0, kb);
     wait_vmem();
     __syncthreads();
     issue(kb + 2, st0);
-    compute(st1, kb + 1);
+    if (busy) compute(st1, kb + 1);
   }
   if (kb < nkb) {
     wait_vmem();
     __syncthreads();
-    compute(st0, kb);
+    if (busy) compute(st0, kb);
   }
 
   // Epilogue. The tile goes out through LDS (the stages are free after the K loop), so that
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_blockscaled(GemmParams p) 
     for (int q = 0; q < WM; ++q) {
       uint8_t* buf = (q & 1) ? sm1 : sm0;
       __syncthreads();                               // the stage is free (K loop / previous chunk)
-      if (wave % WM == q) {
+      if (wmi == q) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
           uint8_t* rowp = buf + (16 * j + (lane & 15)) * ROWF;

@@ -208,6 +208,48 @@ def test_moe_mxfp8_full_size():
                 assert np.all(np.abs(got - ref) <= 2e-3 * rms + half_ulp), f"{name} expert {e} outside tolerance"
 
 
+def test_moe_block128_full_size():
+    """The same MoE layer in the blockwise recipe (bench workload moe_block128): 1x128 row
+    groups of the routed rows, each expert's weights in 128x128 blocks (the [E][N][K] stack
+    quantized as one [E*N][K] matrix, as the benchmark does)."""
+    d = W.moe_mxfp8()
+    off = d["offsets"]
+    E, N, K = d["w_gu"].shape
+    _, N2, K2 = d["w_dn"].shape
+    xq, sx, _, _ = F.fp8_quant_act_1x128(W.to_bf16_tensor(d["x_perm"]).to(dev()))
+    hq, sh, _, _ = F.fp8_quant_act_1x128(W.to_bf16_tensor(d["h"]).to(dev()))
+    wq_gu, sw_gu, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d["w_gu"].reshape(E * N, K)).to(dev()))
+    wq_dn, sw_dn, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d["w_dn"].reshape(E * N2, K2)).to(dev()))
+    wq_gu, sw_gu = wq_gu.view(E, N, K), sw_gu.view(E, N // 128, K // 128)
+    wq_dn, sw_dn = wq_dn.view(E, N2, K2), sw_dn.view(E, N2 // 128, K2 // 128)
+    offd = torch.from_numpy(off).to(dev())
+    blk = F.RECIPE_BLOCK128
+    y_gu = F.fp8_grouped_gemm(xq, sx, wq_gu, sw_gu, offd, recipe=blk, out_dtype=torch.bfloat16)
+    y_dn = F.fp8_grouped_gemm(hq, sh, wq_dn, sw_dn, offd, recipe=blk, out_dtype=torch.float32)
+    counts = np.diff(off)
+    experts = sorted(set([int(np.argmax(counts)), int(np.argmin(counts))] + _sample(len(counts), 4, 12).tolist()))
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.array([lo, lo + 1, (lo + hi) // 2, hi - 2, hi - 1]).clip(lo, hi - 1))
+        for name, xin, q, s, wfull, wq, sw, y, f32 in (
+                ("gate/up", d["x_perm"], xq, sx, d["w_gu"], wq_gu, sw_gu, y_gu, False),
+                ("down", d["h"], hq, sh, d["w_dn"], wq_dn, sw_dn, y_dn, True)):
+            rq, rs = OQ.quant_act_1x128(xin[rows])
+            assert_bytes_equal(_rows_of(q, rows), rq, f"{name} xq rows expert {e}")
+            assert_bytes_equal(_rows_of(s, rows), rs, f"{name} sx rows expert {e}")
+            rwq, rws = OQ.quant_w_128x128(wfull[e])
+            assert_bytes_equal(wq[e], rwq, f"{name} wq expert {e}")
+            assert_bytes_equal(sw[e], rws, f"{name} sw expert {e}")
+            ref = OG.gemm_fwd(rq, rs, rwq, rws)
+            got = host(_rows_of(y, rows))
+            rms = float(np.sqrt(np.mean(ref ** 2)))
+            if f32:
+                assert_gemm_close(got, ref, f"{name} expert {e}", rms=rms)
+            else:
+                half_ulp = np.ldexp(1.0, np.frexp(np.abs(got.astype(np.float64)))[1] - 9)
+                assert np.all(np.abs(got - ref) <= 2e-3 * rms + half_ulp), f"{name} expert {e} outside tolerance"
+
+
 def test_producers_full_size():
     """Fused SwiGLU -> FP8 (GU 8192x24576, rows + cols) and RMSNorm -> FP8 (X 8192x4096, rows
     + cols) as the producers workload runs them; sampled rows (1x128 groups, r) and sampled
