@@ -56,13 +56,14 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "6ec90d2b6d95997e", "gb": 1.6399},         # read 1.2375 + write 0.4024
-    "gemm_gu_pow2": {"sha": "6ec90d2b6d95997e", "gb": 1.6398},    # read 1.2374 + write 0.4024
-    "dgrad": {"sha": "6ec90d2b6d95997e", "gb": 1.3184},           # read 1.2513 + write 0.0671
-    "dgrad_pow2": {"sha": "6ec90d2b6d95997e", "gb": 1.3187},      # read 1.2516 + write 0.0671
-    "mx_fwd": {"sha": "6ec90d2b6d95997e", "gb": 1.6506},          # read 1.2482 + write 0.4024
+    "gemm_gu": {"sha": "4789a809d81d8424", "gb": 1.6404},         # read 1.2381 + write 0.4024
+    "gemm_gu_pow2": {"sha": "4789a809d81d8424", "gb": 1.6403},    # read 1.2380 + write 0.4024
+    "dgrad": {"sha": "4789a809d81d8424", "gb": 1.3196},           # read 1.2526 + write 0.0671
+    "dgrad_pow2": {"sha": "4789a809d81d8424", "gb": 1.3199},      # read 1.2528 + write 0.0671
+    "mx_fwd": {"sha": "4789a809d81d8424", "gb": 1.6505},          # read 1.2481 + write 0.4024
     "decode_n24576": {"sha": "b2504669b2408216", "gb": 0.1221},   # read 0.1095 + write 0.0126 (GEMM launch)
-    "grouped_gu": {"sha": "6ec90d2b6d95997e", "gb": 0.3147},      # read 0.2476 + write 0.0671
+    "grouped_gu": {"sha": "4789a809d81d8424", "gb": 0.3148},      # read 0.2477 + write 0.0671
+    "grouped_gu_block": {"sha": "4789a809d81d8424", "gb": 0.3071},  # read 0.2400 + write 0.0671
     "install_gu": {"sha": "cd3091d8cf3cd067", "gb": 0.2014},      # read 0.1007 + write 0.1007
     "swiglu_fp8": {"sha": "f42bb3cf95940150", "gb": 0.6476},      # read 0.4034 + write 0.2442
     "requant_gu": {"sha": "09a215be0d891edd", "gb": 0.6040},      # read 0.4026 + write 0.2014
