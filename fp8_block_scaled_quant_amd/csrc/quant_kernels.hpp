@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(Src src, uint8_t* __re
 //   kG = 32 (with kPow2): MXFP8 mode. Row output = 1x32 groups, column output = 32x1
 //                   groups written transposed; the scales are E8M0 bytes (e + 127, the
 //                   exponent field of the power-of-two scale) [R][C/32] and [C][R/32].
-// Grid: blockIdx.x = rb * (C/128) + cb.
+// Grid: one workgroup per tile, (R/128) * (C/128) of them (tile order below).
 // Thread t owns the 4x8 sub-block rows 4*(t/16) .. +3, columns 8*(t%16) .. +7. Each wave
 // load instruction then reads 4 whole 256-byte row segments, and each row-output store
 // writes whole 128-byte lines. Row amax: max over the 16 lanes sharing a row.
@@ -123,7 +123,20 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid & 15, rg = tid >> 4;                               // rg: 0..31
   const int64_t ncb = C / 128;
-  const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
+  // Tile order: the hardware deals consecutive workgroups to the 8 XCDs in turn. When the
+  // column blocks split evenly, XCD x takes the column blocks [x w, (x+1) w), w = ncb / 8,
+  // row block by row block. The tiles in flight still cover a few whole block rows (the
+  // read stream keeps its locality), and each XCD's L2 sees fewer of the lines that
+  // several tiles' 4-byte scale stores share.
+  int64_t cb, rb;
+  if (ncb % 8 == 0) {
+    const int64_t w = ncb / 8, i = blockIdx.x >> 3;
+    cb = (int64_t)(blockIdx.x & 7) * w + i % w;
+    rb = i / w;
+  } else {
+    cb = blockIdx.x % ncb;
+    rb = blockIdx.x / ncb;
+  }
   const bool want_rows = q != nullptr, want_cols = qt != nullptr;
 
   typename Src::Raw raw[4];
