@@ -6,12 +6,18 @@
 //             * sum_{k in kb} A[m][k] * B[n][k]
 //
 // Design (gfx950):
-// * Every workgroup takes all M rows (up to 256, rows past M read as zero) and a contiguous
-//   run of F 16-row fragments of B, so a launch of N / (16 F) workgroups (256 for the
-//   decode shapes) puts one workgroup on every CU and streams each weight byte once.
-// * NW waves (4 in use); wave w owns A rows (256/NW) w .. (256/NW)(w+1)-1 against all F
-//   fragments of B. With 4 waves a wave reads 4 A and F B fragments from LDS per K block
-//   (about 80 KB per workgroup for F = 6) against 4 F MFMAs.
+// * Every workgroup takes MR of the rows (MR = 256, 128 or 64; rows past M read as zero)
+//   and a contiguous run of F 16-row fragments of B; the launch holds ceil(M / MR) row
+//   parts times N / (16 F) fragment runs, 256 workgroups for the decode shapes (one per
+//   CU). Every workgroup copies its MR x 128 slice of A from L2 per K block, and each
+//   fragment run is read by all row parts, so MR trades the replicated A reads (MR x 128
+//   bytes per CU per K block) against B's (16 F x 128): a 4096-column weight takes
+//   MR = 64, F = 4 (16 KB per CU per K block instead of 34 KB with MR = 256, F = 1). The
+//   row parts of one fragment run go to the same XCD, one after another, so B comes from
+//   HBM once and from that XCD's L2 after.
+// * NW waves (4 in use); wave w owns A rows (MR/NW) w .. (MR/NW)(w+1)-1 against all F
+//   fragments of B, i.e. reads MR/64 A and F B fragments from LDS per K block against
+//   F MR/64 MFMAs.
 // * Three LDS stages filled by direct global->LDS copies: the copies of K blocks kb+1 and
 //   kb+2 are in flight while kb is computed.
 // * Scales: one fp32 per A row per K block, and one per B fragment per K block (a 16-row
@@ -26,18 +32,17 @@ namespace fp8rl {
 
 namespace {
 
-constexpr int kSkinnyM = 256;   // rows per workgroup (all of M)
 constexpr int kSkinnyLag = 3;
 
-template <int F, int NW>
+template <int F, int NW, int MR>
 struct SkinnyShape {
   static constexpr int NT = NW * 64;
-  static constexpr int FM = kSkinnyM / (16 * NW);     // A fragments per wave
+  static constexpr int FM = MR / (16 * NW);           // A fragments per wave
   static constexpr int BN = 16 * F;
   static constexpr int CR = NT / 8;                   // rows per copy (8 lanes per 128-byte row)
-  static constexpr int LA = kSkinnyM / CR;            // A copies per thread
+  static constexpr int LA = MR / CR;                  // A copies per thread
   static constexpr int LB = (BN + CR - 1) / CR;       // B copies per thread
-  static constexpr int OFF_B = kSkinnyM * 128;
+  static constexpr int OFF_B = MR * 128;
   static constexpr int OFF_SA = OFF_B + LB * CR * 128;
   // one 64-float scale slot per wave for sA (rows 0..255 are slots 0..3) and for sB: every
   // wave's copy lands in its own slot, even an empty one (which writes zeros)
@@ -45,13 +50,15 @@ struct SkinnyShape {
   static constexpr int STAGE = OFF_SB + NW * 256;
   static constexpr int LDS = 3 * STAGE;
   static_assert(CR % 16 == 0, "swizzle phase must repeat across copies");
+  static_assert(FM >= 1 && MR % CR == 0 && MR <= 256, "row part shape");
+  static_assert(F <= 64, "one B fragment scale per lane of wave 0");
 };
 
 }  // namespace
 
-template <int F, int NW, bool kF32>
+template <int F, int NW, int MR, bool kF32>
 __global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
-  using S = SkinnyShape<F, NW>;
+  using S = SkinnyShape<F, NW, MR>;
   constexpr int FM = S::FM;
   constexpr int WR = 16 * FM;                           // A rows per wave
   static_assert(S::LDS <= 160 * 1024, "LDS budget");
@@ -61,9 +68,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t n0 = (int64_t)blockIdx.x * S::BN;
+  // Workgroup b: XCD b % 8; its row part is (b / 8) % ms and its fragment run
+  // 8 ((b / 8) / ms) + b % 8, so the ms row parts of a run share an XCD and follow each
+  // other in dispatch order. The grid is rounded up to whole groups of 8 runs.
+  const int64_t ms = (M + MR - 1) / MR;
+  const int64_t q8 = blockIdx.x >> 3;
+  const int64_t mpart = q8 % ms, run = (q8 / ms) * 8 + (blockIdx.x & 7);
+  const int64_t n0 = run * S::BN, m0 = mpart * MR;
+  if (n0 >= N) return;                                  // uniform: a padding workgroup
   const int nkb = (int)(K / 128);
-  const int64_t rows_a = M < kSkinnyM ? M : kSkinnyM;
+  const int64_t rows_a = (M - m0) < MR ? (M - m0) : MR;
   const int64_t rows_b = (N - n0) < S::BN ? (N - n0) : S::BN;
   const int fvalid = (int)(rows_b / 16);                // fragments inside N (N % 16 == 0)
 
@@ -74,6 +88,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
   // Scale copies: waves 0..3 fetch sA of rows 64w + lane; wave 0 also fetches the F fragment
   // scales of B (lanes past the last valid fragment repeat it); every other copy goes
   // through an empty descriptor, so that every wave counts the same number of copies.
+  const uint8_t* Ap = p.A + m0 * K;
+  const float* sAp = p.sA + m0 * p.sa_ld;
   const uint32_t offSA = (uint32_t)(((wave & 3) * 64 + lane) * p.sa_ld * 4);
   const uint32_t bytesSA = wave < 4 ? (uint32_t)((rows_a - 1) * p.sa_ld * 4 + 4) : 0u;
   const int fl = lane < fvalid ? lane : fvalid - 1;
@@ -83,19 +99,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
   auto issue = [&](int kb, uint32_t st) __attribute__((always_inline)) {
     const bool live = kb < nkb;
     const int kbc = live ? kb : 0;
+    // One descriptor per operand and K block; copy `it` adds its first row to the lane
+    // offset, and lanes whose offset passes the descriptor's range read zeros.
+    const v4i ra = make_rsrc(Ap + kbc * 128, live ? bytesA : 0u);
 #pragma unroll
-    for (int it = 0; it < S::LA; ++it) {
-      const int64_t r0 = (int64_t)it * S::CR;
-      const uint32_t nb = (live && bytesA > r0 * K) ? (uint32_t)(bytesA - r0 * K) : 0u;
-      dma16(make_rsrc(p.A + r0 * K + kbc * 128, nb), off0, st + (it * S::NT + wave * 64) * 16);
-    }
+    for (int it = 0; it < S::LA; ++it)
+      dma16(ra, off0 + (uint32_t)(it * S::CR) * (uint32_t)K, st + (it * S::NT + wave * 64) * 16);
+    const v4i rb = make_rsrc(p.B + n0 * K + kbc * 128, live ? bytesB : 0u);
 #pragma unroll
-    for (int it = 0; it < S::LB; ++it) {
-      const int64_t r0 = (int64_t)it * S::CR;
-      const uint32_t nb = (live && bytesB > r0 * K) ? (uint32_t)(bytesB - r0 * K) : 0u;
-      dma16(make_rsrc(p.B + (n0 + r0) * K + kbc * 128, nb), off0, st + S::OFF_B + (it * S::NT + wave * 64) * 16);
-    }
-    dma4(make_rsrc(p.sA + kbc, live ? bytesSA : 0u), offSA, st + S::OFF_SA + wave * 256);
+    for (int it = 0; it < S::LB; ++it)
+      dma16(rb, off0 + (uint32_t)(it * S::CR) * (uint32_t)K, st + S::OFF_B + (it * S::NT + wave * 64) * 16);
+    dma4(make_rsrc(sAp + kbc, live ? bytesSA : 0u), offSA, st + S::OFF_SA + wave * 256);
     dma4(make_rsrc(p.sB + (int64_t)kbc * p.sb_ld_k, live ? bytesSB : 0u), offSB, st + S::OFF_SB + wave * 256);
   };
   constexpr int kCopies = S::LA + S::LB + 2;            // copies per wave per stage
@@ -197,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
   // Epilogue: lane holds C[m][n .. n+3] of each 16x16 tile.
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int64_t m = wave * WR + 16 * j + (lane & 15);
+    const int64_t m = m0 + wave * WR + 16 * j + (lane & 15);
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
@@ -227,28 +241,57 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_skinny(GemmParams p) {
 // 4 waves of 64 rows: measured faster than 8 waves of 32 rows for every decode shape.
 constexpr int kSkinnyWaves = 4;
 
-template <int F>
+template <int MR, int F>
 static hipError_t launch_skinny_f(const GemmParams& p, bool f32, hipStream_t stream) {
   constexpr int NW = kSkinnyWaves;
-  const int64_t blocks = (p.N + 16 * F - 1) / (16 * F);
+  const int64_t runs = (p.N + 16 * F - 1) / (16 * F), ms = (p.M + MR - 1) / MR;
+  const int64_t blocks = (runs + 7) / 8 * 8 * ms;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (f32)
-    hipLaunchKernelGGL((k_gemm_skinny<F, NW, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_skinny<F, NW, MR, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<F, NW, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_skinny<F, NW, MR, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-// F = fragments per workgroup: the smallest of 1, 2, 3, 4, 6, 8 that needs at most 256
-// workgroups (one per CU), 8 beyond that.
+// The (MR, F) configurations built, in the order they are considered.
+struct SkinnyCfg {
+  int mr, f;
+  hipError_t (*launch)(const GemmParams&, bool, hipStream_t);
+};
+static const SkinnyCfg kSkinnyCfgs[] = {
+    {256, 1, launch_skinny_f<256, 1>},  {256, 2, launch_skinny_f<256, 2>},  {256, 3, launch_skinny_f<256, 3>},
+    {256, 4, launch_skinny_f<256, 4>},  {256, 6, launch_skinny_f<256, 6>},  {256, 8, launch_skinny_f<256, 8>},
+    {128, 2, launch_skinny_f<128, 2>},  {128, 3, launch_skinny_f<128, 3>},  {128, 4, launch_skinny_f<128, 4>},
+    {128, 6, launch_skinny_f<128, 6>},  {128, 8, launch_skinny_f<128, 8>},  {128, 12, launch_skinny_f<128, 12>},
+    {64, 4, launch_skinny_f<64, 4>},    {64, 6, launch_skinny_f<64, 6>},    {64, 8, launch_skinny_f<64, 8>},
+    {64, 12, launch_skinny_f<64, 12>},  {64, 16, launch_skinny_f<64, 16>},
+};
+
+// For each row-part size MR: the smallest F that needs at most 256 workgroups (one per
+// CU), else its largest F. Among those, the least per-CU copy traffic per K block
+// (min(MR, M) rows of A + 16 F rows of B), then the fewest padded rows (MR x row parts),
+// then the larger MR.
 hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream) {
-  const int64_t frags = p.N / 16;
-  if (frags <= 256) return launch_skinny_f<1>(p, f32, stream);
-  if (frags <= 512) return launch_skinny_f<2>(p, f32, stream);
-  if (frags <= 768) return launch_skinny_f<3>(p, f32, stream);
-  if (frags <= 1024) return launch_skinny_f<4>(p, f32, stream);
-  if (frags <= 1536) return launch_skinny_f<6>(p, f32, stream);
-  return launch_skinny_f<8>(p, f32, stream);
+  const int64_t frags = (p.N + 15) / 16;
+  const SkinnyCfg* best = nullptr;
+  int64_t best_cost = 0, best_pad = 0;
+  for (int mr : {256, 128, 64}) {
+    const SkinnyCfg* pick = nullptr;
+    const int64_t ms = (p.M + mr - 1) / mr;
+    for (const SkinnyCfg& c : kSkinnyCfgs) {
+      if (c.mr != mr) continue;
+      pick = &c;
+      if ((frags + c.f - 1) / c.f * ms <= 256) break;
+    }
+    const int64_t cost = (p.M < mr ? p.M : mr) + 16 * pick->f, pad = mr * ms;
+    if (best == nullptr || cost < best_cost || (cost == best_cost && pad < best_pad)) {
+      best = pick;
+      best_cost = cost;
+      best_pad = pad;
+    }
+  }
+  return best->launch(p, f32, stream);
 }
 
 }  // namespace fp8rl
