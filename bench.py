@@ -61,11 +61,11 @@ MEASURED_TRAFFIC = {
     "dgrad": {"sha": "4789a809d81d8424", "gb": 1.3196},           # read 1.2526 + write 0.0671
     "dgrad_pow2": {"sha": "4789a809d81d8424", "gb": 1.3199},      # read 1.2528 + write 0.0671
     "mx_fwd": {"sha": "4789a809d81d8424", "gb": 1.6505},          # read 1.2481 + write 0.4024
-    "decode_n24576": {"sha": "b2504669b2408216", "gb": 0.1221},   # read 0.1095 + write 0.0126 (GEMM launch)
+    "decode_n24576": {"sha": "a6388fb948d9425a", "gb": 0.1220},   # read 0.1095 + write 0.0126 (GEMM launch)
     "grouped_gu": {"sha": "4789a809d81d8424", "gb": 0.3148},      # read 0.2477 + write 0.0671
     "grouped_gu_block": {"sha": "4789a809d81d8424", "gb": 0.3071},  # read 0.2400 + write 0.0671
     "install_gu": {"sha": "cd3091d8cf3cd067", "gb": 0.2014},      # read 0.1007 + write 0.1007
-    "swiglu_fp8": {"sha": "f42bb3cf95940150", "gb": 0.6476},      # read 0.4034 + write 0.2442
+    "swiglu_fp8": {"sha": "d8d0ba59d8a97aae", "gb": 0.6222},      # read 0.4034 + write 0.2188
     "requant_gu": {"sha": "09a215be0d891edd", "gb": 0.6040},      # read 0.4026 + write 0.2014
 }
 
