@@ -46,6 +46,12 @@ fp8rl_status check_dims(int64_t a, int64_t b) {
   return FP8RL_OK;
 }
 
+// GEMM reduction length: the kernels address up to 256 operand rows of one tile through a
+// single buffer descriptor with 32-bit byte offsets, (256 - 1) * kred + 128 < 2^32.
+constexpr int64_t kMaxRed = (int64_t)1 << 23;
+
+fp8rl_status check_red(int64_t kred) { return kred > kMaxRed ? FP8RL_ERR_SHAPE : FP8RL_OK; }
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +255,7 @@ fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const 
   if (fp8rl_status e = check_dims(N, K)) return e;
   if (fp8rl_status e = check_dims(M, N)) return e;
   if (K % 128 != 0 || N % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (fp8rl_status e = check_red(K)) return e;
   if (M == 0 || N == 0) return FP8RL_OK;
   if (K == 0) return FP8RL_ERR_SHAPE;  // the product would be all zeros; not a supported call
   if (!aligned(wq, 16) || !aligned(sw, 4) || !aligned(y, 16)) return FP8RL_ERR_ALIGN;
@@ -293,6 +300,7 @@ fp8rl_status fp8_gemm_blockscaled_pow2_fwd(const uint8_t* xq, const float* sx, c
   if (fp8rl_status e = check_dims(N, K)) return e;
   if (fp8rl_status e = check_dims(M, N)) return e;
   if (K % 128 != 0 || N % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (fp8rl_status e = check_red(K)) return e;
   if (M == 0 || N == 0) return FP8RL_OK;
   if (K == 0) return FP8RL_ERR_SHAPE;
   if (!aligned(xq, 16) || !aligned(sx, 4) || !aligned(wq, 16) || !aligned(sw, 4) || !aligned(y, 16))
@@ -327,6 +335,7 @@ fp8rl_status mx_gemm_impl(const uint8_t* a, const uint8_t* ea, const uint8_t* b,
   if (fp8rl_status e = check_dims(rb, kred)) return e;
   if (fp8rl_status e = check_dims(ra, rb)) return e;
   if (kred % 128 != 0 || rb % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (fp8rl_status e = check_red(kred)) return e;
   if (ra == 0 || rb == 0) return FP8RL_OK;
   if (kred == 0) return FP8RL_ERR_SHAPE;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(ea, 4) || !aligned(eb, 4) || !aligned(c, 16))
@@ -357,6 +366,7 @@ fp8rl_status dgrad_impl(const uint8_t* dyq, const float* sdy, const uint8_t* wqt
   if (fp8rl_status e = check_dims(N, K)) return e;
   if (fp8rl_status e = check_dims(M, K)) return e;
   if (N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (fp8rl_status e = check_red(N)) return e;
   if (M == 0 || K == 0) return FP8RL_OK;
   if (N == 0) return FP8RL_ERR_SHAPE;
   if (!aligned(dyq, 16) || !aligned(wqt, 16) || !aligned(dx, 16) || !aligned(sdy, 4) || !aligned(sw, 4))
@@ -386,6 +396,7 @@ fp8rl_status wgrad_impl(const uint8_t* dyqt, const float* sdyt, const uint8_t* x
   if (fp8rl_status e = check_dims(M, K)) return e;
   if (fp8rl_status e = check_dims(N, K)) return e;
   if (M % 128 != 0 || N % 128 != 0 || K % 128 != 0) return FP8RL_ERR_SHAPE;
+  if (fp8rl_status e = check_red(M)) return e;
   if (N == 0 || K == 0) return FP8RL_OK;
   if (M == 0) return FP8RL_ERR_SHAPE;
   if (!aligned(dyqt, 16) || !aligned(xqt, 16) || !aligned(dw, 16) || !aligned(sdyt, 4) || !aligned(sxt, 4))
@@ -466,6 +477,7 @@ fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, con
   if (fp8rl_status e = check_dims(T, N)) return e;
   if (K % 128 != 0 || N % 16 != 0 || E > ((int64_t)1 << 24)) return FP8RL_ERR_SHAPE;
   if (recipe == FP8RL_RECIPE_BLOCK128 && N % 128 != 0) return FP8RL_ERR_SHAPE;   // whole 128-row weight blocks
+  if (fp8rl_status e = check_red(K)) return e;
   if (T == 0 || N == 0) return FP8RL_OK;
   if (K == 0) return FP8RL_ERR_SHAPE;
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(sx, 4) || !aligned(sw, 4) ||

@@ -22,6 +22,9 @@
  *     returns FP8RL_OK without touching the device.
  *   - Data pointers must be 16-byte aligned (FP8RL_ERR_ALIGN otherwise); scale pointers
  *     4-byte aligned (fp32) or 1-byte (E8M0).
+ *   - Sizes: every matrix holds at most 2^40 elements, and a GEMM's reduction length (K for
+ *     the forward and grouped GEMMs, N for DGrad, the token count M for WGrad) is at most
+ *     2^23 (FP8RL_ERR_SHAPE otherwise).
  *   - FP8RL_ERR_DEVICE: the current device is not gfx950. FP8RL_ERR_LAUNCH: the kernel
  *     launch was rejected by the runtime. Faults inside a kernel surface at the caller's
  *     next synchronization with the stream, as for any HIP kernel.

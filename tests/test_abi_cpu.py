@@ -188,6 +188,20 @@ def test_mx_dense_validation(lib):
     assert w(P, P, P, P, 128, 0, 128, P, 0, None) == OK
 
 
+def test_reduction_length_limit(lib):
+    """Reduction lengths past 2^23 are rejected before any HIP call (the kernels address a
+    tile's 256 rows with 32-bit byte offsets)."""
+    big = (1 << 23) + 128
+    assert lib.fp8_gemm_blockscaled_fwd(P, P, None, P, P, 4, 128, big, P, 0, None, 0, None) == ERR_SHAPE
+    assert lib.fp8_gemm_blockscaled_pow2_fwd(P, P, P, P, 4, 128, big, P, 0, None) == ERR_SHAPE
+    assert lib.fp8_gemm_blockscaled_dgrad(P, P, P, P, 4, big, 128, P, 0, None) == ERR_SHAPE
+    assert lib.fp8_gemm_blockscaled_wgrad(P, P, P, P, big, 128, 128, P, 0, None) == ERR_SHAPE
+    assert lib.fp8_gemm_mxfp8_fwd(P, P, P, P, 4, 128, big, P, 0, None) == ERR_SHAPE
+    assert lib.fp8_grouped_gemm(F.RECIPE_MXFP8, P, P, P, P, P, 64, 2, 128, big, P, 0, None) == ERR_SHAPE
+    # at the limit the shape rules pass: a zero-row call is OK without touching the device
+    assert lib.fp8_gemm_blockscaled_fwd(P, P, None, P, P, 0, 128, 1 << 23, P, 0, None, 0, None) == OK
+
+
 def test_grouped_validation(lib):
     g = lib.fp8_grouped_gemm
     assert g(7, P, P, P, P, P, 64, 2, 128, 128, P, 0, None) == ERR_RECIPE                # unknown recipe
