@@ -269,9 +269,9 @@ static const SkinnyCfg kSkinnyCfgs[] = {
 };
 
 // For each row-part size MR: the smallest F that needs at most 256 workgroups (one per
-// CU), else its largest F. Among those, the least per-CU copy traffic per K block
-// (min(MR, M) rows of A + 16 F rows of B), then the fewest padded rows (MR x row parts),
-// then the larger MR.
+// CU), else its largest F. Among those, the least copy traffic per CU per K block over
+// the launch (rounds of 256 workgroups x (min(MR, M) rows of A + 16 F rows of B)), then
+// the fewest padded rows (MR x row parts), then the larger MR.
 hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream) {
   const int64_t frags = (p.N + 15) / 16;
   const SkinnyCfg* best = nullptr;
@@ -284,7 +284,8 @@ hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream)
       pick = &c;
       if ((frags + c.f - 1) / c.f * ms <= 256) break;
     }
-    const int64_t cost = (p.M < mr ? p.M : mr) + 16 * pick->f, pad = mr * ms;
+    const int64_t wgs = (frags + pick->f - 1) / pick->f * ms;
+    const int64_t cost = (wgs + 255) / 256 * ((p.M < mr ? p.M : mr) + 16 * pick->f), pad = mr * ms;
     if (best == nullptr || cost < best_cost || (cost == best_cost && pad < best_pad)) {
       best = pick;
       best_cost = cost;

@@ -161,12 +161,15 @@ def test_fwd_decodes_every_e4m3_code():
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 8320, 256), (100, 4224, 384), (256, 12416, 128), (64, 16640, 256),
-                                   (33, 24704, 128), (200, 4224, 512), (130, 8320, 1024), (1, 12416, 2048)])
+                                   (33, 24704, 128), (200, 4224, 512), (130, 8320, 1024), (1, 12416, 2048),
+                                   (130, 32768, 128), (90, 12288, 128), (256, 24576, 128), (40, 49152, 128),
+                                   (60, 65536, 128)])
 def test_fwd_few_rows(M, N, K):
-    """M <= 256 runs the few-row kernel, whose workgroups each take a run of 16-row weight
-    fragments. These N give 2, 3, 4, 6 and 8 fragments per workgroup; 8320 and 16640 leave
-    a last workgroup with fewer fragments, and runs straddle 128-row scale blocks. K of 512,
-    1024 and 2048 (1, 2 and 4 chunks of 4 K blocks) take A's row scales through the ring."""
+    """M <= 256 runs the few-row kernel: each workgroup takes a part of MR = 64, 128 or 256
+    rows and a run of F 16-row weight fragments. These shapes select (MR, F) = (256, 1),
+    (256, 3), (256, 8), (128, 3), (128, 6), (128, 8), (128, 12), (64, 4), (64, 6), (64, 8),
+    (64, 12) and (64, 16); row parts end inside M (M = 33, 90, 100, 130, 200), N = 8320 and
+    16640 leave a last run with fewer fragments, and runs straddle 128-row scale blocks."""
     x, w = _quantized_pair(M, N, K, 5500 + M)
     xq, sx, _, _ = F.fp8_quant_act_1x128(bf16_dev(x))
     wq, sw, _ = F.fp8_quant_w_128x128(bf16_dev(w))
