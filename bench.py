@@ -64,7 +64,7 @@ MEASURED_TRAFFIC = {
     "dgrad": {"sha": "4789a809d81d8424", "gb": 1.3196},           # read 1.2526 + write 0.0671
     "dgrad_pow2": {"sha": "4789a809d81d8424", "gb": 1.3199},      # read 1.2528 + write 0.0671
     "mx_fwd": {"sha": "4789a809d81d8424", "gb": 1.6505},          # read 1.2481 + write 0.4024
-    "decode_n24576": {"sha": "a6388fb948d9425a", "gb": 0.1220},   # read 0.1095 + write 0.0126 (GEMM launch)
+    "decode_n24576": {"sha": "b0161bd42d71bc08", "gb": 0.1221},   # read 0.1095 + write 0.0126 (GEMM launch)
     "grouped_gu": {"sha": "4789a809d81d8424", "gb": 0.3148},      # read 0.2477 + write 0.0671
     "grouped_gu_block": {"sha": "4789a809d81d8424", "gb": 0.3071},  # read 0.2400 + write 0.0671
     "install_gu": {"sha": "cd3091d8cf3cd067", "gb": 0.2014},      # read 0.1007 + write 0.1007
