@@ -296,6 +296,33 @@ def test_grouped_block(T_tokens, E, topk, N, K):
     assert_bf16_consistent(y16, y32, ref, "grouped block bf16")
 
 
+@pytest.mark.parametrize("E,recipe", [(150, "mx"), (150, "block"), (129, "mx")])
+def test_grouped_many_experts(E, recipe):
+    """More experts than one 64-lane step of the tile search (three steps for E = 129 and
+    150), many of them empty, rows ragged: every routed row must land on its own expert."""
+    T_tokens, topk, N, K = 300, 2, 128, 256
+    perm, offsets = _routing(T_tokens, E, topk, 9400 + E)
+    assert np.sum(np.diff(offsets) == 0) > 0 and offsets[-1] == T_tokens * topk
+    x = _rand((T_tokens, K), 9401 + E)[perm]
+    w = _rand((E, N, K), 9402 + E, 0.02)
+    off = torch.from_numpy(offsets).to(dev())
+    if recipe == "mx":
+        rxq, rsx = OQ.quant_mx_1x32(x)
+        rwq, rsw = OQ.quant_mx_1x32(w.reshape(E * N, K))
+        rwq, rsw = rwq.reshape(E, N, K), rsw.reshape(E, N, K // 32)
+        args = (u8_dev(rxq), u8_dev(rsx), u8_dev(rwq), u8_dev(rsw), off)
+        y = F.fp8_grouped_gemm(*args, recipe=F.RECIPE_MXFP8, out_dtype=torch.float32)
+        ref = OG.grouped_gemm_mx(rxq, rsx, rwq, rsw, offsets)
+    else:
+        rxq, rsx = OQ.quant_act_1x128(x)
+        rwq, rsw = OQ.quant_w_128x128(w.reshape(E * N, K))
+        rwq, rsw = rwq.reshape(E, N, K), rsw.reshape(E, N // 128, K // 128)
+        args = (u8_dev(rxq), f32_dev(rsx), u8_dev(rwq), f32_dev(rsw), off)
+        y = F.fp8_grouped_gemm(*args, recipe=F.RECIPE_BLOCK128, out_dtype=torch.float32)
+        ref = OG.grouped_gemm_block(rxq, rsx, rwq, rsw, offsets)
+    assert_gemm_close(host(y), ref, f"grouped E={E} {recipe}")
+
+
 def test_grouped_block_empty_experts_and_gpu_quantizers():
     """Empty experts, and operands from the library's own quantizers (whose bytes and scales
     equal the oracle's): the weight stack [E][N][K] quantized as one [E*N][K] matrix gives
