@@ -119,3 +119,33 @@ def test_bigtile_mxfp8(data):
     dw = F.fp8_gemm_mxfp8_wgrad(*A, u8_dev(bq), _e8m0_dev(eb))
     assert_gemm_close(host(dw[torch.from_numpy(ROWS).to(dev())]), OG.gemm_mx_wgrad(aq[ROWS], ea[ROWS], bq, eb),
                       "mx wgrad")
+
+
+def _codes_dev(shape, gen):
+    """Random E4M3 codes on the GPU, NaN codes (0x7F, 0xFF) replaced by 0x7E / 0xFE."""
+    c = torch.randint(0, 256, shape, dtype=torch.int32, device=dev(), generator=gen)
+    c = torch.where((c & 0x7F) == 0x7F, c - 1, c)
+    return c.to(torch.uint8)
+
+
+@pytest.mark.parametrize("nkb", [1024, 1032])
+def test_bigtile_longest_reduction(nkb):
+    """Forward GEMM 4096 x 4096 with K = 128 nkb: 1024 K blocks fill the per-tile table of B's
+    block scales (its maximum), 1032 take the per-K-block scale loads instead. Operands are
+    random E4M3 codes and scales made on the GPU; the oracle recomputes sampled rows against
+    two whole 128-row weight blocks."""
+    M = N = 4096
+    K = 128 * nkb
+    gen = torch.Generator(device=dev())
+    gen.manual_seed(12000 + nkb)
+    xq = _codes_dev((M, K), gen)
+    wq = _codes_dev((N, K), gen)
+    sx = torch.rand((M, nkb), device=dev(), generator=gen) * 2.0 ** -12 + 2.0 ** -14
+    sw = torch.rand((N // 128, nkb), device=dev(), generator=gen) * 2.0 ** -12 + 2.0 ** -14
+    y = F.fp8_gemm_blockscaled_fwd(xq, sx, wq, sw, out_dtype=torch.float32)
+    rows = torch.tensor([0, 1, 255, 256, 2047, 4095], device=dev())
+    blocks = [0, 31]
+    wrows = torch.cat([torch.arange(b * 128, (b + 1) * 128, device=dev()) for b in blocks])
+    ref = OG.gemm_fwd(host(xq[rows]), host(sx[rows]), host(wq[wrows]), host(sw[torch.tensor(blocks, device=dev())]))
+    got = host(y[rows][:, wrows])
+    assert_gemm_close(got, ref, f"fwd K blocks {nkb}")
