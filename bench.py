@@ -59,17 +59,17 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "4789a809d81d8424", "gb": 1.6404},         # read 1.2381 + write 0.4024
-    "gemm_gu_pow2": {"sha": "4789a809d81d8424", "gb": 1.6403},    # read 1.2380 + write 0.4024
-    "dgrad": {"sha": "4789a809d81d8424", "gb": 1.3196},           # read 1.2526 + write 0.0671
-    "dgrad_pow2": {"sha": "4789a809d81d8424", "gb": 1.3199},      # read 1.2528 + write 0.0671
-    "mx_fwd": {"sha": "4789a809d81d8424", "gb": 1.6505},          # read 1.2481 + write 0.4024
-    "decode_n24576": {"sha": "b0161bd42d71bc08", "gb": 0.1221},   # read 0.1095 + write 0.0126 (GEMM launch)
-    "grouped_gu": {"sha": "4789a809d81d8424", "gb": 0.3148},      # read 0.2477 + write 0.0671
-    "grouped_gu_block": {"sha": "4789a809d81d8424", "gb": 0.3071},  # read 0.2400 + write 0.0671
-    "install_gu": {"sha": "cd3091d8cf3cd067", "gb": 0.2014},      # read 0.1007 + write 0.1007
-    "swiglu_fp8": {"sha": "d8d0ba59d8a97aae", "gb": 0.6222},      # read 0.4034 + write 0.2188
-    "requant_gu": {"sha": "09a215be0d891edd", "gb": 0.6040},      # read 0.4026 + write 0.2014
+    "gemm_gu": {"sha": "b00a1adf20202e60", "gb": 1.6404},         # read 1.2381 + write 0.4024
+    "gemm_gu_pow2": {"sha": "b00a1adf20202e60", "gb": 1.6403},    # read 1.2380 + write 0.4024
+    "dgrad": {"sha": "b00a1adf20202e60", "gb": 1.3196},           # read 1.2526 + write 0.0671
+    "dgrad_pow2": {"sha": "b00a1adf20202e60", "gb": 1.3199},      # read 1.2528 + write 0.0671
+    "mx_fwd": {"sha": "b00a1adf20202e60", "gb": 1.6505},          # read 1.2481 + write 0.4024
+    "decode_n24576": {"sha": "5746227836d936c0", "gb": 0.1221},   # read 0.1095 + write 0.0126 (GEMM launch)
+    "grouped_gu": {"sha": "b00a1adf20202e60", "gb": 0.3148},      # read 0.2477 + write 0.0671
+    "grouped_gu_block": {"sha": "b00a1adf20202e60", "gb": 0.3071},  # read 0.2400 + write 0.0671
+    "install_gu": {"sha": "0812b2c187970561", "gb": 0.2014},      # read 0.1007 + write 0.1007
+    "swiglu_fp8": {"sha": "ab708bfd3307f025", "gb": 0.6222},      # read 0.4034 + write 0.2188
+    "requant_gu": {"sha": "a0c8890e60bc35c0", "gb": 0.6040},      # read 0.4026 + write 0.2014
 }
 
 

@@ -126,7 +126,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // from rsrc + voff land at LDS address lds + 16 * i (or 4 * i); lds must be wave-uniform.
 // Issued as inline assembly on purpose: the copy's completion is awaited explicitly
 // (wait_vmem() followed by a barrier before the stage is read), so the compiler must not
-// insert its own conservative vmcnt waits in front of unrelated LDS reads.
+// insert its own conservative vmcnt waits in front of unrelated LDS reads. The copy
+// instruction takes its LDS address in m0, which the asm sets and declares clobbered
+// (the compiler warns that m0 is reserved); gfx950 code needs m0 for nothing else here,
+// and the generated kernels contain no other access to it.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
