@@ -59,16 +59,16 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "b00a1adf20202e60", "gb": 1.6404},         # read 1.2381 + write 0.4024
-    "gemm_gu_pow2": {"sha": "b00a1adf20202e60", "gb": 1.6403},    # read 1.2380 + write 0.4024
-    "dgrad": {"sha": "b00a1adf20202e60", "gb": 1.3196},           # read 1.2526 + write 0.0671
-    "dgrad_pow2": {"sha": "b00a1adf20202e60", "gb": 1.3199},      # read 1.2528 + write 0.0671
-    "mx_fwd": {"sha": "b00a1adf20202e60", "gb": 1.6505},          # read 1.2481 + write 0.4024
-    "decode_n24576": {"sha": "5746227836d936c0", "gb": 0.1221},   # read 0.1095 + write 0.0126 (GEMM launch)
-    "grouped_gu": {"sha": "b00a1adf20202e60", "gb": 0.3148},      # read 0.2477 + write 0.0671
-    "grouped_gu_block": {"sha": "b00a1adf20202e60", "gb": 0.3071},  # read 0.2400 + write 0.0671
+    "gemm_gu": {"sha": "b00a1adf20202e60", "gb": 1.6407},         # read 1.2383 + write 0.4024
+    "gemm_gu_pow2": {"sha": "b00a1adf20202e60", "gb": 1.6404},    # read 1.2380 + write 0.4024
+    "dgrad": {"sha": "b00a1adf20202e60", "gb": 1.3172},           # read 1.2502 + write 0.0671
+    "dgrad_pow2": {"sha": "b00a1adf20202e60", "gb": 1.3173},      # read 1.2503 + write 0.0671
+    "mx_fwd": {"sha": "b00a1adf20202e60", "gb": 1.6497},          # read 1.2474 + write 0.4024
+    "decode_n24576": {"sha": "5746227836d936c0", "gb": 0.1220},   # read 0.1095 + write 0.0126 (GEMM launch)
+    "grouped_gu": {"sha": "b00a1adf20202e60", "gb": 0.3147},      # read 0.2476 + write 0.0671
+    "grouped_gu_block": {"sha": "b00a1adf20202e60", "gb": 0.3067}, # read 0.2397 + write 0.0671
     "install_gu": {"sha": "0812b2c187970561", "gb": 0.2014},      # read 0.1007 + write 0.1007
-    "swiglu_fp8": {"sha": "ab708bfd3307f025", "gb": 0.6222},      # read 0.4034 + write 0.2188
+    "swiglu_fp8": {"sha": "ab708bfd3307f025", "gb": 0.6223},      # read 0.4035 + write 0.2189
     "requant_gu": {"sha": "a0c8890e60bc35c0", "gb": 0.6040},      # read 0.4026 + write 0.2014
 }
 
