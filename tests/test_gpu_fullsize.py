@@ -138,6 +138,35 @@ def test_dense_backward_full_size(dense):
     assert_gemm_close(host(_rows_of(dw, ns))[:, ks], ref, "wgrad")
 
 
+def test_dense_backward_pow2_full_size(dense):
+    """The backward_pow2 workload: power-of-two 1x128 / 128x1 / 128x128 scales, DGrad and
+    WGrad with the scales applied by the MFMA, on sampled outputs."""
+    d, t = dense
+    dy_np = W.dense_backward()["dy"]
+    dy = W.to_bf16_tensor(dy_np).to(dev())
+    M, N = dy_np.shape
+    K = d["x"].shape[1]
+    dyq, sdy, dyqt, sdyt = F.fp8_quant_act_1x128_pow2(dy, rowwise=True, colwise=True)
+    _, _, xqt, sxt = F.fp8_quant_act_1x128_pow2(t["x"], rowwise=False, colwise=True)
+    wq, sw, wqt = F.fp8_quant_w_128x128_pow2(t["w_gu"], transpose=True)
+    dx = F.fp8_gemm_blockscaled_pow2_dgrad(dyq, sdy, wqt, sw, out_dtype=torch.float32)
+    dw = F.fp8_gemm_blockscaled_pow2_wgrad(dyqt, sdyt, xqt, sxt)
+    rows = _sample(M, 12, 16)
+    kblocks = sorted(_sample(K // 128, 2, 17).tolist())
+    kcols = np.concatenate([np.arange(b * 128, (b + 1) * 128) for b in kblocks])
+    rdyq, rsdy = OQ.quant_act_1x128_pow2(dy_np[rows])
+    assert_bytes_equal(_rows_of(dyq, rows), rdyq, "pow2 dyq rows")
+    assert_bytes_equal(_rows_of(sdy, rows), rsdy, "pow2 sdy rows")
+    rwq, rsw = OQ.quant_w_128x128_pow2(np.ascontiguousarray(d["w_gu"][:, kcols]))
+    assert_gemm_close(host(_rows_of(dx, rows))[:, kcols], OG.gemm_dgrad(rdyq, rsdy, rwq, rsw), "pow2 dgrad")
+    ns, ks = _sample(N, 10, 18), _sample(K, 10, 19)
+    rdyqt, rsdyt = OQ.quant_act_1x128_pow2(np.ascontiguousarray(dy_np[:, ns].T))
+    rxqt, rsxt = OQ.quant_act_1x128_pow2(np.ascontiguousarray(d["x"][:, ks].T))
+    assert_bytes_equal(_rows_of(dyqt, ns), rdyqt, "pow2 dyqt columns")
+    assert_bytes_equal(_rows_of(sdyt, ns), rsdyt, "pow2 sdyt columns")
+    assert_gemm_close(host(_rows_of(dw, ns))[:, ks], OG.gemm_wgrad(rdyqt, rsdyt, rxqt, rsxt), "pow2 wgrad")
+
+
 def test_decode_full_size_install_and_naive_control():
     d = W.decode_rollout()
     x = W.to_bf16_tensor(d["x"]).to(dev())
