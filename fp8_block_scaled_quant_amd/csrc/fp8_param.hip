@@ -50,11 +50,19 @@ __global__ __launch_bounds__(512) void k_quant_w_f32(const float* __restrict__ w
     sv = ldexpf(1.0f, e);
   } else {
     sv = (a == 0.0f) ? 1.0f : a / kE4M3Max;
+    // An amax below about 224 * 2^-149 gives a scale that rounds to zero: it is raised to
+    // the smallest positive fp32 value, so every quotient stays finite.
+    if (sv == 0.0f) sv = __uint_as_float(1u);
   }
   if (tid == 0) s[rb * ncb + cb] = sv;
-  // fl32(x / s): exact scaling by 2^-e, or an IEEE division; |x / s| < 449, so the
-  // non-saturating conversion never sees a value it would turn into NaN.
-  auto quo = [&](float x) __attribute__((always_inline)) { return kPow2 ? ldexpf(x, -e) : x / sv; };
+  // fl32(x / s): exact scaling by 2^-e (at most 448 in magnitude), or an IEEE division. A
+  // subnormal scale with few significant bits can give quotients up to 512, which the
+  // non-saturating converter would turn into NaN: they are clamped to +-448 first, the
+  // saturation of the E4M3 encoding (values in (448, 464) round to 448 anyway).
+  auto quo = [&](float x) __attribute__((always_inline)) {
+    if constexpr (kPow2) return ldexpf(x, -e);
+    else return fminf(fmaxf(x / sv, -kE4M3Max), kE4M3Max);
+  };
 
   uint2 code[4];
 #pragma unroll

@@ -117,7 +117,10 @@ fp8rl_status fp8_quant_w_128x128_pow2(const uint16_t* w, int64_t N, int64_t K,
  * parameter storage is recomputed from it after each step). 128x128 blocks quantized from
  * fp32 values: s = fl32(amax / 448) (pow2_scales == 0) or the power-of-two rule of
  * fp8_quant_w_128x128_pow2 (pow2_scales != 0); q = E4M3(fl32(w / s)) with an IEEE fp32
- * division (exact scaling for power-of-two scales).
+ * division (exact scaling for power-of-two scales). A block amax so small that
+ * fl32(amax / 448) rounds to zero (below about 224 * 2^-149) gets s = 2^-149, the smallest
+ * positive fp32 value, and a quotient beyond 448 (possible only with a subnormal s of a few
+ * significant bits) saturates to +-448; neither case arises for bf16-representable values.
  *   w  : fp32 [N][K], finite;  q uint8 [N][K];  s fp32 [N/128][K/128]
  *   qt : optional (NULL allowed) byte transpose of q, uint8 [K][N] (the DGrad operand).
  * Rules: N % 128 == 0, K % 128 == 0. Bytes and scales are bit-identical to the CPU oracle. */

@@ -17,6 +17,12 @@ Readings:
   q = E4M3(fl32(w / s)) with an IEEE fp32 division (w has 24 significant bits here; the
   power-of-two case is the exact scaling). Q(W_t) comes with its byte transpose, the DGrad
   operand.
+* Tiny blocks. An fp32 amax below about 224 * 2^-149 makes fl32(amax / 448) round to zero;
+  such a scale is raised to the smallest positive fp32 value, 2^-149, so the quotient stays
+  finite. A block whose amax sits a little above that gets a subnormal scale with only a few
+  significant bits, and fl32(w / s) can then exceed 448 (up to 512); the encoder saturates
+  it to +-448 like any other value beyond the E4M3 range. bf16 inputs never reach either
+  case: their smallest amax gives a scale with at least 7 significant bits.
 * Displacement after T steps: ||deq Q(W_T) - deq Q(W_0)|| / ||W_T - W_0||, in the L2 and the
   L1 norm (fp64). Cosine: <dW, deq Q(W + dW) - deq Q(W)> / (||dW|| ||..||).
 * Synthetic trajectory (no model or optimizer is available): W_0 ~ N(0, 0.02) fp32 and
@@ -27,9 +33,11 @@ Readings:
 
 Pinned by tests/test_oracle_fp8_param.py: a pure-Python brute force of the fp32-input
 quantizer on small blocks (exact fractions, nearest-in-table encoding; both scale formats),
-the closed form of an update that moves every element by a whole number of quantization
-steps (displacement ratio exactly 1, cosine exactly 1), and invariance of both metrics
-under a common power-of-two scaling.
+blocks whose amax gives an underflowed or few-bit subnormal scale (same brute force), the
+closed form of an update that moves every element by a whole number of quantization
+steps (displacement ratio exactly 1, cosine exactly 1), invariance of both metrics under a
+common power-of-two scaling, hand-computed sign steps (sign(0) = 0, fp32 sum before the
+sign), and the closed form of a trajectory whose every step adds exactly lr.
 """
 
 from __future__ import annotations
@@ -38,6 +46,9 @@ import numpy as np
 
 from .fp8_formats import E4M3_MAX, decode_e4m3, encode_e4m3
 from .quantize import GROUP, mx_exponent
+
+
+_F32_MIN_POSITIVE = np.float32(2.0 ** -149)
 
 
 def _as_f32_finite(w) -> np.ndarray:
@@ -63,6 +74,7 @@ def quant_w_128x128_f32(w, pow2: bool = False):
         v = np.ldexp(b.astype(np.float64), -e[:, None, :, None]).astype(np.float32)   # exact, or the fp32 rounding
     else:
         s = np.where(amax == 0, np.float32(1.0), (amax / np.float32(E4M3_MAX)).astype(np.float32))
+        s = np.where(s == 0, _F32_MIN_POSITIVE, s).astype(np.float32)                    # underflowed scale
         v = (b / s[:, None, :, None]).astype(np.float32)                                 # IEEE fp32 division
     return encode_e4m3(v).reshape(N, K), s.astype(np.float32)
 

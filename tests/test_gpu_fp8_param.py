@@ -42,6 +42,27 @@ def test_fp8_param_requant_parity(N, K, pow2):
     assert_bytes_equal(qt, OQ.transpose_payload(rq), "qt")
 
 
+def test_fp8_param_tiny_blocks():
+    """Blocks whose only nonzero values are fp32 subnormals: a scale that rounds to zero
+    (raised to 2^-149) and one with a single significant bit whose quotient (512) saturates
+    to 448; never a NaN code."""
+    tiny = [2.0 ** -140, 2.0 ** -148, 2.0 ** -149, 300 * 2.0 ** -149, 223 * 2.0 ** -149, 3e-39]
+    w = np.zeros((256, 128 * len(tiny)), np.float32)
+    for b, a in enumerate(tiny):
+        w[0, 128 * b] = np.float32(a)
+        w[131, 128 * b + 5] = -np.float32(a)
+        w[200, 128 * b + 9] = np.float32(a) * np.float32(0.5)
+    for pow2 in (False, True):
+        q, s, qt = F.fp8_quant_w_128x128_f32(_f32_dev(w), transpose=True, pow2_scales=pow2)
+        rq, rs = P.quant_w_128x128_f32(w, pow2)
+        assert_bytes_equal(q, rq, "q")
+        assert_bytes_equal(s, rs, "s")
+        assert_bytes_equal(qt, OQ.transpose_payload(rq), "qt")
+        assert not np.any((host(q) & 0x7F) == 0x7F)
+        if not pow2:
+            assert host(s)[0, 0] == np.float32(2.0 ** -149) and host(q)[0, 0] == 0x7E
+
+
 def test_fp8_param_bf16_values_match_bf16_quantizer():
     """On bf16-representable masters the fp32-input quantizer gives the bf16 quantizer's bytes."""
     rng = np.random.default_rng(30100)

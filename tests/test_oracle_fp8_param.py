@@ -21,6 +21,8 @@ def _brute_block_f32(vals, pow2):
         codes = [_enc_fraction(_fl32(v / s), np.signbit(np.float32(v0))) for v, v0 in zip(fr, vals)]
     else:
         s = Fraction(1) if amax == 0 else _fl32(amax / 448)
+        if s == 0:
+            s = Fraction(1, 2 ** 149)          # a scale that underflowed: the smallest positive fp32
         codes = [_enc_fraction(_fl32(v / s), np.signbit(np.float32(v0))) for v, v0 in zip(fr, vals)]
     return codes, float(s)
 
@@ -40,6 +42,73 @@ def test_f32_quantizer_brute_force(pow2):
         codes, sc = _brute_block_f32(blk.reshape(-1), pow2)
         assert s[bi, 0] == np.float32(sc)
         assert list(q[bi * 128:(bi + 1) * 128].reshape(-1)) == codes
+
+
+def test_f32_quantizer_tiny_blocks():
+    """Blocks whose amax lies deep in the fp32 subnormal range: fl32(amax / 448) is zero (the
+    scale becomes 2^-149) or a subnormal with one or two significant bits (quotients above
+    448 saturate). The brute force applies the same reading with exact fractions; the
+    hand-computed cases fix it independently of the brute force."""
+    tiny = [2.0 ** -140, 2.0 ** -148, 2.0 ** -149, 300 * 2.0 ** -149, 223 * 2.0 ** -149, 225 * 2.0 ** -149]
+    w = np.zeros((128, 128 * len(tiny)), np.float32)
+    for b, a in enumerate(tiny):
+        w[0, 128 * b] = np.float32(a)
+        w[5, 128 * b + 3] = -np.float32(a)
+        w[9, 128 * b + 7] = np.float32(a) * np.float32(0.5) if a >= 2.0 ** -148 else 0.0
+    for pow2 in (False, True):
+        q, s = P.quant_w_128x128_f32(w, pow2)
+        for b in range(len(tiny)):
+            blk = w[:, 128 * b:128 * (b + 1)]
+            codes, sc = _brute_block_f32(blk.reshape(-1), pow2)
+            assert s[0, b] == np.float32(sc), (b, pow2)
+            assert list(q[:, 128 * b:128 * (b + 1)].reshape(-1)) == codes, (b, pow2)
+        assert not np.any((q & 0x7F) == 0x7F)                    # never a NaN code
+    q, s = P.quant_w_128x128_f32(w)
+    two149 = np.float32(2.0 ** -149)
+    # 2^-140 / 448 = 1.14 * 2^-149 rounds to 2^-149: the quotient 512 saturates to 448, the
+    # half-size element's 256 is exact (0x78)
+    assert s[0, 0] == two149 and q[0, 0] == 0x7E and q[5, 3] == 0xFE and q[9, 7] == 0x78
+    # 2^-148 / 448 and 2^-149 / 448 round to zero: s = 2^-149, quotients 2 and 1
+    assert s[0, 1] == two149 and q[0, 128] == 0x40 and q[9, 135] == 0x38     # E4M3(2) = 0x40, E4M3(1) = 0x38
+    assert s[0, 2] == two149 and q[0, 256] == 0x38 and q[5, 259] == 0xB8
+    # 300 * 2^-149 / 448 = 0.67 * 2^-149 rounds to 2^-149 (quotient 300 -> 288 = 0x79); 223 * 2^-149
+    # gives 0.498 * 2^-149 -> 0 -> 2^-149 (quotient 223 -> 224 = 0x76); 225 * 2^-149 gives 0.502 * 2^-149
+    # -> 2^-149 (quotient 225 -> 224)
+    assert s[0, 3] == two149 and q[0, 384] == 0x79
+    assert s[0, 4] == two149 and q[0, 512] == 0x76
+    assert s[0, 5] == two149 and q[0, 640] == 0x76
+
+
+def test_sign_step_hand_values():
+    """dW = fl32(lr) * sign(fl32(b + z)): the sign of the fp32 sum, 0 where the sum is zero."""
+    bias = np.array([1.0, -1.0, 0.0, 0.5, -0.25, 1.0, 1.0, -0.0, 3.0], np.float32)
+    z = np.array([0.0, 0.0, 0.0, -0.5, 0.25, -1.0 + 2.0 ** -23, -1.0 + 2.0 ** -30, 0.0, -2.5], np.float32)
+    # sums: 1, -1, 0, 0, 0, 2^-23 (exact), 0 (z rounds to -1 in fp32), -0, 0.5
+    lr = np.float32(1e-6)
+    expect = np.array([lr, -lr, 0, 0, 0, lr, 0, 0, lr], np.float32)
+    d = P.sign_step(bias, z, 1e-6)
+    assert d.dtype == np.float32 and np.array_equal(d, expect)
+    assert float(d[0]) == float(np.float32(1e-6)) and float(np.float32(1e-6)) != 1e-6     # lr is the fp32 value
+    d2 = P.sign_step(bias[:2], z[:2], 2.0 ** -20)
+    assert d2.tolist() == [2.0 ** -20, -(2.0 ** -20)]
+
+
+def test_trajectory_closed_form():
+    """With a bias that dominates the noise every step adds exactly +lr (or -lr): W_0 and lr
+    powers of two keep every fp32 sum exact, so W_T = W_0 + T * lr * sign(b) in closed form,
+    and the checkpoints carry the quantization of exactly that matrix."""
+    rng = np.random.default_rng(53)
+    w0 = np.full((128, 128), 0.5, np.float32)
+    w0[:, ::2] = -0.25
+    bias = np.where(rng.standard_normal(w0.shape) > 0, np.float32(4.0), np.float32(-4.0)).astype(np.float32)
+    bank = [np.clip(rng.standard_normal(w0.shape), -1, 1).astype(np.float32) for _ in range(3)]
+    lr = 2.0 ** -12
+    out = P.trajectory(w0, bias, bank, lr, 7, [3, 7])
+    for t in (0, 3, 7):
+        expect = (w0.astype(np.float64) + t * lr * np.sign(bias)).astype(np.float32)
+        assert np.array_equal(out[t][0], expect), t
+        q, s = P.quant_w_128x128_f32(expect)
+        assert np.array_equal(out[t][1], q) and np.array_equal(out[t][2], s)
 
 
 def test_f32_quantizer_rejects_bad_input():

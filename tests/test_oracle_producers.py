@@ -192,3 +192,59 @@ def test_rmsnorm_close_to_plain_fp64_and_quant_composition():
     qp, sp = P.rmsnorm_quant_1x128(x, gamma, 1e-6, pow2=True)[:2]
     rqp, rsp = OQ.quant_act_1x128_pow2(y)
     assert np.array_equal(qp, rqp) and np.array_equal(sp, rsp)
+
+
+def _round_binary(fr: Fraction, p: int, emin: int) -> Fraction:
+    """Exact round-to-nearest-even of a rational to a binary format with p significant bits
+    whose smallest normal binade is 2^emin (subnormals below it); integer arithmetic only."""
+    if fr == 0:
+        return Fraction(0)
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, emin) - (p - 1))
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return (fl * quantum) if fr > 0 else -(fl * quantum)
+
+
+def _f32r(fr):
+    return _round_binary(fr, 24, -126)
+
+
+def _bf16r(fr):
+    return _round_binary(fr, 8, -126)
+
+
+def test_rmsnorm_exact_rational_brute_force():
+    """y = bf16(fl32(gamma * bf16(fl32(x * r)))) recomputed in exact rationals from r (itself
+    checked against the exact reciprocal square root). The rows and gamma are such that each
+    plausible mis-reading changes y somewhere: dropping the inner bf16 rounding, multiplying
+    by gamma before r, or rounding the whole product once."""
+    rng = np.random.default_rng(6)
+    M, K = 8, 128
+    x = W.bf16_round(rng.standard_normal((M, K)).astype(np.float32) * np.float32(1.7))
+    x[1] = W.bf16_round(x[1] * np.float32(2.0 ** -20))
+    x[2, ::5] = 0.0
+    gamma = W.bf16_round(1.0 + rng.standard_normal(K).astype(np.float32) * np.float32(0.3))
+    y, r, amb = P.rmsnorm_bf16(x, gamma, 1e-6)
+    assert not amb.any()
+    miss = {"no_inner_bf16": 0, "gamma_first": 0, "single_rounding": 0}
+    for m in range(M):
+        assert _exact_r_check(x[m], 1e-6, r[m]), m
+        rf = Fraction(float(r[m]))
+        for k in range(K):
+            xf, gf = Fraction(float(x[m, k])), Fraction(float(gamma[k]))
+            t = _bf16r(_f32r(xf * rf))
+            want = _bf16r(_f32r(gf * t))
+            assert Fraction(float(y[m, k])) == want, (m, k)
+            miss["no_inner_bf16"] += _bf16r(_f32r(gf * _f32r(xf * rf))) != want
+            miss["gamma_first"] += _bf16r(_f32r(_f32r(gf * xf) * rf)) != want
+            miss["single_rounding"] += _bf16r(gf * xf * rf) != want
+    assert all(v > 0 for v in miss.values()), miss

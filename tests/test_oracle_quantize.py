@@ -319,3 +319,22 @@ def test_mx_32x1_brute_force_and_layout():
     assert et[3, 0] == 127 and et[7, 1] == 127 + 3
     with pytest.raises(ValueError):
         Q.quant_mx_32x1(x[:40])
+
+
+def test_transpose_payload_layout():
+    """qt[j][i] == q[i][j] for every index of a non-square payload of distinct bytes; the
+    result is a new C-contiguous uint8 array (the DGrad operand is read row by row)."""
+    q = (np.arange(3 * 80, dtype=np.int64) % 251).astype(np.uint8).reshape(3, 80)
+    qt = Q.transpose_payload(q)
+    assert qt.shape == (80, 3) and qt.dtype == np.uint8 and qt.flags["C_CONTIGUOUS"]
+    for i in range(3):
+        for j in range(80):
+            assert qt[j, i] == (i * 80 + j) % 251
+    assert qt.ctypes.data != q.ctypes.data
+    # 128x128 blocks map onto 128x128 blocks: block (bi, bj) of q is block (bj, bi) of qt
+    w = (np.arange(256 * 384, dtype=np.int64) % 253).astype(np.uint8).reshape(256, 384)
+    wt = Q.transpose_payload(w)
+    for bi in range(2):
+        for bj in range(3):
+            blk = w[128 * bi:128 * (bi + 1), 128 * bj:128 * (bj + 1)]
+            assert np.array_equal(wt[128 * bj:128 * (bj + 1), 128 * bi:128 * (bi + 1)], blk.T)

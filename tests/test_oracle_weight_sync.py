@@ -48,3 +48,58 @@ def test_relative_error_definition_by_hand():
     # (0.5 + 0 + 0.25 + 1) / (1 + 2 + 0 + 4) = 1.75 / 7
     assert S.mean_relative_error(ref, other) == 0.25
     assert S.mean_relative_error(np.zeros(3), np.ones(3)) == 0.0
+
+
+def _brute_naive(q, s):
+    """Exact-rational naive path: (codes, s_t) and the codes that skipping the bf16 step gives."""
+    from fractions import Fraction
+
+    from test_oracle_producers import _bf16r, _f32r
+    from test_oracle_quantize import _enc_fraction
+
+    dec = [Fraction(float(v)) for v in decode_e4m3(np.arange(0x7F, dtype=np.uint8))]
+    n, k = q.shape
+    v32 = {}
+    for i in range(n):
+        for j in range(k):
+            c = int(q[i, j])
+            v = dec[c & 0x7F] * Fraction(float(s[i // 128, j // 128]))
+            v32[i, j] = _f32r(-v if c & 0x80 else v)
+    wp = {ij: _bf16r(v) for ij, v in v32.items()}
+    st = _f32r(max(abs(v) for v in wp.values()) / 448)
+    codes = np.zeros((n, k), np.int64)
+    skip = np.zeros((n, k), np.int64)
+    for (i, j), v in wp.items():
+        neg = bool(q[i, j] & 0x80)
+        codes[i, j] = _enc_fraction(_f32r(v / st), neg)
+        skip[i, j] = _enc_fraction(_f32r(v32[i, j] / st), neg)
+    return codes, st, skip
+
+
+def test_naive_resync_brute_force():
+    """The naive path recomputed element by element in exact rationals: w' = bf16(fl32(dec(q) s)),
+    s_t = fl32(amax(w') / 448), q' = E4M3(fl32(w' / s_t)), on generic quantized weights and on
+    a constructed pair of blocks: block 0 holds the tensor amax (code 448, s = 1, so s_t = 1),
+    block 1 has s = 1.0625 + 2^-12, so code 1.0 dequantizes to 1.06274 in fp32 (above the
+    1.0 / 1.125 midpoint: E4M3 1.125) but to exactly the midpoint 1.0625 in bf16 (ties to even:
+    E4M3 1.0). Skipping the bf16 step therefore changes that code."""
+    from fractions import Fraction
+
+    w = normal_bf16((128, 384), 0.02, 100, 2)
+    q, s = Q.quant_w_128x128(w)
+    q2, s_t = S.naive_resync(q, s)
+    codes, st, _ = _brute_naive(q, s)
+    assert Fraction(float(s_t)) == st and np.array_equal(q2.astype(np.int64), codes)
+
+    rng = np.random.default_rng(104)
+    qc = rng.integers(0, 0x41, size=(128, 256), dtype=np.uint8) | (rng.integers(0, 2, (128, 256), dtype=np.uint8) << 7)
+    qc[0, 0] = 0x7E
+    qc[3, 130] = 0x38                                           # +1.0 in block 1
+    qc[4, 131] = 0xB8                                           # -1.0 in block 1
+    sc = np.array([[1.0, 1.0625 + 2.0 ** -12]], np.float32)
+    q2, s_t = S.naive_resync(qc, sc)
+    codes, st, skip = _brute_naive(qc, sc)
+    assert s_t == np.float32(1.0) and st == 1
+    assert np.array_equal(q2.astype(np.int64), codes)
+    assert q2[3, 130] == 0x38 and q2[4, 131] == 0xB8            # bf16 midpoint -> even code 1.0
+    assert skip[3, 130] == 0x39 and skip[4, 131] == 0xB9        # without the bf16 step: 1.125
