@@ -87,7 +87,7 @@ KERNEL_SOURCES = {
     "dgrad": ("gemm.hip", "device.hpp"),
     "dgrad_pow2": ("gemm.hip", "device.hpp"),
     "mx_fwd": ("gemm.hip", "device.hpp"),
-    "decode_n24576": ("skinny.hip", "device.hpp"),
+    "decode_n24576": ("decode.hip", "device.hpp"),
     "grouped_gu": ("gemm.hip", "device.hpp"),
     "grouped_gu_block": ("gemm.hip", "device.hpp"),
     "install_gu": ("install.hip", "device.hpp"),
@@ -213,11 +213,11 @@ def decode_setup(torch, F, W, dev):
         wq, sw, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d[f"w{n}"]).to(dev))
         for st in sets:     # installed (rollout-owned) copies, identical bytes
             iq, is_ = torch.empty_like(wq), torch.empty_like(sw)
-            F.fp8_weight_install(wq, sw, iq, is_)
+            F.fp8_weight_install(wq, sw, iq, is_, layout=F.LAYOUT_DECODE)
             st[n] = (iq, is_)
         ys[n] = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
         del wq, sw
-    ws = torch.empty(F.fp8rl_fwd_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    ws = F.fwd_workspace(M, K, dev)
     timers = {f"decode_n{n}": EventTimer(torch) for n in W.DECODE_N}
     it = [0]
 
@@ -226,13 +226,13 @@ def decode_setup(torch, F, W, dev):
         it[0] += 1
         for n, (iq, is_) in st.items():
             if timed: timers[f"decode_n{n}"].start()
-            F.fp8_gemm_blockscaled_fwd(wq=iq, sw=is_, x_bf16=x, y=ys[n], workspace=ws)
+            F.fp8_gemm_blockscaled_fwd_decode_layout(wq=iq, sw=is_, x_bf16=x, N=n, K=K, y=ys[n], workspace=ws)
             if timed: timers[f"decode_n{n}"].stop()
 
     nmax = max(W.DECODE_N)
     info = dict(
         config={"workload": "decode_rollout", "rows_M": M, "K": K, "N": list(W.DECODE_N),
-                "activations": "bf16, quantized 1x128 inside the call", "weights": "installed E4M3 128x128",
+                "activations": "bf16, quantized 1x128 inside the call", "weights": "installed E4M3 128x128, decode layout (16x128 tiles in MFMA operand order)",
                 "weight_copies": n_sets},
         flops=sum(2.0 * M * n * K for n in W.DECODE_N),
         dominant=(f"decode_n{nmax}", "hbm", (nmax * K + nmax * K // 128 // 128 * 4) / 1e9, "GB/s", PEAK_HBM_GBS,

@@ -30,11 +30,14 @@ __all__ = [
     "fp8_gemm_blockscaled_pow2_dgrad", "fp8_gemm_blockscaled_pow2_wgrad",
     "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16", "fp8_rmsnorm_quant_1x128",
     "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad", "fp8_gemm_mxfp8_wgrad",
-    "fp8_quant_w_128x128_f32",
+    "fp8_quant_w_128x128_f32", "LAYOUT_ROWS", "LAYOUT_DECODE", "fp8_gemm_blockscaled_fwd_decode_layout",
+    "fwd_workspace",
 ]
 
 RECIPE_BLOCK128 = 0
 RECIPE_MXFP8 = 1
+LAYOUT_ROWS = 0
+LAYOUT_DECODE = 1
 OUT_BF16 = 0
 OUT_F32 = 1
 
@@ -49,7 +52,7 @@ _sz = ctypes.c_size_t
 
 
 class _Weight(ctypes.Structure):
-    _fields_ = [("recipe", _int), ("rows", _i64), ("cols", _i64), ("q", _vp), ("s", _vp)]
+    _fields_ = [("recipe", _int), ("rows", _i64), ("cols", _i64), ("q", _vp), ("s", _vp), ("layout", _int)]
 
 
 _SIGNATURES = {
@@ -60,6 +63,8 @@ _SIGNATURES = {
     "mxfp8_quant_1x32": ([_vp, _i64, _i64, _vp, _vp, _vp], _int),
     "fp8_gemm_blockscaled_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp], _int),
     "fp8rl_fwd_workspace_bytes": ([_i64, _i64], _sz),
+    "fp8_gemm_blockscaled_fwd_decode_layout": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp],
+                                               _int),
     "fp8_gemm_blockscaled_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_blockscaled_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_grouped_gemm": ([_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _int, _vp], _int),
@@ -380,13 +385,16 @@ def _odt(out_dtype):
     raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
 
 
-def fp8_gemm_blockscaled_fwd(xq=None, sx=None, wq=None, sw=None, *, x_bf16=None, out_dtype=torch.bfloat16, y=None,
-                             workspace=None):
-    """Y[M][N] = deq(X) deq(W)^T. X as (xq, sx) or, for the fused form, as x_bf16 (then a
-    workspace is allocated unless given)."""
+def fwd_workspace(M, K, device):
+    """A zeroed workspace for the bf16-input forward calls (its leading counters must start at
+    zero; every call leaves them zero, so one workspace serves any number of calls made one
+    after another on a stream)."""
+    nbytes = load_library().fp8rl_fwd_workspace_bytes(M, K)
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _fwd(fn, name, xq, sx, wq, sw, x_bf16, out_dtype, y, workspace, N, K):
     lib = load_library()
-    N, K = wq.shape
-    _need(wq, torch.uint8, (N, K), "wq")
     _need(sw, torch.float32, (N // 128, K // 128), "sw")
     dev = wq.device
     if x_bf16 is not None:
@@ -394,19 +402,37 @@ def fp8_gemm_blockscaled_fwd(xq=None, sx=None, wq=None, sw=None, *, x_bf16=None,
         _need(x_bf16, torch.bfloat16, (M, K), "x_bf16")
         if xq is not None or sx is not None:
             raise ValueError("give either (xq, sx) or x_bf16")
-        nbytes = lib.fp8rl_fwd_workspace_bytes(M, K)
         if workspace is None:
-            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+            workspace = fwd_workspace(M, K, dev)
     else:
         M = xq.shape[0]
         _need(xq, torch.uint8, (M, K), "xq")
         _need(sx, torch.float32, (M, K // 128), "sx")
     y = _out(y, out_dtype, (M, N), dev, "y")
     ws_bytes = workspace.numel() if workspace is not None else 0
-    _check(lib.fp8_gemm_blockscaled_fwd(_ptr(xq), _ptr(sx), _ptr(x_bf16), _ptr(wq), _ptr(sw), M, N, K, _ptr(y),
-                                        _odt(out_dtype), _ptr(workspace), ws_bytes, _stream(dev)),
-           "fp8_gemm_blockscaled_fwd")
+    _check(getattr(lib, fn)(_ptr(xq), _ptr(sx), _ptr(x_bf16), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _odt(out_dtype),
+                            _ptr(workspace), ws_bytes, _stream(dev)), name)
     return y
+
+
+def fp8_gemm_blockscaled_fwd(xq=None, sx=None, wq=None, sw=None, *, x_bf16=None, out_dtype=torch.bfloat16, y=None,
+                             workspace=None):
+    """Y[M][N] = deq(X) deq(W)^T. X as (xq, sx) or, for the fused form, as x_bf16 (then a
+    zeroed workspace is allocated unless given; see fwd_workspace)."""
+    N, K = wq.shape
+    _need(wq, torch.uint8, (N, K), "wq")
+    return _fwd("fp8_gemm_blockscaled_fwd", "fp8_gemm_blockscaled_fwd", xq, sx, wq, sw, x_bf16, out_dtype, y,
+                workspace, N, K)
+
+
+def fp8_gemm_blockscaled_fwd_decode_layout(xq=None, sx=None, wq=None, sw=None, *, N, K, x_bf16=None,
+                                           out_dtype=torch.bfloat16, y=None, workspace=None):
+    """The forward product with W's payload in the decode layout (fp8_weight_install with
+    layout=LAYOUT_DECODE): wq holds N * K bytes."""
+    if wq.dtype != torch.uint8 or not wq.is_cuda or not wq.is_contiguous() or wq.numel() != N * K:
+        raise ValueError(f"wq must be a contiguous GPU uint8 tensor of {N} * {K} bytes")
+    return _fwd("fp8_gemm_blockscaled_fwd_decode_layout", "fp8_gemm_blockscaled_fwd_decode_layout", xq, sx, wq, sw,
+                x_bf16, out_dtype, y, workspace, N, K)
 
 
 def fp8_gemm_blockscaled_pow2_fwd(xq, sx, wq, sw, *, out_dtype=torch.bfloat16, y=None):
@@ -496,8 +522,10 @@ def fp8_grouped_gemm(xq, sx, wq, sw, offsets, *, recipe=RECIPE_MXFP8, out_dtype=
     return y
 
 
-def fp8_weight_install(src_q, src_s, dst_q, dst_s, *, recipe=RECIPE_BLOCK128):
-    """Copy a quantized weight's payload and scales verbatim into the destination buffers."""
+def fp8_weight_install(src_q, src_s, dst_q, dst_s, *, recipe=RECIPE_BLOCK128, layout=LAYOUT_ROWS,
+                       src_layout=LAYOUT_ROWS):
+    """Install a quantized weight's payload and scales into the destination buffers, with no
+    quantizer: verbatim, or regrouped into the decode layout (layout=LAYOUT_DECODE)."""
     lib = load_library()
     rows = src_q.shape[0] if src_q.dim() == 2 else src_q.numel() // src_q.shape[-1]
     cols = src_q.shape[-1]
@@ -516,7 +544,7 @@ def fp8_weight_install(src_q, src_s, dst_q, dst_s, *, recipe=RECIPE_BLOCK128):
             need = 0
         if st_.numel() * st_.element_size() < need:
             raise ValueError(f"{name}_s holds {st_.numel() * st_.element_size()} bytes, the recipe needs {need}")
-    src = _Weight(recipe, rows, cols, src_q.data_ptr(), src_s.data_ptr())
-    dst = _Weight(recipe, drows, dst_q.shape[-1], dst_q.data_ptr(), dst_s.data_ptr())
+    src = _Weight(recipe, rows, cols, src_q.data_ptr(), src_s.data_ptr(), src_layout)
+    dst = _Weight(recipe, drows, dst_q.shape[-1], dst_q.data_ptr(), dst_s.data_ptr(), layout)
     _check(lib.fp8_weight_install(ctypes.byref(src), ctypes.byref(dst), _stream(src_q.device)), "fp8_weight_install")
     return dst_q, dst_s

@@ -236,16 +236,28 @@ fp8rl_status mxfp8_quant_act_1x32(const uint16_t* x, int64_t R, int64_t K, uint8
   return launched(launch_quant_mx_tile(x, R, K, q, e8m0, qt, e8m0t, as_stream(stream)));
 }
 
+// Forward workspace: 256 bytes of counters (fused decode form), then the quantized X
+// (row-major for the tiled GEMM, K-block-major for the decode kernel), then its scales.
+constexpr size_t kCtlBytes = 256;
+
 size_t fp8rl_fwd_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % 128 != 0 || check_dims(M, K) != FP8RL_OK) return 0;
   const size_t qbytes = (size_t)(M * K);
   const size_t qpad = (qbytes + 255) & ~(size_t)255;
-  return qpad + (size_t)M * (size_t)(K / 128) * sizeof(float);
+  return kCtlBytes + qpad + (size_t)M * (size_t)(K / 128) * sizeof(float);
 }
 
-fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const uint16_t* x_bf16, const uint8_t* wq,
-                                      const float* sw, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward product for both weight layouts. tiled_b: W in the decode layout (decode
+// kernel for every M). Otherwise M <= 256 goes to the decode kernel and larger M to the tiled
+// GEMM. A bf16 X is quantized inside the decode kernel's launch (K-block-major copy in the
+// workspace), or by the row quantizer before the tiled GEMM.
+fp8rl_status fwd_impl(const uint8_t* xq, const float* sx, const uint16_t* x_bf16, const uint8_t* wq, const float* sw,
+                      int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                      bool tiled_b, void* stream) {
   const bool quantized = xq != nullptr || sx != nullptr;
   if (quantized && (xq == nullptr || sx == nullptr)) return FP8RL_ERR_NULL;
   if (quantized == (x_bf16 != nullptr)) return FP8RL_ERR_NULL;  // exactly one form of X
@@ -256,6 +268,10 @@ fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const 
   if (fp8rl_status e = check_dims(M, N)) return e;
   if (K % 128 != 0 || N % 128 != 0) return FP8RL_ERR_SHAPE;
   if (fp8rl_status e = check_red(K)) return e;
+  const bool decode = tiled_b || M <= 256;
+  // The decode kernel addresses A and B with 32-bit offsets and counts rows in int32.
+  if (decode && (M * K >= ((int64_t)1 << 32) || N * K >= ((int64_t)1 << 32))) return FP8RL_ERR_SHAPE;
+  if (!quantized && M * K >= ((int64_t)1 << 32)) return FP8RL_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8RL_OK;
   if (K == 0) return FP8RL_ERR_SHAPE;  // the product would be all zeros; not a supported call
   if (!aligned(wq, 16) || !aligned(sw, 4) || !aligned(y, 16)) return FP8RL_ERR_ALIGN;
@@ -267,13 +283,48 @@ fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const 
   }
   if (fp8rl_status e = check_device()) return e;
   hipStream_t st = as_stream(stream);
+  uint8_t* wsq = nullptr;
+  float* wss = nullptr;
   if (!quantized) {
     const size_t qpad = ((size_t)(M * K) + 255) & ~(size_t)255;
-    uint8_t* wxq = static_cast<uint8_t*>(workspace);
-    float* wsx = reinterpret_cast<float*>(wxq + qpad);
-    if (launch_quant_rows_1x128(x_bf16, M, K, wxq, wsx, false, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
-    xq = wxq;
-    sx = wsx;
+    wsq = static_cast<uint8_t*>(workspace) + kCtlBytes;
+    wss = reinterpret_cast<float*>(wsq + qpad);
+  }
+  if (decode) {
+    DecodeParams d{};
+    d.B = wq;
+    d.sB = sw;
+    d.C = y;
+    d.M = M;
+    d.N = N;
+    d.K = K;
+    d.sb_ld_n = K / 128;
+    d.sb_ld_k = 1;
+    d.ldc = N;
+    d.tiled_b = tiled_b ? 1 : 0;
+    if (quantized) {
+      d.A = xq;
+      d.sA = sx;
+      d.a_ld = K;
+      d.a_kb = 128;
+      d.sa_ld = K / 128;
+      d.sa_kb = 1;
+    } else {
+      d.A = wsq;
+      d.sA = wss;
+      d.a_ld = 128;
+      d.a_kb = 128 * M;
+      d.sa_ld = 1;
+      d.sa_kb = M;
+      d.X = x_bf16;
+      d.ctl = static_cast<int*>(workspace);
+    }
+    return launched(launch_gemm_decode(d, y_dtype == FP8RL_OUT_F32, st));
+  }
+  if (!quantized) {
+    if (launch_quant_rows_1x128(x_bf16, M, K, wsq, wss, false, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
+    xq = wsq;
+    sx = wss;
   }
   GemmParams p{};
   p.A = xq;
@@ -290,6 +341,23 @@ fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const 
   p.ldc = N;
   p.accumulate = 0;
   return launched(launch_gemm_blockscaled(p, false, y_dtype == FP8RL_OUT_F32, false, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const uint16_t* x_bf16, const uint8_t* wq,
+                                      const float* sw, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(xq, sx, x_bf16, wq, sw, M, N, K, y, y_dtype, workspace, workspace_bytes, false, stream);
+}
+
+fp8rl_status fp8_gemm_blockscaled_fwd_decode_layout(const uint8_t* xq, const float* sx, const uint16_t* x_bf16,
+                                                    const uint8_t* wq, const float* sw, int64_t M, int64_t N,
+                                                    int64_t K, void* y, int y_dtype, void* workspace,
+                                                    size_t workspace_bytes, void* stream) {
+  return fwd_impl(xq, sx, x_bf16, wq, sw, M, N, K, y, y_dtype, workspace, workspace_bytes, true, stream);
 }
 
 fp8rl_status fp8_gemm_blockscaled_pow2_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
@@ -503,6 +571,12 @@ fp8rl_status fp8_grouped_gemm(int recipe, const uint8_t* xq, const void* sx, con
 fp8rl_status fp8_weight_install(const fp8rl_weight* src, const fp8rl_weight* dst, void* stream) {
   if (src == nullptr || dst == nullptr) return FP8RL_ERR_NULL;
   if (src->recipe != dst->recipe || src->rows != dst->rows || src->cols != dst->cols) return FP8RL_ERR_RECIPE;
+  if ((src->layout != FP8RL_LAYOUT_ROWS && src->layout != FP8RL_LAYOUT_DECODE) ||
+      (dst->layout != FP8RL_LAYOUT_ROWS && dst->layout != FP8RL_LAYOUT_DECODE))
+    return FP8RL_ERR_RECIPE;
+  // A decode-layout payload is never turned back into rows; MXFP8 has no decode layout.
+  if (src->layout == FP8RL_LAYOUT_DECODE && dst->layout != FP8RL_LAYOUT_DECODE) return FP8RL_ERR_RECIPE;
+  if (dst->layout == FP8RL_LAYOUT_DECODE && src->recipe != FP8RL_RECIPE_BLOCK128) return FP8RL_ERR_RECIPE;
   const int64_t rows = src->rows, cols = src->cols;
   if (fp8rl_status e = check_dims(rows, cols)) return e;
   int64_t sbytes;
@@ -520,8 +594,14 @@ fp8rl_status fp8_weight_install(const fp8rl_weight* src, const fp8rl_weight* dst
   if (!aligned(src->q, 16) || !aligned(dst->q, 16) || !aligned(src->s, 4) || !aligned(dst->s, 4))
     return FP8RL_ERR_ALIGN;
   if (fp8rl_status e = check_device()) return e;
-  return launched(launch_copy(src->q, dst->q, rows * cols, static_cast<const uint8_t*>(src->s),
-                              static_cast<uint8_t*>(dst->s), sbytes, as_stream(stream)));
+  hipStream_t st = as_stream(stream);
+  if (src->layout == dst->layout)
+    return launched(launch_copy(src->q, dst->q, rows * cols, static_cast<const uint8_t*>(src->s),
+                                static_cast<uint8_t*>(dst->s), sbytes, st));
+  // Rows -> decode layout: the payload is regrouped, the scales copied verbatim.
+  if (launch_decode_layout(src->q, dst->q, rows, cols, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
+  return launched(launch_copy(nullptr, nullptr, 0, static_cast<const uint8_t*>(src->s),
+                              static_cast<uint8_t*>(dst->s), sbytes, st));
 }
 
 }  // extern "C"

@@ -1,0 +1,484 @@
+// Block-scaled FP8 GEMM for the decode shape: few activation rows (256 token rows in the
+// rollout) against a large installed weight, where the weight stream from HBM sets the
+// pace ([SkyRL-FP8] "Performance analysis": generation is memory-bound on the weight reads,
+// activations are quantized on the fly while weights and scales stay fixed; activation
+// groups 1x128 and weight blocks 128x128, as for the training GEMMs).
+//   C[m][n] = sum_kb sA(m, kb) * sB[(n / 128) * sb_ld_n + kb * sb_ld_k]
+//             * sum_{k in kb} A(m, k) * B(n, k)
+// A (the quantized activations) is addressed with a row stride and a K-block stride, so it
+// may be row-major ([M][K]: strides K and 128) or K-block-major ([K/128][M][128]: strides
+// 128 and 128 M, each K block's slice contiguous); its scales likewise.
+// B is row-major [N][K], or in the decode layout (see k_decode_layout below): every
+// 16-row x 128-byte tile stored in the order the matrix instruction reads it, so that every
+// load instruction of the weight stream reads 1 KB of consecutive bytes.
+//
+// Design (gfx950):
+// * Every weight byte is used by exactly one wave, so the weights bypass LDS: wave w loads
+//   its FW 16-row fragments of B for K block kb straight into VGPRs (two 16-byte buffer
+//   loads per lane and fragment, in the operand layout of the MFMA), P K blocks ahead of
+//   the block it computes.
+// * The activations are shared by all waves of the workgroup: the MT x 128 bytes of A and
+//   the MT row scales of K block kb go to LDS by direct global->LDS copies, into one of P + 1
+//   stages, also P K blocks ahead; so are the F = NW FW fragment scales of B.
+// * Workgroup = MT rows (a row part) x a run of F fragments; a launch has ceil(M / MT) row
+//   parts times N / (16 F) runs. Consecutive workgroups b go to XCD b % 8; the row parts of a
+//   run share an XCD and run together, so B comes from HBM once and from that XCD's L2 for
+//   the other row parts.
+// * One v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0 scales) per 16x16 tile and K block,
+//   computed transposed (first operand: 16 rows of B, second: 16 rows of A), so a lane's four
+//   outputs share one row m and one 128-row block of B; its fp32 product is folded into the
+//   accumulator with one FMA per output, kLag MFMAs after it was issued.
+// * K loop: wait for this wave's loads of kb (those of kb+1 .. kb+P-1 stay in flight),
+//   barrier (every wave's copies of kb landed; every wave is done with kb-1, whose stage and
+//   register set are refilled next), issue kb+P, compute kb. Past the last K block the loads
+//   go through empty descriptors (zeros, no memory access), so every step counts the same.
+// * Fused activation quantization (bf16 X): the workgroups of the launch first take K
+//   blocks of X from a counter in the workspace, one at a time, and quantize each (all M
+//   rows, 1x128 groups) into the K-block-major workspace copy, publishing it with a release
+//   fence and a second counter; a workgroup that finds every K block taken starts its weight
+//   prefetch, then waits until all K blocks are published (acquire) and runs the K loop on
+//   the workspace copy. A workgroup only ever waits for work that a running workgroup has
+//   already taken, so the launch completes whatever the occupancy; the wait is bounded.
+//   The last workgroup to finish resets the counters, so every call leaves them zero.
+// Deterministic: fixed K order; the only atomics are the workspace counters.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace fp8rl {
+
+namespace {
+
+constexpr int kDecodeLag = 3;
+// Bounded wait for the published activation blocks: iterations of a 256-cycle sleep
+// (about 0.1 s at 2 GHz; the quantization itself takes microseconds).
+constexpr int kPublishSpins = 1 << 20;
+
+// Buffer load of 16 bytes per lane into VGPRs. Issued as inline assembly so that the compiler
+// neither inserts its own vmcnt waits (which would count the direct-to-LDS copies wrongly)
+// nor schedules a use before the explicit wait: the consumer waits with wait_vmem_n<>() and
+// then hold()s the value. The s_nop 4 gives the 5 wait states a buffer instruction needs
+// after a VALU write of its descriptor SGPRs, which the compiler cannot insert into asm.
+__device__ __forceinline__ v4i bload16(v4i rsrc, uint32_t voff) {
+  v4i r;
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc) : "memory");
+  return r;
+}
+
+template <int MT, int NW, int FW, int P>
+struct DecodeShape {
+  static constexpr int NT = NW * 64;
+  static constexpr int F = NW * FW;                  // B fragments per workgroup
+  static constexpr int BN = 16 * F;
+  static constexpr int XF = MT / 16;                 // A fragments
+  static constexpr int NS = P + 1;                   // stages / register sets
+  static constexpr int LX = MT * 8 / NT;             // A copies (16 B per lane) per wave per K block
+  static constexpr int OFF_SA = MT * 128;
+  static constexpr int OFF_SB = OFF_SA + MT * 4;
+  static constexpr int STAGE = OFF_SB + 256;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int SA_WAVES = (MT + 63) / 64;    // waves that copy A's row scales
+  static constexpr int SB_WAVE = SA_WAVES % NW;      // the wave that copies B's fragment scales
+  static_assert(MT % 64 == 0 && MT <= 256, "row part");
+  static_assert((MT * 8) % NT == 0 && (NT / 8) % 16 == 0, "A copy split keeps the swizzle phase");
+  static_assert(F <= 64, "one B fragment scale per lane");
+  static_assert(P >= 1 && P <= 8, "prefetch distance");
+};
+
+// 1x128 quantization of K block kb of bf16 X[M][K] (all M rows) into the K-block-major
+// copy: group (m, kb) -> payload q[(kb M + m) * 128 ..], scale s[kb M + m]. 8 lanes per
+// group, 16 elements each; 256 threads cover 32 rows per pass. Bytes and scales equal
+// those of the row-major 1x128 quantizer ([AIS] quantizer equation; [Jet-RL] 1x128 groups).
+__device__ __forceinline__ void quant_kblock(const uint16_t* __restrict__ x, int M, int64_t K, int kb,
+                                             uint8_t* __restrict__ q, float* __restrict__ s, int tid) {
+  const int part = tid & 7;
+  for (int r0 = 0; r0 < M; r0 += 32) {
+    const int m = r0 + (tid >> 3);
+    const bool valid = m < M;
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + (int64_t)kb * 128 + part * 16);
+      a = src[0];
+      b = src[1];
+    }
+    float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
+                       fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const BlockScale bs = block_scale(amax);
+    if (valid) {
+      const int64_t g = (int64_t)kb * M + m;
+      const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
+      const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
+      *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      if (part == 0) s[g] = bs.s;
+    }
+  }
+}
+
+}  // namespace
+
+// kFused: X arrives as bf16 (p.X) and is quantized inside the launch into p.A / p.sA
+// (K-block-major), synchronised through p.ctl. kTiledB: B is in the decode layout.
+template <int MT, int NW, int FW, int P, bool kF32, bool kFused, bool kTiledB>
+__global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
+  using S = DecodeShape<MT, NW, FW, P>;
+  constexpr int NT = S::NT, XF = S::XF, NS = S::NS, LX = S::LX;
+  static_assert(S::LDS <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
+  __shared__ int s_claim;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = (int)p.M;
+  const int64_t N = p.N, K = p.K;
+  const int nkb = (int)(K / 128);
+  const int ms = (M + MT - 1) / MT;
+  const int q8 = (int)(blockIdx.x >> 3);
+  const int mpart = q8 % ms, run = (q8 / ms) * 8 + (int)(blockIdx.x & 7);
+  const int64_t n0 = (int64_t)run * S::BN;
+  const int m0 = mpart * MT;
+  const bool active = n0 < N;                          // uniform: padding workgroups only help quantize
+
+  if constexpr (kFused) {
+    // Quantize K blocks of X until every one has been taken. Thread 0 publishes a block and
+    // claims the next one in a single branch that a barrier closes, and the claimed index is
+    // read back wave-uniform, so the loop runs in lockstep for every lane: with one branch on
+    // thread 0 before the back-edge (publish) and another after it (claim), the compiler may
+    // route the other lanes straight back to the barrier past both, and they then loop on a
+    // stale claim while thread 0 waits for them.
+    if (tid == 0) s_claim = atomicAdd(&p.ctl[0], 1);
+    __syncthreads();
+    int c = __builtin_amdgcn_readfirstlane(s_claim);
+    while (c < nkb) {
+      quant_kblock(p.X, M, K, c, const_cast<uint8_t*>(p.A), const_cast<float*>(p.sA), tid);
+      __threadfence();                                 // release this thread's stores (device scope)
+      __syncthreads();                                 // ... and every thread has read s_claim
+      if (tid == 0) {
+        atomicAdd(&p.ctl[1], 1);                       // publish K block c
+        s_claim = atomicAdd(&p.ctl[0], 1);             // take the next one
+      }
+      __syncthreads();
+      c = __builtin_amdgcn_readfirstlane(s_claim);
+    }
+  }
+
+  const int64_t rows_b = active ? ((N - n0) < S::BN ? (N - n0) : S::BN) : 16;
+  const int fvalid = (int)(rows_b / 16);
+
+  // A copies: thread t moves 16 bytes of tile row t/8 (+ NT/8 per copy), LDS chunk t%8,
+  // global chunk swz(row, t%8) (see frag_offsets). Rows past M read zeros (row-major) or
+  // another K block's rows (K-block-major); their results are never stored.
+  const int lr = tid >> 3;
+  const uint32_t offA = (uint32_t)((int64_t)(m0 + lr) * p.a_ld) + (uint32_t)(swz(lr, tid & 7) << 4);
+  const uint64_t a_total = (uint64_t)M * (uint64_t)K;
+  // A's row scales: wave w < SA_WAVES copies rows 64 w + lane.
+  const bool cA = wave < S::SA_WAVES;
+  const uint32_t offSA = (uint32_t)((int64_t)(m0 + (wave & 3) * 64 + lane) * p.sa_ld * 4);
+  const uint64_t sa_total = (uint64_t)M * (uint64_t)nkb * 4;
+  // B's fragment scales: lane f holds fragment f's block scale (lanes past the last valid
+  // fragment repeat it).
+  const bool cB = wave == S::SB_WAVE;
+  const int fl = lane < fvalid ? lane : fvalid - 1;
+  const uint32_t offSB = (uint32_t)((((active ? n0 : 0) + 16 * fl) >> 7) * p.sb_ld_n * 4);
+  const uint64_t sb_total = (uint64_t)(((N - 1) >> 7) * p.sb_ld_n + (int64_t)(nkb - 1) * p.sb_ld_k + 1) * 4;
+  // B fragments. Row-major: lane l reads row (l & 15) of the fragment, bytes 16 g and
+  // 64 + 16 g of the K block (g = l >> 4), the operand layout of the MFMA. Decode layout:
+  // the fragment's tile for K block kb is 2 KB at (fragment * nkb + kb) * 2048; lane l reads
+  // bytes 16 l (first half) and 1024 + 16 l (second half).
+  const uint32_t offB = kTiledB ? (uint32_t)((int64_t)wave * FW * 16 * K + 16 * lane)
+                                : (uint32_t)((int64_t)(wave * FW * 16 + (lane & 15)) * K + 16 * (lane >> 4));
+  const uint32_t bytesB = (uint32_t)(kTiledB ? rows_b * K : (rows_b - 1) * K + 128);
+  const uint8_t* Bp = p.B + (active ? n0 : 0) * K;
+
+  auto rng = [](uint64_t total, uint64_t used) __attribute__((always_inline)) -> uint32_t {
+    const uint64_t r = total - used;
+    return r > 0xffffffffull ? 0xffffffffu : (uint32_t)r;
+  };
+
+  v4i wlo[NS][FW], whi[NS][FW];
+  // The weight loads of K block kb into register set `set`.
+  auto issue_b = [&](int kb, auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
+    const bool live = kb < nkb;
+    const int kbc = live ? kb : 0;
+    const v4i rb = make_rsrc(Bp + (kTiledB ? 0 : kbc * 128), live ? bytesB : 0u);
+    const uint32_t ok = kTiledB ? (uint32_t)kbc * 2048u : 0u;
+#pragma unroll
+    for (int i = 0; i < FW; ++i) {
+      const uint32_t o = offB + ok + (uint32_t)(i * 16) * (uint32_t)K;
+      wlo[set][i] = bload16(rb, o);
+      whi[set][i] = bload16(rb, o + (kTiledB ? 1024u : 64u));
+    }
+  };
+  // The activation and scale copies of K block kb into stage `set`.
+  auto issue_a = [&](int kb, auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
+    const uint32_t st = lds_addr(smem) + set * S::STAGE;
+    const bool live = kb < nkb;
+    const int64_t kbc = live ? kb : 0;
+    const v4i ra = make_rsrc(p.A + kbc * p.a_kb, live ? rng(a_total, (uint64_t)(kbc * p.a_kb)) : 0u);
+#pragma unroll
+    for (int it = 0; it < LX; ++it)
+      dma16(ra, offA + (uint32_t)(it * (NT / 8)) * (uint32_t)p.a_ld, st + (it * NT + wave * 64) * 16);
+    if (cA)
+      dma4(make_rsrc(p.sA + kbc * p.sa_kb, live ? rng(sa_total, (uint64_t)(kbc * p.sa_kb) * 4) : 0u), offSA,
+           st + S::OFF_SA + wave * 256);
+    if (cB)
+      dma4(make_rsrc(p.sB + kbc * p.sb_ld_k, live ? rng(sb_total, (uint64_t)(kbc * p.sb_ld_k) * 4) : 0u), offSB,
+           st + S::OFF_SB);
+  };
+  // Vector-memory operations per K block of this wave: LX + (cA) + (cB) + 2 FW; at the wait
+  // of K block kb, those of kb+1 .. kb+P-1 may stay outstanding.
+  constexpr int LBASE = LX + 2 * FW;
+  const int cnt = (cA ? 1 : 0) + (cB ? 1 : 0);
+  auto wait_block = [&]() __attribute__((always_inline)) {
+    if (cnt == 0) wait_vmem_n<(P - 1) * LBASE>();
+    else if (cnt == 1) wait_vmem_n<(P - 1) * (LBASE + 1)>();
+    else wait_vmem_n<(P - 1) * (LBASE + 2)>();
+  };
+
+  v4f acc[FW][XF];
+#pragma unroll
+  for (int i = 0; i < FW; ++i)
+#pragma unroll
+    for (int j = 0; j < XF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const FragOffsets fa = frag_offsets(0, lane);
+  const uint32_t o_sa = S::OFF_SA + (lane & 15) * 4;
+
+  auto compute = [&](auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
+    const uint32_t st = lds_addr(smem) + set * S::STAGE;
+    const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi, sa_ad = st + o_sa;
+    const uint32_t sb_ad = st + S::OFF_SB + wave * FW * 4;
+    float sb[FW];
+    static_for<0, FW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      sb[i] = ds_read4f<i * 4>(sb_ad);
+    });
+    v4i xlo = ds_read16<0>(a_lo), xhi = ds_read16<0>(a_hi);
+    float sx = ds_read4f<0>(sa_ad);
+    lds_wait<0>();
+    v8i bf[FW];
+    static_for<0, FW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      hold(sb[i]);
+      hold(wlo[set][i]);
+      hold(whi[set][i]);
+      bf[i] = join(wlo[set][i], whi[set][i]);
+    });
+    hold(xlo);
+    hold(xhi);
+    hold(sx);
+    v4f pipe[kDecodeLag + 1];
+    float prod[kDecodeLag + 1];
+    auto fold = [&](int u) __attribute__((always_inline)) {
+      const int j = u / FW, i = u % FW;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[i][j][r] = __builtin_fmaf(pipe[u % (kDecodeLag + 1)][r], prod[u % (kDecodeLag + 1)], acc[i][j][r]);
+    };
+    static_for<0, XF>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      v4i nlo, nhi;
+      float nsx = 0.f;
+      if constexpr (j + 1 < XF) {
+        nlo = ds_read16<(j + 1) * 2048>(a_lo);
+        nhi = ds_read16<(j + 1) * 2048>(a_hi);
+        nsx = ds_read4f<(j + 1) * 64>(sa_ad);
+      }
+      const v8i xf = join(xlo, xhi);
+#pragma unroll
+      for (int i = 0; i < FW; ++i) {
+        const int t = j * FW + i;
+        pipe[t % (kDecodeLag + 1)] = mfma_fp8(bf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
+        prod[t % (kDecodeLag + 1)] = sx * sb[i];
+        if (t >= kDecodeLag) fold(t - kDecodeLag);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (j + 1 < XF) {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait<0>();
+        hold(nlo);
+        hold(nhi);
+        hold(nsx);
+        xlo = nlo;
+        xhi = nhi;
+        sx = nsx;
+      }
+    });
+#pragma unroll
+    for (int u = (XF * FW > kDecodeLag ? XF * FW - kDecodeLag : 0); u < XF * FW; ++u) fold(u);
+  };
+
+  if (active) {
+    // Prologue: weights of K blocks 0 .. P-1 first (they do not depend on the activations),
+    // then, once the activation copy is complete, its copies. The first step waits for all.
+    static_for<0, P>([&](auto sc) { issue_b(decltype(sc)::value, sc); });
+    if constexpr (kFused) {
+      if (tid == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(&p.ctl[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < nkb) {
+          if (++spins > kPublishSpins) {
+            atomicOr(&p.ctl[3], 1);                    // give up waiting; the output is not valid
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      __syncthreads();
+      __threadfence();                                 // acquire: later reads see the published blocks
+    }
+    static_for<0, P>([&](auto sc) { issue_a(decltype(sc)::value, sc); });
+    for (int kb0 = 0; kb0 < nkb; kb0 += NS) {
+      static_for<0, NS>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        const int kb = kb0 + s;
+        if (kb < nkb) {
+          if (kb == 0) wait_vmem();
+          else wait_block();
+          __syncthreads();
+          constexpr auto nxt = std::integral_constant<int, (s + P) % NS>{};
+          issue_a(kb + P, nxt);
+          issue_b(kb + P, nxt);
+          compute(sc);
+        }
+      });
+    }
+    wait_vmem();      // the empty loads issued past the last K block
+    // Those loads have no consumer, so without a use after the wait the compiler could give
+    // their destination registers to epilogue arithmetic placed ahead of the wait, which the
+    // arriving zeros would then overwrite.
+    static_for<0, NS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+#pragma unroll
+      for (int i = 0; i < FW; ++i) {
+        hold(wlo[s][i]);
+        hold(whi[s][i]);
+      }
+    });
+
+    // Epilogue: lane holds C[m][n .. n+3] for m = m0 + 16 j + (lane & 15) and
+    // n = n0 + 16 (wave FW + i) + 4 (lane >> 4).
+#pragma unroll
+    for (int j = 0; j < XF; ++j) {
+      const int m = m0 + 16 * j + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < FW; ++i) {
+        const int64_t n = n0 + 16 * (wave * FW + i) + 4 * (lane >> 4);
+        if (n >= N) continue;
+        if constexpr (kF32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n) =
+              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        } else {
+          uint2 v;
+          v.x = f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16);
+          v.y = f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = v;
+        }
+      }
+    }
+  }
+
+  if constexpr (kFused) {
+    // The last workgroup to finish resets the counters for the next call. Its increment is
+    // acquire-release, so this workgroup's own counter updates are complete before it counts.
+    __syncthreads();
+    if (tid == 0 &&
+        __hip_atomic_fetch_add(&p.ctl[2], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+      __hip_atomic_store(&p.ctl[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl[3], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Decode layout of a row-major FP8 weight W[N][K] (N % 16 == 0, K % 128 == 0): for 16-row
+// fragment f and K block kb, the 2 KB tile at (f * (K / 128) + kb) * 2048 holds, for lane
+// l = 0..63, row 16 f + (l & 15), bytes kb * 128 + 16 (l >> 4) .. + 15 at 16 l and bytes
+// kb * 128 + 64 + 16 (l >> 4) .. + 15 at 1024 + 16 l. A permutation of each fragment's
+// 16 K bytes: the values are the trainer's bytes, unchanged. Thread t moves 16 bytes.
+__global__ __launch_bounds__(256) void k_decode_layout(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                       int64_t N, int64_t K) {
+  const int64_t nkb = K / 128;
+  const int64_t chunks = N * K / 16;
+  for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < chunks; d += (int64_t)gridDim.x * 256) {
+    const int64_t tile = d >> 7;                       // 128 chunks of 16 bytes per tile
+    const int in = (int)(d & 127), h = in >> 6, l = in & 63;
+    const int64_t f = tile / nkb, kb = tile - f * nkb;
+    const uint4* s = reinterpret_cast<const uint4*>(src + (f * 16 + (l & 15)) * K + kb * 128 + h * 64 + 16 * (l >> 4));
+    reinterpret_cast<uint4*>(dst)[d] = *s;
+  }
+}
+
+hipError_t launch_decode_layout(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t chunks = N * K / 16;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_decode_layout, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, N, K);
+  return hipGetLastError();
+}
+
+template <int MT, int NW, int FW, int P>
+static hipError_t launch_decode_cfg(const DecodeParams& p, bool f32, hipStream_t stream) {
+  using S = DecodeShape<MT, NW, FW, P>;
+  const int64_t runs = (p.N + S::BN - 1) / S::BN, ms = (p.M + MT - 1) / MT;
+  const int64_t blocks = (runs + 7) / 8 * 8 * ms;
+  if (blocks > 0x7fffffff || p.M > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 g((unsigned)blocks), b(NW * 64);
+  const bool fused = p.ctl != nullptr;
+#define FP8RL_DECODE_LAUNCH(F32, FUSED, TILED) \
+  hipLaunchKernelGGL((k_gemm_decode<MT, NW, FW, P, F32, FUSED, TILED>), g, b, 0, stream, p)
+  if (f32) {
+    if (fused) {
+      if (p.tiled_b) FP8RL_DECODE_LAUNCH(true, true, true); else FP8RL_DECODE_LAUNCH(true, true, false);
+    } else {
+      if (p.tiled_b) FP8RL_DECODE_LAUNCH(true, false, true); else FP8RL_DECODE_LAUNCH(true, false, false);
+    }
+  } else {
+    if (fused) {
+      if (p.tiled_b) FP8RL_DECODE_LAUNCH(false, true, true); else FP8RL_DECODE_LAUNCH(false, true, false);
+    } else {
+      if (p.tiled_b) FP8RL_DECODE_LAUNCH(false, false, true); else FP8RL_DECODE_LAUNCH(false, false, false);
+    }
+  }
+#undef FP8RL_DECODE_LAUNCH
+  return hipGetLastError();
+}
+
+struct DecodeCfg {
+  int mt, fw, p;
+  hipError_t (*launch)(const DecodeParams&, bool, hipStream_t);
+};
+// 4 waves per workgroup; (row part, fragments per wave, prefetch distance).
+static const DecodeCfg kDecodeCfgs[] = {
+    {128, 3, 2, launch_decode_cfg<128, 4, 3, 2>}, {128, 2, 3, launch_decode_cfg<128, 4, 2, 3>},
+    {128, 1, 4, launch_decode_cfg<128, 4, 1, 4>}, {64, 3, 3, launch_decode_cfg<64, 4, 3, 3>},
+    {64, 2, 4, launch_decode_cfg<64, 4, 2, 4>},   {64, 1, 6, launch_decode_cfg<64, 4, 1, 6>},
+    {256, 2, 2, launch_decode_cfg<256, 4, 2, 2>}, {256, 1, 3, launch_decode_cfg<256, 4, 1, 3>},
+};
+
+// Choice: the fewest rounds of 256 workgroups, then the least data per CU and K block
+// (MT rows of A copied into LDS + 16 F rows of B loaded), then the larger row part.
+hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t stream) {
+  const DecodeCfg* best = nullptr;
+  int64_t best_rounds = 0, best_bytes = 0;
+  for (const DecodeCfg& c : kDecodeCfgs) {
+    const int64_t ms = (p.M + c.mt - 1) / c.mt;
+    const int64_t runs = (p.N + 64 * c.fw - 1) / (64 * c.fw);
+    const int64_t rounds = (ms * runs + 255) / 256;
+    const int64_t rows = (p.M < c.mt ? p.M : c.mt) + 64 * c.fw;
+    if (best == nullptr || rounds < best_rounds || (rounds == best_rounds && rows * rounds < best_bytes)) {
+      best = &c;
+      best_rounds = rounds;
+      best_bytes = rows * rounds;
+    }
+  }
+  return best->launch(p, f32, stream);
+}
+
+}  // namespace fp8rl

@@ -130,12 +130,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // instruction takes its LDS address in m0, which the asm sets and declares clobbered
 // (the compiler warns that m0 is reserved); gfx950 code needs m0 for nothing else here,
 // and the generated kernels contain no other access to it.
+// Wait states (CDNA3/CDNA4 ISA, manually inserted wait states): a buffer instruction that
+// reads an SGPR needs 5 wait states after a VALU instruction wrote that SGPR (the compiler
+// often rebuilds a descriptor with v_readfirstlane right before the asm), and a copy to LDS
+// needs 1 after an SALU write of m0. The compiler's hazard pass cannot see inside an asm
+// statement, so every asm buffer instruction here pays for both itself: the s_nop 4 after
+// the m0 write (or in front of the load) supplies the wait states. Without them the load may
+// use the previous descriptor or m0, i.e. read another buffer or write another LDS slot.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
 
@@ -149,6 +156,7 @@ __device__ __forceinline__ void dma16_if(v4i rsrc, uint32_t voff, uint32_t lds, 
       "s_cmp_eq_u32 %3, 0\n\t"
       "s_cbranch_scc1 1f\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds\n"
       "1:"
       :

@@ -568,11 +568,29 @@ static hipError_t launch_cfg(const GemmParams& p, bool f32, hipStream_t stream) 
   return launch_sk<BM, BN, WM, WN, kRowB, kScale, 1>(p, f32, tiles, stream);
 }
 
-// Tile choice: at most 256 rows with block-scaled fp32 scales go to the few-row kernel (skinny.hip);
-// otherwise 256x256 tiles (8 waves, 64x128 per wave) when there are enough of them to fill
-// the 256 CUs, else 128x128 tiles (4 waves, 64x64 per wave).
+// Tile choice: at most 256 rows with block-scaled fp32 scales go to the decode kernel
+// (decode.hip; A row-major); otherwise 256x256 tiles (8 waves, 64x128 per wave) when there
+// are enough of them to fill the 256 CUs, else 128x128 tiles (4 waves, 64x64 per wave).
 hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, bool pow2, hipStream_t stream) {
-  if (!pow2 && !row_scale_b && p.M <= 256) return launch_gemm_skinny(p, f32, stream);
+  if (!pow2 && !row_scale_b && p.M <= 256 && !p.accumulate) {
+    DecodeParams d{};
+    d.A = p.A;
+    d.sA = p.sA;
+    d.B = p.B;
+    d.sB = p.sB;
+    d.C = p.C;
+    d.M = p.M;
+    d.N = p.N;
+    d.K = p.K;
+    d.a_ld = p.K;
+    d.a_kb = 128;
+    d.sa_ld = p.sa_ld;
+    d.sa_kb = 1;
+    d.sb_ld_n = p.sb_ld_n;
+    d.sb_ld_k = p.sb_ld_k;
+    d.ldc = p.ldc;
+    return launch_gemm_decode(d, f32, stream);
+  }
   const int64_t big_tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   const bool big = big_tiles >= 256;
   if (pow2) {

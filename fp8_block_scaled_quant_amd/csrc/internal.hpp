@@ -55,8 +55,30 @@ struct GemmParams {
 hipError_t launch_gemm_blockscaled(const GemmParams& p, bool row_scale_b, bool f32, bool pow2, hipStream_t stream);
 // MXFP8 TN GEMM: sA / sB are E8M0 bytes [rows][K/32] (passed as float* to dwords of 4 bytes).
 hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream);
-// Few-row form (M <= 256, block-scaled B only): all rows per workgroup, one workgroup per CU.
-hipError_t launch_gemm_skinny(const GemmParams& p, bool f32, hipStream_t stream);
+// Few-row forward GEMM (decode.hip), M <= 256, block-scaled B [N][K] with fp32 scales
+// sB[(n / 128) * sb_ld_n + kb * sb_ld_k]. A is addressed through strides: element (m, k) at
+// A[m * a_ld + (k / 128) * a_kb + k % 128], its scale at sA[m * sa_ld + (k / 128) * sa_kb];
+// row-major A: (a_ld, a_kb) = (K, 128), (sa_ld, sa_kb) = (K / 128, 1); K-block-major:
+// (128, 128 M) and (1, M). C [M][ldc], bf16 or fp32 (no accumulation).
+// Fused form (ctl != NULL): X is bf16 [M][K] (row-major) and the launch quantizes it into A /
+// sA (K-block-major, which A / sA and the strides must then describe), synchronised through
+// the four int32 counters at ctl, zero on entry and left zero. tiled_b: B in the decode
+// layout (launch_decode_layout) instead of row-major.
+struct DecodeParams {
+  const uint8_t* A;
+  const float* sA;
+  const uint8_t* B;
+  const float* sB;
+  void* C;
+  int64_t M, N, K;
+  int64_t a_ld, a_kb, sa_ld, sa_kb, sb_ld_n, sb_ld_k, ldc;
+  const uint16_t* X;
+  int* ctl;
+  int tiled_b;
+};
+hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t stream);
+// Row-major FP8 weight [N][K] -> decode layout (decode.hip), N % 16 == 0, K % 128 == 0.
+hipError_t launch_decode_layout(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K, hipStream_t stream);
 
 // Scales: MXFP8 = E8M0 bytes Xs [T][K/32], Ws [E][N][K/32]; blockwise = fp32
 // Xs [T][K/128] (1x128 groups), Ws [E][N/128][K/128] (128x128 blocks per expert).

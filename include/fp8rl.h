@@ -67,8 +67,14 @@ typedef enum {
   FP8RL_OUT_F32 = 1
 } fp8rl_out;
 
+/* Payload layouts of an installed weight (see fp8_weight_install). */
+typedef enum {
+  FP8RL_LAYOUT_ROWS = 0,       /* row-major [rows][cols]: the layout every quantizer writes */
+  FP8RL_LAYOUT_DECODE = 1      /* BLOCK128 only: the same bytes regrouped for the decode GEMM */
+} fp8rl_layout;
+
 /* ABI version of this header. */
-#define FP8RL_ABI_VERSION 5
+#define FP8RL_ABI_VERSION 6
 int fp8rl_abi_version(void);
 const char* fp8rl_status_str(fp8rl_status status);
 
@@ -202,13 +208,29 @@ fp8rl_status fp8_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, i
  *   y: [M][N], bf16 or fp32 per y_dtype.
  *   workspace/workspace_bytes: only for the bf16-input form; at least
  *   fp8rl_fwd_workspace_bytes(M, K) bytes, 16-byte aligned. Ignored otherwise (may be NULL).
- * Rules: K % 128 == 0, N % 128 == 0, M >= 0 (any M). */
+ *   Its first 256 bytes hold counters through which the workgroups of one launch share the
+ *   quantization of X (M <= 256: quantization and GEMM are a single kernel launch); they must
+ *   be zero before the first call on a workspace (allocate it zeroed) and every call leaves
+ *   them zero. Calls that run at the same time must not share a workspace.
+ * Rules: K % 128 == 0, N % 128 == 0, M >= 0 (any M); M * K < 2^32 for the bf16-input form. */
 fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const uint16_t* x_bf16,
                                       const uint8_t* wq, const float* sw,
                                       int64_t M, int64_t N, int64_t K,
                                       void* y, int y_dtype,
                                       void* workspace, size_t workspace_bytes, void* stream);
 size_t fp8rl_fwd_workspace_bytes(int64_t M, int64_t K);
+
+/* Forward with the weight in the decode layout (FP8RL_LAYOUT_DECODE, written by
+ * fp8_weight_install): the same product, arguments and rules as fp8_gemm_blockscaled_fwd,
+ * with wq the decode-layout payload of W[N][K] (N * K bytes) and sw W's block scales
+ * [N/128][K/128]. The output is bit-identical to fp8_gemm_blockscaled_fwd on the row-major
+ * payload for M <= 256. Made for decode-shaped calls (few rows, weight-stream bound); any M
+ * is accepted. Extra rule: M * K < 2^32 and N * K < 2^32. */
+fp8rl_status fp8_gemm_blockscaled_fwd_decode_layout(const uint8_t* xq, const float* sx, const uint16_t* x_bf16,
+                                                    const uint8_t* wq, const float* sw,
+                                                    int64_t M, int64_t N, int64_t K,
+                                                    void* y, int y_dtype,
+                                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* DGrad: dX[M][K] = deq(dY) . deq(W)  ([Jet-RL] "Quantization scheme": DGrad in FP8).
  *   dyq uint8 [M][N], sdy fp32 [M][N/128]  (dY quantized 1x128 along N)
@@ -303,14 +325,24 @@ typedef struct {
   int recipe;        /* fp8rl_recipe */
   int64_t rows;      /* N (for MXFP8 expert stacks: E*N) */
   int64_t cols;      /* K */
-  uint8_t* q;        /* payload uint8 [rows][cols] */
+  uint8_t* q;        /* payload, rows * cols bytes in the descriptor's layout */
   void* s;           /* BLOCK128: fp32 [rows/128][cols/128];  MXFP8: E8M0 uint8 [rows][cols/32] */
+  int layout;        /* fp8rl_layout of q (FP8RL_LAYOUT_ROWS = 0 when zero-initialised) */
 } fp8rl_weight;
 
-/* Copies src's payload and scales verbatim into dst's buffers. The descriptors must agree
- * on recipe, rows and cols (FP8RL_ERR_RECIPE otherwise: the library never requantizes).
- * Rules: BLOCK128: rows % 128 == 0, cols % 128 == 0; MXFP8: cols % 32 == 0. src and dst
- * buffers must not overlap. */
+/* Installs src's payload and scales into dst's buffers without any quantizer: the scales
+ * are copied verbatim, and so is the payload when both layouts agree. With src row-major
+ * and dst FP8RL_LAYOUT_DECODE (BLOCK128), the payload bytes are regrouped for the decode
+ * GEMM (fp8_gemm_blockscaled_fwd_decode_layout): for 16-row group f and 128-column block
+ * kb, the 2048 bytes at (f * cols/128 + kb) * 2048 hold, for i = 0..63, bytes
+ * kb*128 + 16*(i/16) .. +15 of row 16 f + i%16 at 16 i and bytes kb*128 + 64 + 16*(i/16) .. +15
+ * of that row at 1024 + 16 i -- the order in which the matrix instruction takes them; every
+ * byte keeps its value ([SkyRL-FP8] practical findings: one configuration fixes values,
+ * scales and layout conversions for both engines).
+ * The descriptors must agree on recipe, rows and cols; a DECODE dst needs a ROWS or DECODE
+ * src (FP8RL_ERR_RECIPE otherwise: the library never requantizes).
+ * Rules: BLOCK128: rows % 128 == 0, cols % 128 == 0; MXFP8: cols % 32 == 0, ROWS layout
+ * only. src and dst buffers must not overlap. */
 fp8rl_status fp8_weight_install(const fp8rl_weight* src, const fp8rl_weight* dst, void* stream);
 
 #ifdef __cplusplus

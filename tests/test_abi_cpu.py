@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
               "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd", "fp8_gemm_blockscaled_pow2_dgrad",
               "fp8_gemm_blockscaled_pow2_wgrad", "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16",
               "fp8_rmsnorm_quant_1x128", "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad",
-              "fp8_gemm_mxfp8_wgrad", "fp8_quant_w_128x128_f32"]:
+              "fp8_gemm_mxfp8_wgrad", "fp8_quant_w_128x128_f32", "fp8_gemm_blockscaled_fwd_decode_layout"]:
         assert n in names
 
 
@@ -58,15 +58,16 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8rl_abi_version() == 5
+    assert lib.fp8rl_abi_version() == 6
     for code in range(9):
         assert len(lib.fp8rl_status_str(code)) > 0
     assert lib.fp8rl_status_str(99) == b"unknown status"
 
 
 def test_workspace_size(lib):
-    assert lib.fp8rl_fwd_workspace_bytes(256, 4096) == 256 * 4096 + 256 * 32 * 4
-    assert lib.fp8rl_fwd_workspace_bytes(3, 128) == 512 + 3 * 4
+    # 256 bytes of counters, the quantized X padded to 256 bytes, then its fp32 scales
+    assert lib.fp8rl_fwd_workspace_bytes(256, 4096) == 256 + 256 * 4096 + 256 * 32 * 4
+    assert lib.fp8rl_fwd_workspace_bytes(3, 128) == 256 + 512 + 3 * 4
     assert lib.fp8rl_fwd_workspace_bytes(0, 128) == 0
     assert lib.fp8rl_fwd_workspace_bytes(4, 100) == 0
 
@@ -110,6 +111,16 @@ def test_gemm_validation(lib):
     assert fwd(None, None, P, P, P, 4, 128, 128, P, 0, None, 0, None) == ERR_WORKSPACE
     assert fwd(None, None, P, P, P, 4, 128, 128, P, 0, P2, 100, None) == ERR_WORKSPACE
     assert fwd(None, None, P, P, P, 4, 128, 128, P, 0, MIS, 1 << 20, None) == ERR_ALIGN
+    # the decode-layout forward: same rules, plus 32-bit offsets (M K and N K below 2^32)
+    fd = lib.fp8_gemm_blockscaled_fwd_decode_layout
+    assert fd(P, P, P, P, P, 4, 128, 128, P, 0, None, 0, None) == ERR_NULL
+    assert fd(P, P, None, P, P, 4, 100, 128, P, 0, None, 0, None) == ERR_SHAPE
+    assert fd(P, P, None, P, P, 4, 1 << 21, 1 << 11, P, 0, None, 0, None) == ERR_SHAPE   # N K = 2^32
+    assert fd(P, P, None, P, P, 1 << 21, 128, 1 << 11, P, 0, None, 0, None) == ERR_SHAPE  # M K = 2^32
+    assert fd(None, None, P, P, P, 4, 128, 128, P, 0, P2, 100, None) == ERR_WORKSPACE
+    assert fd(P, P, None, P, P, 0, 128, 128, P, 0, None, 0, None) == OK
+    # bf16-input form of the general forward: M K below 2^32 (a larger M goes to the tiled GEMM)
+    assert fwd(None, None, P, P, P, 1 << 21, 128, 1 << 11, P, 0, P2, 1 << 40, None) == ERR_SHAPE
     dg = lib.fp8_gemm_blockscaled_dgrad
     assert dg(P, P, None, P, 4, 128, 128, P, 0, None) == ERR_NULL
     assert dg(P, P, P, P, 4, 100, 128, P, 0, None) == ERR_SHAPE
@@ -232,6 +243,15 @@ def test_install_validation(lib):
     assert lib.fp8_weight_install(ctypes.byref(nul), ctypes.byref(W(F.RECIPE_BLOCK128, 128, 128, P2, P2)), None) == ERR_NULL
     e = W(F.RECIPE_BLOCK128, 0, 128, None, None)
     assert lib.fp8_weight_install(ctypes.byref(e), ctypes.byref(W(F.RECIPE_BLOCK128, 0, 128, None, None)), None) == OK
+    # layouts: the decode layout is BLOCK128 only, and a decode-layout payload never goes back to rows
+    rows_to_dec = W(F.RECIPE_BLOCK128, 256, 256, P2, P2, F.LAYOUT_DECODE)
+    dec = W(F.RECIPE_BLOCK128, 256, 256, P, P, F.LAYOUT_DECODE)
+    assert lib.fp8_weight_install(ctypes.byref(dec), ctypes.byref(W(F.RECIPE_BLOCK128, 256, 256, P2, P2)), None) == ERR_RECIPE
+    mxa = W(F.RECIPE_MXFP8, 256, 256, P, P)
+    assert lib.fp8_weight_install(ctypes.byref(mxa), ctypes.byref(W(F.RECIPE_MXFP8, 256, 256, P2, P2, F.LAYOUT_DECODE)), None) == ERR_RECIPE
+    assert lib.fp8_weight_install(ctypes.byref(a), ctypes.byref(W(F.RECIPE_BLOCK128, 256, 256, P2, P2, 5)), None) == ERR_RECIPE
+    assert lib.fp8_weight_install(ctypes.byref(bad), ctypes.byref(W(F.RECIPE_BLOCK128, 100, 256, P2, P2, F.LAYOUT_DECODE)), None) == ERR_SHAPE
+    del rows_to_dec
 
 
 def _gpu_present():

@@ -42,7 +42,7 @@ def test_graph_decode_call():
     x = bf16_dev(_rand((M, K), 11000))
     wq, sw, _ = F.fp8_quant_w_128x128(bf16_dev(_rand((N, K), 11001, 0.02)))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
-    ws = torch.empty(F.fp8rl_fwd_workspace_bytes(M, K), dtype=torch.uint8, device=dev())
+    ws = F.fwd_workspace(M, K, dev())
     _replays_match(lambda: F.fp8_gemm_blockscaled_fwd(wq=wq, sw=sw, x_bf16=x, y=y, workspace=ws), [y])
 
 
