@@ -386,11 +386,10 @@ def _odt(out_dtype):
 
 
 def fwd_workspace(M, K, device):
-    """A zeroed workspace for the bf16-input forward calls (its leading counters must start at
-    zero; every call leaves them zero, so one workspace serves any number of calls made one
-    after another on a stream)."""
+    """A workspace for the bf16-input forward calls: the quantized X and its scales (any
+    contents; calls running at the same time need one each)."""
     nbytes = load_library().fp8rl_fwd_workspace_bytes(M, K)
-    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def _fwd(fn, name, xq, sx, wq, sw, x_bf16, out_dtype, y, workspace, N, K):
@@ -418,7 +417,7 @@ def _fwd(fn, name, xq, sx, wq, sw, x_bf16, out_dtype, y, workspace, N, K):
 def fp8_gemm_blockscaled_fwd(xq=None, sx=None, wq=None, sw=None, *, x_bf16=None, out_dtype=torch.bfloat16, y=None,
                              workspace=None):
     """Y[M][N] = deq(X) deq(W)^T. X as (xq, sx) or, for the fused form, as x_bf16 (then a
-    zeroed workspace is allocated unless given; see fwd_workspace)."""
+    workspace is allocated unless given; see fwd_workspace)."""
     N, K = wq.shape
     _need(wq, torch.uint8, (N, K), "wq")
     return _fwd("fp8_gemm_blockscaled_fwd", "fp8_gemm_blockscaled_fwd", xq, sx, wq, sw, x_bf16, out_dtype, y,

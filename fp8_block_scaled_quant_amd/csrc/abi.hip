@@ -236,15 +236,13 @@ fp8rl_status mxfp8_quant_act_1x32(const uint16_t* x, int64_t R, int64_t K, uint8
   return launched(launch_quant_mx_tile(x, R, K, q, e8m0, qt, e8m0t, as_stream(stream)));
 }
 
-// Forward workspace: 256 bytes of counters (fused decode form), then the quantized X
-// (row-major for the tiled GEMM, K-block-major for the decode kernel), then its scales.
-constexpr size_t kCtlBytes = 256;
-
+// Forward workspace: the quantized X (row-major for the tiled GEMM, K-block-major for the
+// decode kernel), then its scales.
 size_t fp8rl_fwd_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % 128 != 0 || check_dims(M, K) != FP8RL_OK) return 0;
   const size_t qbytes = (size_t)(M * K);
   const size_t qpad = (qbytes + 255) & ~(size_t)255;
-  return kCtlBytes + qpad + (size_t)M * (size_t)(K / 128) * sizeof(float);
+  return qpad + (size_t)M * (size_t)(K / 128) * sizeof(float);
 }
 
 }  // extern "C"
@@ -253,8 +251,8 @@ namespace {
 
 // The forward product for both weight layouts. tiled_b: W in the decode layout (decode
 // kernel for every M). Otherwise M <= 256 goes to the decode kernel and larger M to the tiled
-// GEMM. A bf16 X is quantized inside the decode kernel's launch (K-block-major copy in the
-// workspace), or by the row quantizer before the tiled GEMM.
+// GEMM. A bf16 X is first quantized into the workspace: K-block-major for the decode kernel,
+// row-major for the tiled GEMM.
 fp8rl_status fwd_impl(const uint8_t* xq, const float* sx, const uint16_t* x_bf16, const uint8_t* wq, const float* sw,
                       int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                       bool tiled_b, void* stream) {
@@ -287,7 +285,7 @@ fp8rl_status fwd_impl(const uint8_t* xq, const float* sx, const uint16_t* x_bf16
   float* wss = nullptr;
   if (!quantized) {
     const size_t qpad = ((size_t)(M * K) + 255) & ~(size_t)255;
-    wsq = static_cast<uint8_t*>(workspace) + kCtlBytes;
+    wsq = static_cast<uint8_t*>(workspace);
     wss = reinterpret_cast<float*>(wsq + qpad);
   }
   if (decode) {
@@ -310,14 +308,13 @@ fp8rl_status fwd_impl(const uint8_t* xq, const float* sx, const uint16_t* x_bf16
       d.sa_ld = K / 128;
       d.sa_kb = 1;
     } else {
+      if (launch_quant_kbmajor(x_bf16, M, K, wsq, wss, st) != hipSuccess) return FP8RL_ERR_LAUNCH;
       d.A = wsq;
       d.sA = wss;
       d.a_ld = 128;
       d.a_kb = 128 * M;
       d.sa_ld = 1;
       d.sa_kb = M;
-      d.X = x_bf16;
-      d.ctl = static_cast<int*>(workspace);
     }
     return launched(launch_gemm_decode(d, y_dtype == FP8RL_OUT_F32, st));
   }

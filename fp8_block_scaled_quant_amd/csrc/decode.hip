@@ -32,15 +32,14 @@
 //   barrier (every wave's copies of kb landed; every wave is done with kb-1, whose stage and
 //   register set are refilled next), issue kb+P, compute kb. Past the last K block the loads
 //   go through empty descriptors (zeros, no memory access), so every step counts the same.
-// * Fused activation quantization (bf16 X): the workgroups of the launch first take K
-//   blocks of X from a counter in the workspace, one at a time, and quantize each (all M
-//   rows, 1x128 groups) into the K-block-major workspace copy, publishing it with a release
-//   fence and a second counter; a workgroup that finds every K block taken starts its weight
-//   prefetch, then waits until all K blocks are published (acquire) and runs the K loop on
-//   the workspace copy. A workgroup only ever waits for work that a running workgroup has
-//   already taken, so the launch completes whatever the occupancy; the wait is bounded.
-//   The last workgroup to finish resets the counters, so every call leaves them zero.
-// Deterministic: fixed K order; the only atomics are the workspace counters.
+// * bf16 X: a first launch quantizes X 1x128 into a K-block-major copy in the caller's
+//   workspace (k_quant_kbmajor: one workgroup per K block x 32 rows), and the GEMM reads that
+//   copy, each K block's MT rows one contiguous run. Quantizing inside the GEMM launch instead
+//   needs a device-scope hand-over between workgroups (release, counter, acquire), and on a
+//   chip whose eight L2s are not coherent with each other every such fence writes back or
+//   invalidates an L2: measured, that costs 20 to 45 us per call against a few us for the
+//   second launch.
+// Deterministic: fixed K order, no atomics.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -49,20 +48,33 @@ namespace fp8rl {
 namespace {
 
 constexpr int kDecodeLag = 3;
-// Bounded wait for the published activation blocks: iterations of a 256-cycle sleep
-// (about 0.1 s at 2 GHz; the quantization itself takes microseconds).
-constexpr int kPublishSpins = 1 << 20;
+// The weight loads and the direct-to-LDS copies are issued through the LLVM buffer-load
+// intrinsics, not inline assembly: the compiler then knows which registers a load has not
+// filled yet and puts an exact vmcnt wait in front of any use, copy or spill of them, and it
+// counts the copies when computing those waits (it also sets m0 and keeps the wait states
+// buffer instructions need). With asm loads it would treat the registers as ready at once and
+// could move them (say, to AGPRs under register pressure) before the data arrived.
+typedef __attribute__((address_space(3))) uint8_t* lds_bytes_t;
+extern "C" __device__ void fp8rl_raw_buffer_load_lds(v4i rsrc, lds_bytes_t lds, int size, int voffset, int soffset,
+                                                     int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+extern "C" __device__ v4i fp8rl_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
-// Buffer load of 16 bytes per lane into VGPRs. Issued as inline assembly so that the compiler
-// neither inserts its own vmcnt waits (which would count the direct-to-LDS copies wrongly)
-// nor schedules a use before the explicit wait: the consumer waits with wait_vmem_n<>() and
-// then hold()s the value. The s_nop 4 gives the 5 wait states a buffer instruction needs
-// after a VALU write of its descriptor SGPRs, which the compiler cannot insert into asm.
 __device__ __forceinline__ v4i bload16(v4i rsrc, uint32_t voff) {
-  v4i r;
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc) : "memory");
-  return r;
+  return fp8rl_raw_buffer_load_v4i32(rsrc, (int)voff, 0, 0);
 }
+// Lane i's 16 (or 4) bytes from rsrc + voff land at LDS byte lds + 16 i (or 4 i); lds is
+// wave-uniform.
+__device__ __forceinline__ void copy16(v4i rsrc, uint32_t voff, lds_bytes_t lds) {
+  fp8rl_raw_buffer_load_lds(rsrc, lds, 16, (int)voff, 0, 0, 0);
+}
+__device__ __forceinline__ void copy4(v4i rsrc, uint32_t voff, lds_bytes_t lds) {
+  fp8rl_raw_buffer_load_lds(rsrc, lds, 4, (int)voff, 0, 0, 0);
+}
+// Workgroup barrier that orders memory operations around it for the compiler but adds no
+// wait of its own (__syncthreads() would wait for every copy in flight, prefetches included);
+// the K loop waits for exactly the copies it needs before it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int MT, int NW, int FW, int P>
 struct DecodeShape {
@@ -84,49 +96,56 @@ struct DecodeShape {
   static_assert(P >= 1 && P <= 8, "prefetch distance");
 };
 
-// 1x128 quantization of K block kb of bf16 X[M][K] (all M rows) into the K-block-major
-// copy: group (m, kb) -> payload q[(kb M + m) * 128 ..], scale s[kb M + m]. 8 lanes per
-// group, 16 elements each; 256 threads cover 32 rows per pass. Bytes and scales equal
-// those of the row-major 1x128 quantizer ([AIS] quantizer equation; [Jet-RL] 1x128 groups).
-__device__ __forceinline__ void quant_kblock(const uint16_t* __restrict__ x, int M, int64_t K, int kb,
-                                             uint8_t* __restrict__ q, float* __restrict__ s, int tid) {
+}  // namespace
+
+// 1x128 quantization of bf16 X[M][K] into the K-block-major copy: workgroup u covers K block
+// kb = u / mch and rows 32 (u % mch) .. +31 (mch = ceil(M / 32)); group (m, kb) -> payload
+// q[(kb M + m) * 128 ..], scale s[kb M + m]. 256 threads, 8 lanes per group, 16 elements
+// each. Bytes and scales equal those of the row-major 1x128 quantizer ([AIS] quantizer
+// equation; [Jet-RL] 1x128 groups).
+__global__ __launch_bounds__(256) void k_quant_kbmajor(const uint16_t* __restrict__ x, int M, int64_t K, int mch,
+                                                       uint8_t* __restrict__ q, float* __restrict__ s) {
+  const int tid = threadIdx.x;
+  const int u = (int)blockIdx.x;
+  const int kb = u / mch;
+  const int m = (u - kb * mch) * 32 + (tid >> 3);
   const int part = tid & 7;
-  for (int r0 = 0; r0 < M; r0 += 32) {
-    const int m = r0 + (tid >> 3);
-    const bool valid = m < M;
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + (int64_t)kb * 128 + part * 16);
-      a = src[0];
-      b = src[1];
-    }
-    float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
-                       fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    const BlockScale bs = block_scale(amax);
-    if (valid) {
-      const int64_t g = (int64_t)kb * M + m;
-      const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
-      const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
-      *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      if (part == 0) s[g] = bs.s;
-    }
+  const bool valid = m < M;
+  uint4 a = make_uint4(0, 0, 0, 0), b = a;
+  if (valid) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + (int64_t)kb * 128 + part * 16);
+    a = src[0];
+    b = src[1];
+  }
+  float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
+                     fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const BlockScale bs = block_scale(amax);
+  if (valid) {
+    const int64_t g = (int64_t)kb * M + m;
+    const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
+    const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
+    *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    if (part == 0) s[g] = bs.s;
   }
 }
 
-}  // namespace
+hipError_t launch_quant_kbmajor(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, hipStream_t stream) {
+  const int64_t mch = (M + 31) / 32, units = (K / 128) * mch;
+  if (units > 0x7fffffff || M > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_kbmajor, dim3((unsigned)units), dim3(256), 0, stream, x, (int)M, K, (int)mch, q, s);
+  return hipGetLastError();
+}
 
-// kFused: X arrives as bf16 (p.X) and is quantized inside the launch into p.A / p.sA
-// (K-block-major), synchronised through p.ctl. kTiledB: B is in the decode layout.
-template <int MT, int NW, int FW, int P, bool kF32, bool kFused, bool kTiledB>
+// kTiledB: B is in the decode layout.
+template <int MT, int NW, int FW, int P, bool kF32, bool kTiledB>
 __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
   using S = DecodeShape<MT, NW, FW, P>;
   constexpr int NT = S::NT, XF = S::XF, NS = S::NS, LX = S::LX;
   static_assert(S::LDS <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
-  __shared__ int s_claim;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,32 +158,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
   const int mpart = q8 % ms, run = (q8 / ms) * 8 + (int)(blockIdx.x & 7);
   const int64_t n0 = (int64_t)run * S::BN;
   const int m0 = mpart * MT;
-  const bool active = n0 < N;                          // uniform: padding workgroups only help quantize
+  if (n0 >= N) return;                                 // padding workgroup (uniform)
 
-  if constexpr (kFused) {
-    // Quantize K blocks of X until every one has been taken. Thread 0 publishes a block and
-    // claims the next one in a single branch that a barrier closes, and the claimed index is
-    // read back wave-uniform, so the loop runs in lockstep for every lane: with one branch on
-    // thread 0 before the back-edge (publish) and another after it (claim), the compiler may
-    // route the other lanes straight back to the barrier past both, and they then loop on a
-    // stale claim while thread 0 waits for them.
-    if (tid == 0) s_claim = atomicAdd(&p.ctl[0], 1);
-    __syncthreads();
-    int c = __builtin_amdgcn_readfirstlane(s_claim);
-    while (c < nkb) {
-      quant_kblock(p.X, M, K, c, const_cast<uint8_t*>(p.A), const_cast<float*>(p.sA), tid);
-      __threadfence();                                 // release this thread's stores (device scope)
-      __syncthreads();                                 // ... and every thread has read s_claim
-      if (tid == 0) {
-        atomicAdd(&p.ctl[1], 1);                       // publish K block c
-        s_claim = atomicAdd(&p.ctl[0], 1);             // take the next one
-      }
-      __syncthreads();
-      c = __builtin_amdgcn_readfirstlane(s_claim);
-    }
-  }
-
-  const int64_t rows_b = active ? ((N - n0) < S::BN ? (N - n0) : S::BN) : 16;
+  const int64_t rows_b = (N - n0) < S::BN ? (N - n0) : S::BN;
   const int fvalid = (int)(rows_b / 16);
 
   // A copies: thread t moves 16 bytes of tile row t/8 (+ NT/8 per copy), LDS chunk t%8,
@@ -181,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
   // fragment repeat it).
   const bool cB = wave == S::SB_WAVE;
   const int fl = lane < fvalid ? lane : fvalid - 1;
-  const uint32_t offSB = (uint32_t)((((active ? n0 : 0) + 16 * fl) >> 7) * p.sb_ld_n * 4);
+  const uint32_t offSB = (uint32_t)(((n0 + 16 * fl) >> 7) * p.sb_ld_n * 4);
   const uint64_t sb_total = (uint64_t)(((N - 1) >> 7) * p.sb_ld_n + (int64_t)(nkb - 1) * p.sb_ld_k + 1) * 4;
   // B fragments. Row-major: lane l reads row (l & 15) of the fragment, bytes 16 g and
   // 64 + 16 g of the K block (g = l >> 4), the operand layout of the MFMA. Decode layout:
@@ -190,7 +186,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
   const uint32_t offB = kTiledB ? (uint32_t)((int64_t)wave * FW * 16 * K + 16 * lane)
                                 : (uint32_t)((int64_t)(wave * FW * 16 + (lane & 15)) * K + 16 * (lane >> 4));
   const uint32_t bytesB = (uint32_t)(kTiledB ? rows_b * K : (rows_b - 1) * K + 128);
-  const uint8_t* Bp = p.B + (active ? n0 : 0) * K;
+  const uint8_t* Bp = p.B + n0 * K;
 
   auto rng = [](uint64_t total, uint64_t used) __attribute__((always_inline)) -> uint32_t {
     const uint64_t r = total - used;
@@ -215,18 +211,18 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
   // The activation and scale copies of K block kb into stage `set`.
   auto issue_a = [&](int kb, auto setc) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
-    const uint32_t st = lds_addr(smem) + set * S::STAGE;
+    lds_bytes_t st = (lds_bytes_t)smem + set * S::STAGE;  // generic -> LDS address space
     const bool live = kb < nkb;
     const int64_t kbc = live ? kb : 0;
     const v4i ra = make_rsrc(p.A + kbc * p.a_kb, live ? rng(a_total, (uint64_t)(kbc * p.a_kb)) : 0u);
 #pragma unroll
     for (int it = 0; it < LX; ++it)
-      dma16(ra, offA + (uint32_t)(it * (NT / 8)) * (uint32_t)p.a_ld, st + (it * NT + wave * 64) * 16);
+      copy16(ra, offA + (uint32_t)(it * (NT / 8)) * (uint32_t)p.a_ld, st + (it * NT + wave * 64) * 16);
     if (cA)
-      dma4(make_rsrc(p.sA + kbc * p.sa_kb, live ? rng(sa_total, (uint64_t)(kbc * p.sa_kb) * 4) : 0u), offSA,
+      copy4(make_rsrc(p.sA + kbc * p.sa_kb, live ? rng(sa_total, (uint64_t)(kbc * p.sa_kb) * 4) : 0u), offSA,
            st + S::OFF_SA + wave * 256);
     if (cB)
-      dma4(make_rsrc(p.sB + kbc * p.sb_ld_k, live ? rng(sb_total, (uint64_t)(kbc * p.sb_ld_k) * 4) : 0u), offSB,
+      copy4(make_rsrc(p.sB + kbc * p.sb_ld_k, live ? rng(sb_total, (uint64_t)(kbc * p.sb_ld_k) * 4) : 0u), offSB,
            st + S::OFF_SB);
   };
   // Vector-memory operations per K block of this wave: LX + (cA) + (cB) + 2 FW; at the wait
@@ -265,8 +261,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
     static_for<0, FW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       hold(sb[i]);
-      hold(wlo[set][i]);
-      hold(whi[set][i]);
       bf[i] = join(wlo[set][i], whi[set][i]);
     });
     hold(xlo);
@@ -313,24 +307,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
     for (int u = (XF * FW > kDecodeLag ? XF * FW - kDecodeLag : 0); u < XF * FW; ++u) fold(u);
   };
 
-  if (active) {
-    // Prologue: weights of K blocks 0 .. P-1 first (they do not depend on the activations),
-    // then, once the activation copy is complete, its copies. The first step waits for all.
+  {
+    // Prologue: weights of K blocks 0 .. P-1, then the activation copies; the first step
+    // waits for all of them.
     static_for<0, P>([&](auto sc) { issue_b(decltype(sc)::value, sc); });
-    if constexpr (kFused) {
-      if (tid == 0) {
-        int spins = 0;
-        while (__hip_atomic_load(&p.ctl[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < nkb) {
-          if (++spins > kPublishSpins) {
-            atomicOr(&p.ctl[3], 1);                    // give up waiting; the output is not valid
-            break;
-          }
-          __builtin_amdgcn_s_sleep(4);
-        }
-      }
-      __syncthreads();
-      __threadfence();                                 // acquire: later reads see the published blocks
-    }
     static_for<0, P>([&](auto sc) { issue_a(decltype(sc)::value, sc); });
     for (int kb0 = 0; kb0 < nkb; kb0 += NS) {
       static_for<0, NS>([&](auto sc) {
@@ -339,7 +319,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
         if (kb < nkb) {
           if (kb == 0) wait_vmem();
           else wait_block();
-          __syncthreads();
+          barrier_only();
           constexpr auto nxt = std::integral_constant<int, (s + P) % NS>{};
           issue_a(kb + P, nxt);
           issue_b(kb + P, nxt);
@@ -347,18 +327,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
         }
       });
     }
-    wait_vmem();      // the empty loads issued past the last K block
-    // Those loads have no consumer, so without a use after the wait the compiler could give
-    // their destination registers to epilogue arithmetic placed ahead of the wait, which the
-    // arriving zeros would then overwrite.
-    static_for<0, NS>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-#pragma unroll
-      for (int i = 0; i < FW; ++i) {
-        hold(wlo[s][i]);
-        hold(whi[s][i]);
-      }
-    });
+    wait_vmem();      // the empty loads and copies issued past the last K block
 
     // Epilogue: lane holds C[m][n .. n+3] for m = m0 + 16 j + (lane & 15) and
     // n = n0 + 16 (wave FW + i) + 4 (lane >> 4).
@@ -380,19 +349,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = v;
         }
       }
-    }
-  }
-
-  if constexpr (kFused) {
-    // The last workgroup to finish resets the counters for the next call. Its increment is
-    // acquire-release, so this workgroup's own counter updates are complete before it counts.
-    __syncthreads();
-    if (tid == 0 &&
-        __hip_atomic_fetch_add(&p.ctl[2], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
-      __hip_atomic_store(&p.ctl[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.ctl[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.ctl[3], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.ctl[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -430,21 +386,12 @@ static hipError_t launch_decode_cfg(const DecodeParams& p, bool f32, hipStream_t
   const int64_t blocks = (runs + 7) / 8 * 8 * ms;
   if (blocks > 0x7fffffff || p.M > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 g((unsigned)blocks), b(NW * 64);
-  const bool fused = p.ctl != nullptr;
-#define FP8RL_DECODE_LAUNCH(F32, FUSED, TILED) \
-  hipLaunchKernelGGL((k_gemm_decode<MT, NW, FW, P, F32, FUSED, TILED>), g, b, 0, stream, p)
+#define FP8RL_DECODE_LAUNCH(F32, TILED) \
+  hipLaunchKernelGGL((k_gemm_decode<MT, NW, FW, P, F32, TILED>), g, b, 0, stream, p)
   if (f32) {
-    if (fused) {
-      if (p.tiled_b) FP8RL_DECODE_LAUNCH(true, true, true); else FP8RL_DECODE_LAUNCH(true, true, false);
-    } else {
-      if (p.tiled_b) FP8RL_DECODE_LAUNCH(true, false, true); else FP8RL_DECODE_LAUNCH(true, false, false);
-    }
+    if (p.tiled_b) FP8RL_DECODE_LAUNCH(true, true); else FP8RL_DECODE_LAUNCH(true, false);
   } else {
-    if (fused) {
-      if (p.tiled_b) FP8RL_DECODE_LAUNCH(false, true, true); else FP8RL_DECODE_LAUNCH(false, true, false);
-    } else {
-      if (p.tiled_b) FP8RL_DECODE_LAUNCH(false, false, true); else FP8RL_DECODE_LAUNCH(false, false, false);
-    }
+    if (p.tiled_b) FP8RL_DECODE_LAUNCH(false, true); else FP8RL_DECODE_LAUNCH(false, false);
   }
 #undef FP8RL_DECODE_LAUNCH
   return hipGetLastError();
@@ -454,28 +401,37 @@ struct DecodeCfg {
   int mt, fw, p;
   hipError_t (*launch)(const DecodeParams&, bool, hipStream_t);
 };
-// 4 waves per workgroup; (row part, fragments per wave, prefetch distance).
+// 4 waves per workgroup; (row part, fragments per wave, prefetch distance). For each
+// (row part, fragments per wave) the prefetch distance is the fastest one measured on the
+// rollout decode shapes (M = 256, K = 4096; N = 4096, 12288, 24576; weights in the decode
+// layout, streamed from HBM); deeper prefetch only added register pressure.
 static const DecodeCfg kDecodeCfgs[] = {
-    {128, 3, 2, launch_decode_cfg<128, 4, 3, 2>}, {128, 2, 3, launch_decode_cfg<128, 4, 2, 3>},
-    {128, 1, 4, launch_decode_cfg<128, 4, 1, 4>}, {64, 3, 3, launch_decode_cfg<64, 4, 3, 3>},
-    {64, 2, 4, launch_decode_cfg<64, 4, 2, 4>},   {64, 1, 6, launch_decode_cfg<64, 4, 1, 6>},
-    {256, 2, 2, launch_decode_cfg<256, 4, 2, 2>}, {256, 1, 3, launch_decode_cfg<256, 4, 1, 3>},
+    {64, 1, 4, launch_decode_cfg<64, 4, 1, 4>},   {64, 2, 2, launch_decode_cfg<64, 4, 2, 2>},
+    {64, 3, 3, launch_decode_cfg<64, 4, 3, 3>},   {64, 4, 2, launch_decode_cfg<64, 4, 4, 2>},
+    {128, 1, 2, launch_decode_cfg<128, 4, 1, 2>}, {128, 2, 2, launch_decode_cfg<128, 4, 2, 2>},
+    {128, 3, 2, launch_decode_cfg<128, 4, 3, 2>}, {256, 1, 2, launch_decode_cfg<256, 4, 1, 2>},
+    {256, 2, 2, launch_decode_cfg<256, 4, 2, 2>},
 };
 
-// Choice: the fewest rounds of 256 workgroups, then the least data per CU and K block
-// (MT rows of A copied into LDS + 16 F rows of B loaded), then the larger row part.
+// Choice: the fewest rounds of 256 workgroups (one per CU), then the least data per CU and
+// K block (the MT rows of A copied to LDS + the 64 FW rows of B loaded), then more fragments
+// per wave (longer weight runs per copied activation row), then the smaller row part. On the
+// decode shapes this picks the fastest measured configuration for every N.
 hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t stream) {
   const DecodeCfg* best = nullptr;
-  int64_t best_rounds = 0, best_bytes = 0;
+  int64_t best_rounds = 0, best_rows = 0;
   for (const DecodeCfg& c : kDecodeCfgs) {
     const int64_t ms = (p.M + c.mt - 1) / c.mt;
     const int64_t runs = (p.N + 64 * c.fw - 1) / (64 * c.fw);
     const int64_t rounds = (ms * runs + 255) / 256;
-    const int64_t rows = (p.M < c.mt ? p.M : c.mt) + 64 * c.fw;
-    if (best == nullptr || rounds < best_rounds || (rounds == best_rounds && rows * rounds < best_bytes)) {
+    const int64_t rows = ((p.M < c.mt ? p.M : c.mt) + 64 * c.fw) * rounds;
+    bool take = best == nullptr || rounds < best_rounds || (rounds == best_rounds && rows < best_rows);
+    if (!take && rounds == best_rounds && rows == best_rows)
+      take = c.fw > best->fw || (c.fw == best->fw && c.mt < best->mt);
+    if (take) {
       best = &c;
       best_rounds = rounds;
-      best_bytes = rows * rounds;
+      best_rows = rows;
     }
   }
   return best->launch(p, f32, stream);

@@ -60,10 +60,7 @@ hipError_t launch_gemm_mx(const GemmParams& p, bool f32, hipStream_t stream);
 // A[m * a_ld + (k / 128) * a_kb + k % 128], its scale at sA[m * sa_ld + (k / 128) * sa_kb];
 // row-major A: (a_ld, a_kb) = (K, 128), (sa_ld, sa_kb) = (K / 128, 1); K-block-major:
 // (128, 128 M) and (1, M). C [M][ldc], bf16 or fp32 (no accumulation).
-// Fused form (ctl != NULL): X is bf16 [M][K] (row-major) and the launch quantizes it into A /
-// sA (K-block-major, which A / sA and the strides must then describe), synchronised through
-// the four int32 counters at ctl, zero on entry and left zero. tiled_b: B in the decode
-// layout (launch_decode_layout) instead of row-major.
+// tiled_b: B in the decode layout (launch_decode_layout) instead of row-major.
 struct DecodeParams {
   const uint8_t* A;
   const float* sA;
@@ -72,11 +69,12 @@ struct DecodeParams {
   void* C;
   int64_t M, N, K;
   int64_t a_ld, a_kb, sa_ld, sa_kb, sb_ld_n, sb_ld_k, ldc;
-  const uint16_t* X;
-  int* ctl;
   int tiled_b;
 };
 hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t stream);
+// 1x128 quantization of bf16 X [M][K] into the K-block-major copy q [K/128][M][128], s
+// [K/128][M] (decode.hip); same bytes and scales as launch_quant_rows_1x128, permuted.
+hipError_t launch_quant_kbmajor(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s, hipStream_t stream);
 // Row-major FP8 weight [N][K] -> decode layout (decode.hip), N % 16 == 0, K % 128 == 0.
 hipError_t launch_decode_layout(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K, hipStream_t stream);
 

@@ -74,7 +74,7 @@ typedef enum {
 } fp8rl_layout;
 
 /* ABI version of this header. */
-#define FP8RL_ABI_VERSION 6
+#define FP8RL_ABI_VERSION 7
 int fp8rl_abi_version(void);
 const char* fp8rl_status_str(fp8rl_status status);
 
@@ -200,18 +200,17 @@ fp8rl_status fp8_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, i
 /* Forward: Y[M][N] = deq(X) . deq(W)^T.
  *   X given EITHER quantized (xq uint8 [M][K] + sx fp32 [M][K/128], x_bf16 = NULL)
  *   OR as bf16 (x_bf16 [M][K], xq = sx = NULL): then X is quantized 1x128 on the device
- *   inside this call ([SkyRL-FP8] "Performance analysis", generation: activation
- *   quantization folded into the GEMM path while weights and scales stay fixed), into the
- *   caller's workspace, with bytes identical to fp8_quant_act_1x128.
+ *   inside this call ([SkyRL-FP8] "Performance analysis", generation: activations quantized
+ *   on the fly in the GEMM path while weights and scales stay fixed), into the caller's
+ *   workspace, with bytes identical to fp8_quant_act_1x128 (a quantizer launch, then the
+ *   GEMM launch, on the given stream).
  *   wq uint8 [N][K], sw fp32 [N/128][K/128] (as produced by fp8_quant_w_128x128 or
  *   installed by fp8_weight_install).
  *   y: [M][N], bf16 or fp32 per y_dtype.
  *   workspace/workspace_bytes: only for the bf16-input form; at least
- *   fp8rl_fwd_workspace_bytes(M, K) bytes, 16-byte aligned. Ignored otherwise (may be NULL).
- *   Its first 256 bytes hold counters through which the workgroups of one launch share the
- *   quantization of X (M <= 256: quantization and GEMM are a single kernel launch); they must
- *   be zero before the first call on a workspace (allocate it zeroed) and every call leaves
- *   them zero. Calls that run at the same time must not share a workspace.
+ *   fp8rl_fwd_workspace_bytes(M, K) bytes, 16-byte aligned, any contents (the call overwrites
+ *   it with quantized X). Ignored otherwise (may be NULL). Calls that run at the same time
+ *   must not share a workspace.
  * Rules: K % 128 == 0, N % 128 == 0, M >= 0 (any M); M * K < 2^32 for the bf16-input form. */
 fp8rl_status fp8_gemm_blockscaled_fwd(const uint8_t* xq, const float* sx, const uint16_t* x_bf16,
                                       const uint8_t* wq, const float* sw,

@@ -58,16 +58,16 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8rl_abi_version() == 6
+    assert lib.fp8rl_abi_version() == 7
     for code in range(9):
         assert len(lib.fp8rl_status_str(code)) > 0
     assert lib.fp8rl_status_str(99) == b"unknown status"
 
 
 def test_workspace_size(lib):
-    # 256 bytes of counters, the quantized X padded to 256 bytes, then its fp32 scales
-    assert lib.fp8rl_fwd_workspace_bytes(256, 4096) == 256 + 256 * 4096 + 256 * 32 * 4
-    assert lib.fp8rl_fwd_workspace_bytes(3, 128) == 256 + 512 + 3 * 4
+    # the quantized X padded to 256 bytes, then its fp32 scales
+    assert lib.fp8rl_fwd_workspace_bytes(256, 4096) == 256 * 4096 + 256 * 32 * 4
+    assert lib.fp8rl_fwd_workspace_bytes(3, 128) == 512 + 3 * 4
     assert lib.fp8rl_fwd_workspace_bytes(0, 128) == 0
     assert lib.fp8rl_fwd_workspace_bytes(4, 100) == 0
 

@@ -1,5 +1,5 @@
-"""GPU tests of the decode-shaped forward path: the fused bf16-input form (the activations
-quantized inside the GEMM launch), the decode weight layout written by the install, and
+"""GPU tests of the decode-shaped forward path: the bf16-input form (the activations
+quantized 1x128 inside the call), the decode weight layout written by the install, and
 the bit identity of trainer and rollout outputs across both layouts ([SkyRL-FP8]
 "On-Policy FP8 weight sync": installed weights reproduce the trainer's outputs exactly;
 "Performance analysis": decode is bound by the weight stream)."""
@@ -68,7 +68,7 @@ def test_decode_layout_forward_matches_rows(M, N, K):
         y_dec_f = F.fp8_gemm_blockscaled_fwd_decode_layout(wq=dq, sw=ds, x_bf16=xt, N=N, K=K, out_dtype=dt)
         torch.cuda.synchronize()
         iv = torch.int32 if dt == torch.float32 else torch.int16
-        for other, name in ((y_dec, "decode layout"), (y_rows_f, "fused bf16 X"), (y_dec_f, "fused, decode layout")):
+        for other, name in ((y_dec, "decode layout"), (y_rows_f, "bf16 X"), (y_dec_f, "bf16 X, decode layout")):
             assert torch.equal(other.view(iv), y_rows.view(iv)), f"{name} differs from the row-major forward"
         if dt == torch.float32:
             rxq, rsx = OQ.quant_act_1x128(x)
@@ -76,25 +76,26 @@ def test_decode_layout_forward_matches_rows(M, N, K):
             assert_gemm_close(host(y_rows), OG.gemm_fwd(rxq, rsx, rwq, rsw), f"decode fwd M={M} N={N} K={K}")
 
 
-def test_fused_workspace_counters_and_repeat():
-    """The bf16-input call leaves the workspace counters zero and its K-block-major copy of X
-    holds exactly the 1x128 quantizer's bytes; repeated calls on one workspace agree."""
+def test_bf16_form_workspace_copy_and_repeat():
+    """The bf16-input call accepts a workspace with any contents, its K-block-major copy of X
+    holds exactly the 1x128 quantizer's bytes and scales, and repeated calls on one workspace
+    agree bit for bit."""
     M, N, K = 200, 1024, 1536
     x = W.normal_bf16((M, K), 1.0, 79, 1)
     _, wq, sw = _weights(N, K, 5)
     ws = F.fwd_workspace(M, K, dev())
+    ws.fill_(0xFF)
     xt = bf16_dev(x)
     ys = [F.fp8_gemm_blockscaled_fwd(wq=wq, sw=sw, x_bf16=xt, out_dtype=torch.float32, workspace=ws)
           for _ in range(3)]
     torch.cuda.synchronize()
-    assert int(ws[:256].count_nonzero()) == 0, "counters not reset"
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int32), ys[0].view(torch.int32))
     rq, rs = OQ.quant_act_1x128(x)
     nkb = K // 128
     qpad = (M * K + 255) // 256 * 256
-    wsq = host(ws[256:256 + M * K]).reshape(nkb, M, 128)
-    wss = host(ws[256 + qpad:256 + qpad + M * nkb * 4]).view(np.float32).reshape(nkb, M)
+    wsq = host(ws[:M * K]).reshape(nkb, M, 128)
+    wss = host(ws[qpad:qpad + M * nkb * 4]).view(np.float32).reshape(nkb, M)
     assert np.array_equal(wsq, rq.reshape(M, nkb, 128).transpose(1, 0, 2))
     assert np.array_equal(wss.view(np.uint32), np.ascontiguousarray(rs.T).view(np.uint32))
 
@@ -144,6 +145,37 @@ def test_decode_every_k_block(K):
                                                            out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(y_dec.view(torch.int32), y_rows.view(torch.int32)), f"K block {j}: layouts differ"
-        assert torch.equal(y_dec_f.view(torch.int32), y_rows.view(torch.int32)), f"K block {j}: fused differs"
+        assert torch.equal(y_dec_f.view(torch.int32), y_rows.view(torch.int32)), f"K block {j}: bf16-X form differs"
         rxq, rsx = OQ.quant_act_1x128(host(xt))
         assert_gemm_close(host(y_rows), OG.gemm_fwd(rxq, rsx, rwq, rsw), f"K={K} block {j}")
+
+
+# One (M, N) per configuration of the decode kernel that the launch chooses (row part, weight
+# fragments per wave, prefetch distance), so every configuration runs: (64,1,4), (64,2,2),
+# (64,3,3), (64,4,2), (128,1,2), (128,2,2), (128,3,2), (256,1,2), (256,2,2).
+_CONFIG_SHAPES = [(1, 128), (1, 16512), (1, 32896), (1, 49280), (65, 8320), (65, 16512), (65, 32896),
+                  (129, 11008), (129, 16512)]
+
+
+@pytest.mark.parametrize("M,N", _CONFIG_SHAPES)
+@pytest.mark.parametrize("K", [256, 640])
+def test_decode_every_config(M, N, K):
+    """Each configuration: row-major and decode-layout weights and both forms of X give the
+    same bits, and sampled 128-column blocks match the oracle."""
+    x = W.normal_bf16((M, K), 1.0, 83, M * 3 + N + K)
+    w = W.normal_bf16((N, K), 0.02, 84, N + K)
+    wq, sw, _ = F.fp8_quant_w_128x128(bf16_dev(w))
+    dq, ds = _install_decode(wq, sw)
+    xt = bf16_dev(x)
+    xq, sx = F.fp8_quant_act_1x128(xt)[:2]
+    y_rows = F.fp8_gemm_blockscaled_fwd(xq, sx, wq, sw, out_dtype=torch.float32)
+    y_dec = F.fp8_gemm_blockscaled_fwd_decode_layout(xq, sx, dq, ds, N=N, K=K, out_dtype=torch.float32)
+    y_dec_b = F.fp8_gemm_blockscaled_fwd_decode_layout(wq=dq, sw=ds, x_bf16=xt, N=N, K=K, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y_dec.view(torch.int32), y_rows.view(torch.int32)), "decode layout differs"
+    assert torch.equal(y_dec_b.view(torch.int16), y_rows.to(torch.bfloat16).view(torch.int16)), "bf16 form differs"
+    blocks = np.random.default_rng(N).choice(N // 128, min(4, N // 128), replace=False)
+    cols = np.concatenate([np.arange(b * 128, (b + 1) * 128) for b in sorted(blocks)])
+    rxq, rsx = OQ.quant_act_1x128(x)
+    rwq, rsw = OQ.quant_w_128x128(w[cols])
+    assert_gemm_close(host(y_rows)[:, cols], OG.gemm_fwd(rxq, rsx, rwq, rsw), f"M={M} N={N} K={K}")
