@@ -31,6 +31,7 @@ __all__ = [
     "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16", "fp8_rmsnorm_quant_1x128",
     "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad", "fp8_gemm_mxfp8_wgrad",
     "fp8_quant_w_128x128_f32", "LAYOUT_ROWS", "LAYOUT_DECODE", "fp8_gemm_blockscaled_fwd_decode_layout",
+    "fp8_gemm_blockscaled_fwd_decode_layout_noalloc", "NOALLOC_SCRATCH_BYTES",
     "fwd_workspace",
 ]
 
@@ -65,6 +66,8 @@ _SIGNATURES = {
     "fp8rl_fwd_workspace_bytes": ([_i64, _i64], _sz),
     "fp8_gemm_blockscaled_fwd_decode_layout": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp],
                                                _int),
+    "fp8_gemm_blockscaled_fwd_decode_layout_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
+                                                       _int),
     "fp8_gemm_blockscaled_dgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_gemm_blockscaled_wgrad": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp], _int),
     "fp8_grouped_gemm": ([_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _int, _vp], _int),
@@ -432,6 +435,35 @@ def fp8_gemm_blockscaled_fwd_decode_layout(xq=None, sx=None, wq=None, sw=None, *
         raise ValueError(f"wq must be a contiguous GPU uint8 tensor of {N} * {K} bytes")
     return _fwd("fp8_gemm_blockscaled_fwd_decode_layout", "fp8_gemm_blockscaled_fwd_decode_layout", xq, sx, wq, sw,
                 x_bf16, out_dtype, y, workspace, N, K)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # FP8RL_NOALLOC_SCRATCH_BYTES
+
+
+def fp8_gemm_blockscaled_fwd_decode_layout_noalloc(xq=None, sx=None, wq=None, sw=None, *, N, K, x_bf16=None,
+                                                   out_dtype=torch.bfloat16, y=None):
+    """fp8_gemm_blockscaled_fwd_decode_layout without a workspace: the C call quantizes a bf16
+    X into the library's built-in scratch and allocates nothing (pass y to allocate nothing
+    here either). Calls that may overlap on one GPU must be serialised by the caller."""
+    if wq.dtype != torch.uint8 or not wq.is_cuda or not wq.is_contiguous() or wq.numel() != N * K:
+        raise ValueError(f"wq must be a contiguous GPU uint8 tensor of {N} * {K} bytes")
+    lib = load_library()
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    dev = wq.device
+    if x_bf16 is not None:
+        if xq is not None or sx is not None:
+            raise ValueError("give either (xq, sx) or x_bf16")
+        M = x_bf16.shape[0]
+        _need(x_bf16, torch.bfloat16, (M, K), "x_bf16")
+    else:
+        M = xq.shape[0]
+        _need(xq, torch.uint8, (M, K), "xq")
+        _need(sx, torch.float32, (M, K // 128), "sx")
+    y = _out(y, out_dtype, (M, N), dev, "y")
+    _check(lib.fp8_gemm_blockscaled_fwd_decode_layout_noalloc(_ptr(xq), _ptr(sx), _ptr(x_bf16), _ptr(wq), _ptr(sw), M, N,
+                                                              K, _ptr(y), _odt(out_dtype), _stream(dev)),
+           "fp8_gemm_blockscaled_fwd_decode_layout_noalloc")
+    return y
 
 
 def fp8_gemm_blockscaled_pow2_fwd(xq, sx, wq, sw, *, out_dtype=torch.bfloat16, y=None):

@@ -7,6 +7,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fp8rl.h"
 #include "internal.hpp"
@@ -51,6 +52,31 @@ fp8rl_status check_dims(int64_t a, int64_t b) {
 constexpr int64_t kMaxRed = (int64_t)1 << 23;
 
 fp8rl_status check_red(int64_t kred) { return kred > kMaxRed ? FP8RL_ERR_SHAPE : FP8RL_OK; }
+
+// Scratch of the allocation-free forward (fp8_gemm_blockscaled_fwd_decode_layout_noalloc):
+// the quantized X and its scales of one call, in a file-scope device array that every GPU
+// the library runs on holds until the process ends. In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[FP8RL_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+fp8rl_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8RL_ERR_DEVICE;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FP8RL_ERR_DEVICE;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8RL_OK;
+}
 
 }  // namespace
 
@@ -253,9 +279,10 @@ namespace {
 // kernel for every M). Otherwise M <= 256 goes to the decode kernel and larger M to the tiled
 // GEMM. A bf16 X is first quantized into the workspace: K-block-major for the decode kernel,
 // row-major for the tiled GEMM.
+// noalloc: the workspace is the library's scratch array (workspace arguments ignored).
 fp8rl_status fwd_impl(const uint8_t* xq, const float* sx, const uint16_t* x_bf16, const uint8_t* wq, const float* sw,
                       int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
-                      bool tiled_b, void* stream) {
+                      bool tiled_b, void* stream, bool noalloc = false) {
   const bool quantized = xq != nullptr || sx != nullptr;
   if (quantized && (xq == nullptr || sx == nullptr)) return FP8RL_ERR_NULL;
   if (quantized == (x_bf16 != nullptr)) return FP8RL_ERR_NULL;  // exactly one form of X
@@ -276,10 +303,17 @@ fp8rl_status fwd_impl(const uint8_t* xq, const float* sx, const uint16_t* x_bf16
   if (quantized && (!aligned(xq, 16) || !aligned(sx, 4))) return FP8RL_ERR_ALIGN;
   if (!quantized) {
     if (!aligned(x_bf16, 16)) return FP8RL_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < fp8rl_fwd_workspace_bytes(M, K)) return FP8RL_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+    if (noalloc) {
+      if (fp8rl_fwd_workspace_bytes(M, K) > FP8RL_NOALLOC_SCRATCH_BYTES) return FP8RL_ERR_WORKSPACE;
+    } else {
+      if (workspace == nullptr || workspace_bytes < fp8rl_fwd_workspace_bytes(M, K)) return FP8RL_ERR_WORKSPACE;
+      if (!aligned(workspace, 16)) return FP8RL_ERR_ALIGN;
+    }
   }
   if (fp8rl_status e = check_device()) return e;
+  if (!quantized && noalloc) {
+    if (fp8rl_status e = scratch_address(&workspace)) return e;
+  }
   hipStream_t st = as_stream(stream);
   uint8_t* wsq = nullptr;
   float* wss = nullptr;
@@ -355,6 +389,12 @@ fp8rl_status fp8_gemm_blockscaled_fwd_decode_layout(const uint8_t* xq, const flo
                                                     int64_t K, void* y, int y_dtype, void* workspace,
                                                     size_t workspace_bytes, void* stream) {
   return fwd_impl(xq, sx, x_bf16, wq, sw, M, N, K, y, y_dtype, workspace, workspace_bytes, true, stream);
+}
+
+fp8rl_status fp8_gemm_blockscaled_fwd_decode_layout_noalloc(const uint8_t* xq, const float* sx, const uint16_t* x_bf16,
+                                                            const uint8_t* wq, const float* sw, int64_t M, int64_t N,
+                                                            int64_t K, void* y, int y_dtype, void* stream) {
+  return fwd_impl(xq, sx, x_bf16, wq, sw, M, N, K, y, y_dtype, nullptr, 0, true, stream, true);
 }
 
 fp8rl_status fp8_gemm_blockscaled_pow2_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,

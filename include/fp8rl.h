@@ -50,7 +50,8 @@ typedef enum {
   FP8RL_ERR_RECIPE = 4,    /* unknown / unsupported recipe or dtype, or install descriptors disagree */
   FP8RL_ERR_DEVICE = 5,    /* current HIP device is not gfx950, or it could not be queried */
   FP8RL_ERR_LAUNCH = 6,    /* kernel launch failed */
-  FP8RL_ERR_WORKSPACE = 7, /* workspace missing or smaller than fp8rl_fwd_workspace_bytes() */
+  FP8RL_ERR_WORKSPACE = 7, /* workspace missing or smaller than fp8rl_fwd_workspace_bytes(), or that size
+                              exceeds FP8RL_NOALLOC_SCRATCH_BYTES in the allocation-free call */
   FP8RL_ERR_VALUE = 8      /* a scalar argument is out of range (e.g. eps not positive and finite) */
 } fp8rl_status;
 
@@ -230,6 +231,22 @@ fp8rl_status fp8_gemm_blockscaled_fwd_decode_layout(const uint8_t* xq, const flo
                                                     int64_t M, int64_t N, int64_t K,
                                                     void* y, int y_dtype,
                                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free variant of fp8_gemm_blockscaled_fwd_decode_layout, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same product, arguments and rules without the workspace. The
+ * bf16-input form quantizes X into a device array built into the library (the library's own
+ * scratch, FP8RL_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held until the process
+ * ends), so the call allocates nothing. FP8RL_ERR_WORKSPACE when
+ * fp8rl_fwd_workspace_bytes(M, K) exceeds FP8RL_NOALLOC_SCRATCH_BYTES. All calls on one GPU
+ * share that array: calls that may overlap on one GPU (different streams, or host threads)
+ * race and must be serialised by the caller; calls in order on one stream are safe. */
+#define FP8RL_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fp8rl_status fp8_gemm_blockscaled_fwd_decode_layout_noalloc(const uint8_t* xq, const float* sx,
+                                                            const uint16_t* x_bf16,
+                                                            const uint8_t* wq, const float* sw,
+                                                            int64_t M, int64_t N, int64_t K,
+                                                            void* y, int y_dtype, void* stream);
 
 /* DGrad: dX[M][K] = deq(dY) . deq(W)  ([Jet-RL] "Quantization scheme": DGrad in FP8).
  *   dyq uint8 [M][N], sdy fp32 [M][N/128]  (dY quantized 1x128 along N)

@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
               "fp8_quant_w_128x128_pow2", "fp8_gemm_blockscaled_pow2_fwd", "fp8_gemm_blockscaled_pow2_dgrad",
               "fp8_gemm_blockscaled_pow2_wgrad", "fp8_swiglu_bf16", "fp8_swiglu_quant_1x128", "fp8_rmsnorm_bf16",
               "fp8_rmsnorm_quant_1x128", "mxfp8_quant_act_1x32", "fp8_gemm_mxfp8_fwd", "fp8_gemm_mxfp8_dgrad",
-              "fp8_gemm_mxfp8_wgrad", "fp8_quant_w_128x128_f32", "fp8_gemm_blockscaled_fwd_decode_layout"]:
+              "fp8_gemm_mxfp8_wgrad", "fp8_quant_w_128x128_f32", "fp8_gemm_blockscaled_fwd_decode_layout",
+              "fp8_gemm_blockscaled_fwd_decode_layout_noalloc"]:
         assert n in names
 
 
