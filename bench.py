@@ -1,6 +1,6 @@
 """Benchmark of the FP8 block-scaled hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-graph]
                     [--workload dense|dense_pow2|decode|backward|backward_pow2|moe|moe_block128|install|producers|mx_dense|fp8_param] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input, inputs resident in
@@ -18,6 +18,13 @@ the pass in which every kernel is also timed by HIP events (`--no-graph`: eager 
 `roofline` reports the dominant kernel (the gate/up GEMM) from the HIP events of the eager
 pass, recorded on the stream the library launches on, against the 5.0 PFLOP/s dense FP8
 MFMA peak; `quant_roofline` the X quantizer against 8 TB/s HBM.
+
+The default run also measures one short pass (10 steps) of each of the decode, backward and
+MoE workloads with their own rooflines, under "also" (--no-also skips them); the decode
+pass carries the weight-sync figures: the installed weights' error (0: the rollout runs on
+the trainer's bytes, and trainer and rollout outputs are compared bit for bit) and the naive
+dequantize -> bf16 -> per-tensor requantize path's mean relative error and Frobenius ratio
+per weight, computed with the oracle on the host before the GPU is used.
 
 Other workloads (--workload) time the decode, backward, MoE and weight-install paths the
 same way; dense_pow2 and backward_pow2 run the dense layer with power-of-two block scales,
@@ -114,6 +121,8 @@ def _args():
                                                          "moe_block128", "install", "producers", "mx_dense", "fp8_param"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the eager steps only (no HIP graph replay)")
+    ap.add_argument("--no-also", action="store_true",
+                    help="dense workload only: skip the extra decode, backward and MoE passes")
     return ap.parse_args()
 
 
@@ -201,22 +210,37 @@ def dense_setup(torch, F, W, dev, pow2=False):
     return step, timers, info
 
 
+_DECODE_DATA = {}
+
+
+def decode_data(W):
+    """The decode workload's synthetic activations and weights (generated once per process)."""
+    if not _DECODE_DATA:
+        _DECODE_DATA.update(W.decode_rollout())
+    return _DECODE_DATA
+
+
 def decode_setup(torch, F, W, dev):
-    d = W.decode_rollout()
+    d = decode_data(W)
     x = W.to_bf16_tensor(d["x"]).to(dev)
     M, K = x.shape
     set_bytes = sum(n * K + (n // 128) * (K // 128) * 4 for n in W.DECODE_N)
     n_sets = -(-ROTATE_BYTES // set_bytes)
     sets = [dict() for _ in range(n_sets)]
     ys = {}
+    bitwise = {}
     for n in W.DECODE_N:
         wq, sw, _ = F.fp8_quant_w_128x128(W.to_bf16_tensor(d[f"w{n}"]).to(dev))
-        for st in sets:     # installed (rollout-owned) copies, identical bytes
+        for st in sets:     # installed (rollout-owned) copies in the decode layout, the trainer's bytes
             iq, is_ = torch.empty_like(wq), torch.empty_like(sw)
             F.fp8_weight_install(wq, sw, iq, is_, layout=F.LAYOUT_DECODE)
             st[n] = (iq, is_)
         ys[n] = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
-        del wq, sw
+        # trainer forward (row-major payload) vs rollout forward (installed copy), outside the timed steps
+        y_train = F.fp8_gemm_blockscaled_fwd(wq=wq, sw=sw, x_bf16=x)
+        y_roll = F.fp8_gemm_blockscaled_fwd_decode_layout(wq=sets[0][n][0], sw=sets[0][n][1], x_bf16=x, N=n, K=K)
+        bitwise[str(n)] = bool(torch.equal(y_train.view(torch.int16), y_roll.view(torch.int16)))
+        del wq, sw, y_train, y_roll
     ws = F.fwd_workspace(M, K, dev)
     timers = {f"decode_n{n}": EventTimer(torch) for n in W.DECODE_N}
     it = [0]
@@ -232,15 +256,71 @@ def decode_setup(torch, F, W, dev):
     nmax = max(W.DECODE_N)
     info = dict(
         config={"workload": "decode_rollout", "rows_M": M, "K": K, "N": list(W.DECODE_N),
-                "activations": "bf16, quantized 1x128 inside the call", "weights": "installed E4M3 128x128, decode layout (16x128 tiles in MFMA operand order)",
+                "activations": "bf16, quantized 1x128 inside each call (quantizer launch + GEMM launch)",
+                "weights": "installed E4M3 128x128, decode layout (16x128 tiles in MFMA operand order)",
                 "weight_copies": n_sets},
         flops=sum(2.0 * M * n * K for n in W.DECODE_N),
         dominant=(f"decode_n{nmax}", "hbm", (nmax * K + nmax * K // 128 // 128 * 4) / 1e9, "GB/s", PEAK_HBM_GBS,
-                  "weight stream: E4M3 payload + fp32 block scales per launch"),
+                  "weight stream: E4M3 payload + fp32 block scales per call (the call is the 1x128 quantizer "
+                  "launch + the GEMM launch)"),
         quant=None,
         gemm_keys=tuple(timers),
+        weight_sync={"installed_rel_error": 0.0, "installed_output_bitwise_equal": bitwise},
     )
     return step, timers, info
+
+
+# The naive weight-sync control ([SkyRL-FP8] "When independent quantization breaks policy
+# consistency", Fig. 2): each decode weight quantized 128x128, dequantized to bf16 and
+# requantized per tensor, its mean relative error and Frobenius ratio against the trainer's
+# dequantized weight. Oracle arithmetic on the host, over 1024-row chunks in a process pool
+# forked before the GPU is touched: pass 1 quantizes and finds the tensor maximum, pass 2
+# requantizes with the tensor's scale and sums the errors.
+_NAIVE_W = {}
+
+
+def _naive_pass1(task):
+    from oracle import quantize as OQ, weight_sync as WS
+    n, r0, r1 = task
+    q, s = OQ.quant_w_128x128(_NAIVE_W[n][r0:r1])
+    return n, q, s, float(np.max(np.abs(WS.dequant_to_bf16(q, s))))
+
+
+def _naive_pass2(task):
+    from oracle import weight_sync as WS
+    n, q, s, s_t = task
+    q2 = WS.requant_per_tensor(WS.dequant_to_bf16(q, s), s_t)
+    a = WS.weight_value_block(q, s)
+    d = WS.weight_value_tensor(q2, s_t) - a
+    return n, float(np.sum(np.abs(d))), float(np.sum(np.abs(a))), float(np.sum(d * d)), float(np.sum(a * a))
+
+
+def naive_weight_sync_errors(W):
+    import multiprocessing as mp
+    from oracle import weight_sync as WS
+    t0 = time.perf_counter()
+    d = decode_data(W)
+    _NAIVE_W.update({n: d[f"w{n}"] for n in W.DECODE_N})
+    tasks = [(n, r, min(r + 1024, w.shape[0])) for n, w in _NAIVE_W.items() for r in range(0, w.shape[0], 1024)]
+    procs = max(1, min(16, os.cpu_count() or 1))
+    with mp.get_context("fork").Pool(procs) as pool:
+        p1 = pool.map(_naive_pass1, tasks)
+        amax = {}
+        for n, _, _, m in p1:
+            amax[n] = max(amax.get(n, 0.0), m)
+        s_t = {n: WS.per_tensor_scale(amax[n]) for n in amax}
+        p2 = pool.map(_naive_pass2, [(n, q, s, s_t[n]) for n, q, s, _ in p1])
+    _NAIVE_W.clear()
+    acc = {}
+    for n, ad, aa, dd, a2 in p2:
+        t = acc.setdefault(n, [0.0, 0.0, 0.0, 0.0])
+        t[0] += ad; t[1] += aa; t[2] += dd; t[3] += a2
+    out = {str(n): {"mean_rel_error": round(t[0] / t[1], 5), "frobenius_ratio": round(float(np.sqrt(t[2] / t[3])), 5),
+                    "per_tensor_scale": float(s_t[n])} for n, t in sorted(acc.items())}
+    return {"naive_rel_error": out, "processes": procs, "seconds": round(time.perf_counter() - t0, 1),
+            "how": "oracle: 128x128 quantization, dequantize to bf16, per-tensor requantization (amax/448); "
+                   "error = sum|w_naive - w_trainer| / sum|w_trainer|, Frobenius ratio ||w_naive - w_trainer|| / "
+                   "||w_trainer||; the page quotes 0.038 on a 4B model"}
 
 
 def backward_setup(torch, F, W, dev, pow2=False):
@@ -414,7 +494,9 @@ def moe_setup(torch, F, W, dev):
     fl_gu, fl_dn = 2.0 * T * N * K, 2.0 * T * N2 * K2
     info = dict(
         config={"workload": "moe_mxfp8_grouped", "routed_rows_T": T, "experts": E, "gate_up": [N, K],
-                "down": [N2, K2], "routing": "Zipf(1.1) top-8"},
+                "down": [N2, K2], "routing": "Zipf(1.1) top-8",
+                "weights": "expert weights MXFP8-quantized once before the timed steps (as installed for a rollout); "
+                           "the step quantizes the activations and runs both grouped GEMMs"},
         flops=fl_gu + fl_dn,
         dominant=("grouped_gu", "mfma", fl_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
                   f"2*T*N*K = {fl_gu:.4g} FLOP per launch"),
@@ -691,51 +773,39 @@ def cpu_baseline(workload: str, budget_s: float = 12.0):
             "sample": f"{reps} x {what}", "seconds": round(dt, 2)}
 
 
-def main():
-    a = _args()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on a single MI355X).",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    import fp8_block_scaled_quant_amd as F
-    import workloads as W
-
-    dev = torch.device("cuda", 0)
-    F.load_library()
+def measure(workload, steps, warmup, no_graph, torch, F, W, dev):
+    """Set up one workload, run `warmup` untimed steps, time `steps` eager steps (HIP events around
+    every kernel on the library's stream), then the next `steps` steps captured into one HIP
+    graph (one untimed replay, one timed replay). Returns the workload's part of the JSON line."""
     setup = {"dense": dense_setup, "dense_pow2": lambda *args: dense_setup(*args, pow2=True), "decode": decode_setup,
-             "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True), "moe": moe_setup, "moe_block128": moe_block128_setup,
-             "install": install_setup, "producers": producers_setup, "mx_dense": mx_dense_setup,
-             "fp8_param": fp8_param_setup}[a.workload]
+             "backward": backward_setup, "backward_pow2": lambda *args: backward_setup(*args, pow2=True),
+             "moe": moe_setup, "moe_block128": moe_block128_setup, "install": install_setup,
+             "producers": producers_setup, "mx_dense": mx_dense_setup, "fp8_param": fp8_param_setup}[workload]
     step, timers, info = setup(torch, F, W, dev)
 
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
-    # Eager pass: K steps launched one call at a time, with HIP events around every kernel
-    # launch on the library's stream (the per-kernel times and the roofline come from here).
     t0 = time.perf_counter()
-    for _ in range(a.steps):
+    for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step_eager = wall / a.steps * 1e3
+    ms_per_step_eager = (time.perf_counter() - t0) / steps * 1e3
     ms_per_step = ms_per_step_eager
-    if not a.no_graph:
-        # Graph pass: the next K steps (the same calls, continuing any input rotation) are
-        # captured once into a HIP graph, which removes the launch gaps between dependent
-        # kernels; one untimed replay, then one timed replay of exactly K steps.
+    if not no_graph:
+        # The same calls (continuing any input rotation) captured once, which removes the launch
+        # gaps between dependent kernels.
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for _ in range(a.steps):
+            for _ in range(steps):
                 step(False)
         graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         graph.replay()
         torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) / a.steps * 1e3
+        ms_per_step = (time.perf_counter() - t0) / steps * 1e3
+        del graph
 
     breakdown = {k: round(v.mean_ms() * 1e3, 2) for k, v in timers.items()}          # microseconds
     name, bound, per_launch, unit, peak, per_unit = info["dominant"]
@@ -747,21 +817,12 @@ def main():
         value, vunit = round(info["flops"] / (ms_per_step * 1e-3) / 1e12, 2), "TFLOP/s"
     else:
         value, vunit = round(info["bytes"] / (ms_per_step * 1e-3) / 1e9, 1), "GB/s"
-    out = {
-        "metric": METRIC,
+    rec = {
         "value": value,
         "unit": vunit,
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_eager": round(ms_per_step_eager, 4),
-        "step_launch": "eager" if a.no_graph else "hip_graph",
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate",
-        "data": "synthetic",
+        "step_launch": "eager" if no_graph else "hip_graph",
         "config": info["config"],
         "roofline": {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic, "traffic_unit": "GB per launch (HBM)",
@@ -769,11 +830,11 @@ def main():
         "kernel_us": breakdown,
     }
     if info["gemm_keys"]:
-        out["gemm_tflops"] = round(info["flops"] / (gemm_ms * 1e-3) / 1e12, 2)
+        rec["gemm_tflops"] = round(info["flops"] / (gemm_ms * 1e-3) / 1e12, 2)
     if info["quant"] is not None:
         qname, qgb, qdesc = info["quant"]
         qms = timers[qname].mean_ms()
-        out["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
+        rec["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
                                  "per_launch": qdesc}
     if "algorithmic_gb" in info:
@@ -781,11 +842,60 @@ def main():
         # peak FLOP/s / peak B/s) cannot reach the MFMA peak: report the attainable rate too.
         ai = info["dominant"][2] * 1e12 / (info["algorithmic_gb"] * 1e9)
         attainable = min(peak, ai * PEAK_HBM_GBS / 1e3)
-        out["roofline"]["arithmetic_intensity"] = round(ai, 1)
-        out["roofline"]["attainable"] = round(attainable, 1)
-        out["roofline"]["frac_attainable"] = round(achieved / attainable, 4)
+        rec["roofline"]["arithmetic_intensity"] = round(ai, 1)
+        rec["roofline"]["attainable"] = round(attainable, 1)
+        rec["roofline"]["frac_attainable"] = round(achieved / attainable, 4)
     if "extra" in info:
-        out["unfused_kernel_us"] = info["extra"]()
+        rec["unfused_kernel_us"] = info["extra"]()
+    if "weight_sync" in info:
+        rec["weight_sync"] = info["weight_sync"]
+    return rec
+
+
+# Workloads the default run (the dense layer) also measures, one short pass each, so that
+# one line carries the decode, backward and MoE figures next to the headline.
+ALSO = ("decode", "backward", "moe")
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on a single MI355X).",
+              file=sys.stderr)
+        sys.exit(2)
+    import workloads as W
+
+    also = ALSO if (a.workload == "dense" and not a.no_also) else ()
+    naive = None
+    if a.workload == "decode" or "decode" in also:
+        naive = naive_weight_sync_errors(W)      # host work in forked processes, before any GPU use
+
+    import gc
+
+    import torch
+
+    import fp8_block_scaled_quant_amd as F
+
+    dev = torch.device("cuda", 0)
+    F.load_library()
+    rec = measure(a.workload, a.steps, a.warmup, a.no_graph, torch, F, W, dev)
+    out = {"metric": METRIC, "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": rec.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate", "data": "synthetic"}
+    out.update(rec)
+    if a.workload == "decode":
+        out["weight_sync"].update(naive)
+    if also:
+        out["also"] = {}
+        for wl in also:
+            gc.collect()
+            torch.cuda.empty_cache()
+            steps, warmup = min(a.steps, 10), min(a.warmup, 2)
+            r = measure(wl, steps, warmup, a.no_graph, torch, F, W, dev)
+            r["steps"], r["warmup"] = steps, warmup
+            if wl == "decode":
+                r["weight_sync"].update(naive)
+            out["also"][wl] = r
     if not a.no_cpu_baseline and a.workload not in ("install", "fp8_param"):
         out["cpu_baseline"] = cpu_baseline(a.workload)
     print(json.dumps(out))

@@ -35,21 +35,37 @@ def install(q, s):
     return np.array(q, dtype=np.uint8, copy=True), np.array(s, copy=True)
 
 
+def dequant_to_bf16(q, s):
+    """First step of the naive path: the 128x128-block weight dequantized in fp32
+    (fl32(dec(q) * s)) and rounded to bf16 (float32 array of bf16 values). Elementwise, so
+    any split into 128-row blocks gives the same values."""
+    q = np.asarray(q, dtype=np.uint8)
+    s = np.asarray(s, dtype=np.float32)
+    s_full = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+    w32 = decode_e4m3(q).astype(np.float32) * s_full           # fp32 product, IEEE rounding
+    return round_to_bf16(w32)
+
+
+def per_tensor_scale(amax) -> np.float32:
+    """The rollout recipe's per-tensor scale fl32(amax / 448) of the bf16 tensor (1 if all zero)."""
+    amax = np.float32(amax)
+    return np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(E4M3_MAX))
+
+
+def requant_per_tensor(wb, s_t):
+    """Last step of the naive path: E4M3(fl32(w' / s_t)), elementwise."""
+    return encode_e4m3(np.asarray(wb, dtype=np.float32) / np.float32(s_t))
+
+
 def naive_resync(q, s):
     """Dequantize a 128x128-block weight to bf16 and requantize it per tensor.
 
     Returns (q' uint8 [N][K], s_t float32 scalar).
     """
-    q = np.asarray(q, dtype=np.uint8)
-    s = np.asarray(s, dtype=np.float32)
-    N, K = q.shape
-    s_full = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
-    w32 = decode_e4m3(q).astype(np.float32) * s_full           # fp32 product, IEEE rounding
-    wb = round_to_bf16(w32)
+    wb = dequant_to_bf16(q, s)
     amax = np.float32(np.max(np.abs(wb))) if wb.size else np.float32(0)
-    s_t = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(E4M3_MAX))
-    q2 = encode_e4m3(wb / s_t)
-    return q2, s_t
+    s_t = per_tensor_scale(amax)
+    return requant_per_tensor(wb, s_t), s_t
 
 
 def mean_relative_error(w_ref, w_other) -> float:

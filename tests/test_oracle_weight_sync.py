@@ -8,7 +8,7 @@ import numpy as np
 from oracle import quantize as Q
 from oracle.fp8_formats import decode_e4m3
 from oracle import weight_sync as S
-from workloads import normal_bf16
+from workloads import bf16_round, normal_bf16
 
 
 def test_install_is_verbatim():
@@ -103,3 +103,26 @@ def test_naive_resync_brute_force():
     assert np.array_equal(q2.astype(np.int64), codes)
     assert q2[3, 130] == 0x38 and q2[4, 131] == 0xB8            # bf16 midpoint -> even code 1.0
     assert skip[3, 130] == 0x39 and skip[4, 131] == 0xB9        # without the bf16 step: 1.125
+
+
+def test_naive_path_by_row_blocks_equals_whole_tensor():
+    """Split into 128-row blocks with the tensor scale taken from the maximum of the blocks'
+    maxima, the naive path gives the whole tensor's bytes and scale, and its error sums add
+    up to the whole tensor's mean relative error (how the benchmark evaluates it in
+    parallel)."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((512, 256)) * 0.02).astype(np.float32)
+    w[300, 7] = 0.9                                     # the tensor maximum sits in one block only
+    q, s = Q.quant_w_128x128(bf16_round(w))
+    q2, s_t = S.naive_resync(q, s)
+    parts = [S.dequant_to_bf16(q[r:r + 128], s[r // 128:r // 128 + 1]) for r in range(0, 512, 128)]
+    s_t_b = S.per_tensor_scale(max(np.max(np.abs(p)) for p in parts))
+    assert s_t_b == s_t
+    q2_b = np.concatenate([S.requant_per_tensor(p, s_t_b) for p in parts])
+    assert np.array_equal(q2_b, q2)
+    a = S.weight_value_block(q, s)
+    b = S.weight_value_tensor(q2, s_t)
+    num = sum(float(np.sum(np.abs(S.weight_value_tensor(q2_b[r:r + 128], s_t_b)
+                                  - S.weight_value_block(q[r:r + 128], s[r // 128:r // 128 + 1]))))
+              for r in range(0, 512, 128))
+    assert abs(num / float(np.sum(np.abs(a))) - S.mean_relative_error(a, b)) < 1e-12
