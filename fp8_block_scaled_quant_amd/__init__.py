@@ -43,7 +43,8 @@ OUT_BF16 = 0
 OUT_F32 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libfp8rl.so")
+# FP8RL_LIBRARY names another build of the library (the sanitizer test loads one that way).
+_LIB_PATH = os.environ.get("FP8RL_LIBRARY") or os.path.join(_HERE, "libfp8rl.so")
 _lib = None
 
 _vp = ctypes.c_void_p

@@ -84,7 +84,7 @@ extern "C" {
 
 int fp8rl_abi_version(void) { return FP8RL_ABI_VERSION; }
 
-const char* fp8rl_status_str(fp8rl_status s) {
+const char* fp8rl_status_str(int s) {
   switch (s) {
     case FP8RL_OK: return "ok";
     case FP8RL_ERR_NULL: return "required pointer is NULL (or an output pair is half given)";

@@ -77,7 +77,8 @@ typedef enum {
 /* ABI version of this header. */
 #define FP8RL_ABI_VERSION 7
 int fp8rl_abi_version(void);
-const char* fp8rl_status_str(fp8rl_status status);
+/* Text of a status code; any int is accepted ("unknown status" outside the enum). */
+const char* fp8rl_status_str(int status);
 
 /* ---------------------------------------------------------------------------------------
  * Quantizers. The quantizer is the symmetric one of [AIS] (quantizer equation), with the
