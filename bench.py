@@ -145,9 +145,11 @@ class EventTimer:
         e.record()
         self.pairs[-1][1] = e
 
-    def mean_ms(self):
+    def per_launch_ms(self):
+        """Median over the launches (one host stall between a pair of events, e.g. the first call
+        of a pass waiting on the host, would otherwise dominate a mean over a few calls)."""
         ts = [a.elapsed_time(b) for a, b in self.pairs]
-        return float(np.mean(ts)) if ts else float("nan")
+        return float(np.median(ts)) if ts else float("nan")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -658,7 +660,7 @@ def producers_setup(torch, F, W, dev):
             F.fp8_quant_act_1x128(h, q=b["hq"], s=b["hs"], qt=b["hqt"], st=b["hst"], colwise=True)
             if tm: tm["quant_h"].stop()
         torch.cuda.synchronize()
-        return {k: round(v.mean_ms() * 1e3, 2) for k, v in t.items()}
+        return {k: round(v.per_launch_ms() * 1e3, 2) for k, v in t.items()}
 
     # algorithmic bytes: bf16 inputs once, both FP8 copies, both scale sets (+ gamma, r)
     sw_bytes = M * F2 * 2 + 2 * M * Fh + 2 * (M * Fh // 128) * 4
@@ -809,11 +811,11 @@ def measure(workload, steps, warmup, no_graph, torch, F, W, dev):
         ms_per_step = (time.perf_counter() - t0) / steps * 1e3
         del graph
 
-    breakdown = {k: round(v.mean_ms() * 1e3, 2) for k, v in timers.items()}          # microseconds
+    breakdown = {k: round(v.per_launch_ms() * 1e3, 2) for k, v in timers.items()}          # microseconds
     name, bound, per_launch, unit, peak, per_unit = info["dominant"]
-    dom_ms = timers[name].mean_ms()
+    dom_ms = timers[name].per_launch_ms()
     achieved = per_launch / (dom_ms * 1e-3)
-    gemm_ms = sum(timers[k].mean_ms() for k in info["gemm_keys"])
+    gemm_ms = sum(timers[k].per_launch_ms() for k in info["gemm_keys"])
     traffic, sha = _traffic(info.get("traffic_key", name))
     if info["flops"] is not None:
         value, vunit = round(info["flops"] / (ms_per_step * 1e-3) / 1e12, 2), "TFLOP/s"
@@ -835,7 +837,7 @@ def measure(workload, steps, warmup, no_graph, torch, F, W, dev):
         rec["gemm_tflops"] = round(info["flops"] / (gemm_ms * 1e-3) / 1e12, 2)
     if info["quant"] is not None:
         qname, qgb, qdesc = info["quant"]
-        qms = timers[qname].mean_ms()
+        qms = timers[qname].per_launch_ms()
         rec["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
                                  "per_launch": qdesc}

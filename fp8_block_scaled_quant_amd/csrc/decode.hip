@@ -48,32 +48,30 @@ namespace fp8rl {
 namespace {
 
 constexpr int kDecodeLag = 3;
-// The weight loads and the direct-to-LDS copies are issued through the LLVM buffer-load
-// intrinsics, not inline assembly: the compiler then knows which registers a load has not
-// filled yet and puts an exact vmcnt wait in front of any use, copy or spill of them, and it
-// counts the copies when computing those waits (it also sets m0 and keeps the wait states
-// buffer instructions need). With asm loads it would treat the registers as ready at once and
-// could move them (say, to AGPRs under register pressure) before the data arrived.
-typedef __attribute__((address_space(3))) uint8_t* lds_bytes_t;
-extern "C" __device__ void fp8rl_raw_buffer_load_lds(v4i rsrc, lds_bytes_t lds, int size, int voffset, int soffset,
-                                                     int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-extern "C" __device__ v4i fp8rl_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
-
-__device__ __forceinline__ v4i bload16(v4i rsrc, uint32_t voff) {
-  return fp8rl_raw_buffer_load_v4i32(rsrc, (int)voff, 0, 0);
+// Every load and copy of the K loop is inline assembly, and every wait for them is explicit:
+// the compiler inserts no wait of its own in the loop. (With the loads expressed as compiler
+// intrinsics, its wait analysis merged the states of the loop's guarded steps and of the
+// loop back-edge, and in some unrolled steps waited for the next K block's loads as well,
+// i.e. ran without prefetch.) A weight register is therefore written by the hardware after
+// the compiler believes it holds its value; the kernel reads it only after the wait for
+// its K block, and the register must not be moved, copied, spilled or reused before then.
+// The kernel is built for at most 256 VGPRs and no AGPRs (two waves per SIMD), and a test
+// scans the compiled code of every configuration for any access to a weight register
+// between its load and the wait that covers it.
+template <int OFF>
+__device__ __forceinline__ v4i wload16(v4i rsrc, uint32_t voff) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate buffer offset");
+  v4i r;
+  // s_nop 4: wait states after a VALU write of the descriptor's SGPRs (see dma16).
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3"
+               : "=v"(r)
+               : "v"(voff), "s"(rsrc), "i"(OFF)
+               : "memory");
+  return r;
 }
-// Lane i's 16 (or 4) bytes from rsrc + voff land at LDS byte lds + 16 i (or 4 i); lds is
-// wave-uniform.
-__device__ __forceinline__ void copy16(v4i rsrc, uint32_t voff, lds_bytes_t lds) {
-  fp8rl_raw_buffer_load_lds(rsrc, lds, 16, (int)voff, 0, 0, 0);
-}
-__device__ __forceinline__ void copy4(v4i rsrc, uint32_t voff, lds_bytes_t lds) {
-  fp8rl_raw_buffer_load_lds(rsrc, lds, 4, (int)voff, 0, 0, 0);
-}
-// Workgroup barrier that orders memory operations around it for the compiler but adds no
-// wait of its own (__syncthreads() would wait for every copy in flight, prefetches included);
-// the K loop waits for exactly the copies it needs before it.
+// Workgroup barrier with no wait of its own (__syncthreads() would also wait for every
+// copy in flight, prefetches included); the K loop waits for exactly the copies it needs
+// before it.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int MT, int NW, int FW, int P>
@@ -86,10 +84,12 @@ struct DecodeShape {
   static constexpr int LX = MT * 8 / NT;             // A copies (16 B per lane) per wave per K block
   static constexpr int OFF_SA = MT * 128;
   static constexpr int OFF_SB = OFF_SA + MT * 4;
-  static constexpr int STAGE = OFF_SB + 256;
+  static constexpr int OFF_NIL = OFF_SB + 256;       // scale copies of waves that have none
+  static constexpr int STAGE = OFF_NIL + 256;
   static constexpr int LDS = NS * STAGE;
   static constexpr int SA_WAVES = (MT + 63) / 64;    // waves that copy A's row scales
   static constexpr int SB_WAVE = SA_WAVES % NW;      // the wave that copies B's fragment scales
+  static constexpr int OPS = MT * 8 / NT + 2 + 2 * FW; // vector-memory operations per wave and K block
   static_assert(MT % 64 == 0 && MT <= 256, "row part");
   static_assert((MT * 8) % NT == 0 && (NT / 8) % 16 == 0, "A copy split keeps the swizzle phase");
   static_assert(F <= 64, "one B fragment scale per lane");
@@ -141,7 +141,7 @@ hipError_t launch_quant_kbmajor(const uint16_t* x, int64_t M, int64_t K, uint8_t
 
 // kTiledB: B is in the decode layout.
 template <int MT, int NW, int FW, int P, bool kF32, bool kTiledB>
-__global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_decode(DecodeParams p) {
   using S = DecodeShape<MT, NW, FW, P>;
   constexpr int NT = S::NT, XF = S::XF, NS = S::NS, LX = S::LX;
   static_assert(S::LDS <= 160 * 1024, "LDS budget");
@@ -204,36 +204,35 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < FW; ++i) {
       const uint32_t o = offB + ok + (uint32_t)(i * 16) * (uint32_t)K;
-      wlo[set][i] = bload16(rb, o);
-      whi[set][i] = bload16(rb, o + (kTiledB ? 1024u : 64u));
+      wlo[set][i] = wload16<0>(rb, o);
+      whi[set][i] = wload16<kTiledB ? 1024 : 64>(rb, o);
     }
   };
-  // The activation and scale copies of K block kb into stage `set`.
+  // The activation and scale copies of K block kb into stage `set`. Every wave issues both
+  // scale copies; a wave without scales to copy issues them through empty descriptors (no
+  // memory access) into the stage's unused slot, so that every wave has the same number of
+  // operations in flight and one wait count serves all.
+  const uint32_t st0 = lds_addr(smem);
+  const uint32_t dSA = cA ? S::OFF_SA + wave * 256 : S::OFF_NIL;
+  const uint32_t dSB = cB ? S::OFF_SB : S::OFF_NIL;
   auto issue_a = [&](int kb, auto setc) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
-    lds_bytes_t st = (lds_bytes_t)smem + set * S::STAGE;  // generic -> LDS address space
+    const uint32_t st = st0 + set * S::STAGE;
     const bool live = kb < nkb;
     const int64_t kbc = live ? kb : 0;
     const v4i ra = make_rsrc(p.A + kbc * p.a_kb, live ? rng(a_total, (uint64_t)(kbc * p.a_kb)) : 0u);
 #pragma unroll
     for (int it = 0; it < LX; ++it)
-      copy16(ra, offA + (uint32_t)(it * (NT / 8)) * (uint32_t)p.a_ld, st + (it * NT + wave * 64) * 16);
-    if (cA)
-      copy4(make_rsrc(p.sA + kbc * p.sa_kb, live ? rng(sa_total, (uint64_t)(kbc * p.sa_kb) * 4) : 0u), offSA,
-           st + S::OFF_SA + wave * 256);
-    if (cB)
-      copy4(make_rsrc(p.sB + kbc * p.sb_ld_k, live ? rng(sb_total, (uint64_t)(kbc * p.sb_ld_k) * 4) : 0u), offSB,
-           st + S::OFF_SB);
+      dma16(ra, offA + (uint32_t)(it * (NT / 8)) * (uint32_t)p.a_ld, st + (it * NT + wave * 64) * 16);
+    dma4(make_rsrc(p.sA + kbc * p.sa_kb, live && cA ? rng(sa_total, (uint64_t)(kbc * p.sa_kb) * 4) : 0u), offSA,
+         st + dSA);
+    dma4(make_rsrc(p.sB + kbc * p.sb_ld_k, live && cB ? rng(sb_total, (uint64_t)(kbc * p.sb_ld_k) * 4) : 0u), offSB,
+         st + dSB);
   };
-  // Vector-memory operations per K block of this wave: LX + (cA) + (cB) + 2 FW; at the wait
-  // of K block kb, those of kb+1 .. kb+P-1 may stay outstanding.
-  constexpr int LBASE = LX + 2 * FW;
-  const int cnt = (cA ? 1 : 0) + (cB ? 1 : 0);
-  auto wait_block = [&]() __attribute__((always_inline)) {
-    if (cnt == 0) wait_vmem_n<(P - 1) * LBASE>();
-    else if (cnt == 1) wait_vmem_n<(P - 1) * (LBASE + 1)>();
-    else wait_vmem_n<(P - 1) * (LBASE + 2)>();
-  };
+  // Operations per wave and K block: LX activation copies, 2 scale copies, 2 FW weight
+  // loads (OPS). At the wait of K block kb those of kb+1 .. kb+P-1 stay outstanding.
+  static_assert((P - 1) * S::OPS <= 63, "vmcnt range");
+  auto wait_block = [&]() __attribute__((always_inline)) { wait_vmem_n<(P - 1) * S::OPS>(); };
 
   v4f acc[FW][XF];
 #pragma unroll
@@ -246,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
 
   auto compute = [&](auto setc) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
-    const uint32_t st = lds_addr(smem) + set * S::STAGE;
+    const uint32_t st = st0 + set * S::STAGE;
     const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi, sa_ad = st + o_sa;
     const uint32_t sb_ad = st + S::OFF_SB + wave * FW * 4;
     float sb[FW];
@@ -308,26 +307,37 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_decode(DecodeParams p) {
   };
 
   {
-    // Prologue: weights of K blocks 0 .. P-1, then the activation copies; the first step
-    // waits for all of them.
-    static_for<0, P>([&](auto sc) { issue_b(decltype(sc)::value, sc); });
-    static_for<0, P>([&](auto sc) { issue_a(decltype(sc)::value, sc); });
+    // Prologue: K blocks 0 .. P-1 in the loop's own order (copies, then weights), so the
+    // first step's wait is the same as every other step's. The loop issues loads and copies
+    // in every step, also in the at most NS - 1 steps past the last K block (empty
+    // descriptors); only the compute is skipped there. Every path through the loop thus
+    // issues the same operations and the wait counts hold on all of them.
+    static_for<0, P>([&](auto sc) {
+      issue_a(decltype(sc)::value, sc);
+      issue_b(decltype(sc)::value, sc);
+    });
     for (int kb0 = 0; kb0 < nkb; kb0 += NS) {
       static_for<0, NS>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         const int kb = kb0 + s;
-        if (kb < nkb) {
-          if (kb == 0) wait_vmem();
-          else wait_block();
-          barrier_only();
-          constexpr auto nxt = std::integral_constant<int, (s + P) % NS>{};
-          issue_a(kb + P, nxt);
-          issue_b(kb + P, nxt);
-          compute(sc);
-        }
+        wait_block();
+        barrier_only();
+        constexpr auto nxt = std::integral_constant<int, (s + P) % NS>{};
+        issue_a(kb + P, nxt);
+        issue_b(kb + P, nxt);
+        if (kb < nkb) compute(sc);
       });
     }
-    wait_vmem();      // the empty loads and copies issued past the last K block
+    // The loads of the last P steps (past the last K block: zeros) are never read; they still
+    // write their registers when they complete. Tying every weight register to this wait keeps
+    // the compiler from giving any of them to another value before then.
+    wait_vmem();
+    static_for<0, NS>([&](auto sc) {
+      static_for<0, FW>([&](auto ic) {
+        hold(wlo[decltype(sc)::value][decltype(ic)::value]);
+        hold(whi[decltype(sc)::value][decltype(ic)::value]);
+      });
+    });
 
     // Epilogue: lane holds C[m][n .. n+3] for m = m0 + 16 j + (lane & 15) and
     // n = n0 + 16 (wave FW + i) + 4 (lane >> 4).
@@ -397,44 +407,33 @@ static hipError_t launch_decode_cfg(const DecodeParams& p, bool f32, hipStream_t
   return hipGetLastError();
 }
 
+// Row part MT = 64 and 4 waves; fragments per wave FW = 1, 2 or 3 with the prefetch distance
+// that measured fastest for it (P = 3, 2, 2). On the rollout decode shapes (M = 256,
+// K = 4096, N = 4096 / 12288 / 24576, weights in the decode layout and streamed from HBM)
+// a row part of 128, four fragments per wave or deeper prefetch were slower or equal; with
+// more than three fragments per wave (or 128 rows and three) the kernel no longer fits in
+// 256 VGPRs. Each configuration fits two workgroups per CU (registers and LDS).
 struct DecodeCfg {
-  int mt, fw, p;
+  int fw;
   hipError_t (*launch)(const DecodeParams&, bool, hipStream_t);
 };
-// 4 waves per workgroup; (row part, fragments per wave, prefetch distance). For each
-// (row part, fragments per wave) the prefetch distance is the fastest one measured on the
-// rollout decode shapes (M = 256, K = 4096; N = 4096, 12288, 24576; weights in the decode
-// layout, streamed from HBM); deeper prefetch only added register pressure.
 static const DecodeCfg kDecodeCfgs[] = {
-    {64, 1, 4, launch_decode_cfg<64, 4, 1, 4>},   {64, 2, 2, launch_decode_cfg<64, 4, 2, 2>},
-    {64, 3, 3, launch_decode_cfg<64, 4, 3, 3>},   {64, 4, 2, launch_decode_cfg<64, 4, 4, 2>},
-    {128, 1, 2, launch_decode_cfg<128, 4, 1, 2>}, {128, 2, 2, launch_decode_cfg<128, 4, 2, 2>},
-    {128, 3, 2, launch_decode_cfg<128, 4, 3, 2>}, {256, 1, 2, launch_decode_cfg<256, 4, 1, 2>},
-    {256, 2, 2, launch_decode_cfg<256, 4, 2, 2>},
+    {3, launch_decode_cfg<64, 4, 3, 2>},
+    {2, launch_decode_cfg<64, 4, 2, 2>},
+    {1, launch_decode_cfg<64, 4, 1, 3>},
 };
 
-// Choice: the fewest rounds of 256 workgroups (one per CU), then the least data per CU and
-// K block (the MT rows of A copied to LDS + the 64 FW rows of B loaded), then more fragments
-// per wave (longer weight runs per copied activation row), then the smaller row part. On the
-// decode shapes this picks the fastest measured configuration for every N.
+// Choice: the most fragments per wave (the longest weight run per copied activation row)
+// whose grid still has a workgroup for every one of the 256 CUs; one fragment per wave when
+// none has. On the decode shapes this picks the fastest measured configuration for every N:
+// FW = 1 at N = 4096, FW = 3 at N = 12288 and 24576.
 hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t stream) {
-  const DecodeCfg* best = nullptr;
-  int64_t best_rounds = 0, best_rows = 0;
+  const int64_t ms = (p.M + 63) / 64;
   for (const DecodeCfg& c : kDecodeCfgs) {
-    const int64_t ms = (p.M + c.mt - 1) / c.mt;
     const int64_t runs = (p.N + 64 * c.fw - 1) / (64 * c.fw);
-    const int64_t rounds = (ms * runs + 255) / 256;
-    const int64_t rows = ((p.M < c.mt ? p.M : c.mt) + 64 * c.fw) * rounds;
-    bool take = best == nullptr || rounds < best_rounds || (rounds == best_rounds && rows < best_rows);
-    if (!take && rounds == best_rounds && rows == best_rows)
-      take = c.fw > best->fw || (c.fw == best->fw && c.mt < best->mt);
-    if (take) {
-      best = &c;
-      best_rounds = rounds;
-      best_rows = rows;
-    }
+    if (ms * runs >= 256 || c.fw == 1) return c.launch(p, f32, stream);
   }
-  return best->launch(p, f32, stream);
+  return hipErrorInvalidValue;   // not reached: the last configuration always applies
 }
 
 }  // namespace fp8rl

@@ -150,9 +150,9 @@ def test_decode_every_k_block(K):
         assert_gemm_close(host(y_rows), OG.gemm_fwd(rxq, rsx, rwq, rsw), f"K={K} block {j}")
 
 
-# One (M, N) per configuration of the decode kernel that the launch chooses (row part, weight
-# fragments per wave, prefetch distance), so every configuration runs: (64,1,4), (64,2,2),
-# (64,3,3), (64,4,2), (128,1,2), (128,2,2), (128,3,2), (256,1,2), (256,2,2).
+# Shapes that make the launch choose each configuration of the decode kernel (weight
+# fragments per wave 1, 2 and 3; row part 64), with one to three row parts (the last one
+# ragged) and grids of one to a few hundred workgroups.
 _CONFIG_SHAPES = [(1, 128), (1, 16512), (1, 32896), (1, 49280), (65, 8320), (65, 16512), (65, 32896),
                   (129, 11008), (129, 16512)]
 
