@@ -162,3 +162,25 @@ def test_producers_guarded():
     for a, b in zip(outs, F.fp8_rmsnorm_quant_1x128(x, gamma, 1e-6, rowwise=True, colwise=True)):
         _same(a, b, "rmsnorm quant")
     g.check("producers")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("M,K", [(2560, 4096), (4096, 3200), (8320, 1024)])
+def test_tile_quantizer_many_tiles(M, K, pow2):
+    """Row + column quantization with several 128x128 tiles per CU (tile counts that do not
+    divide evenly over the CUs, column-block counts with and without a factor 8, i.e. both
+    tile orders): guarded outputs, rows equal to the row-only quantizer's, columns equal to
+    the row-only quantizer's on the transposed matrix."""
+    g = Guarded(M * 3 + K)
+    x = bf16_dev(W.normal_bf16((M, K), 1.0, 93, M + K))
+    outs = (g((M, K), torch.uint8), g((M, K // 128), torch.float32), g((K, M), torch.uint8),
+            g((K, M // 128), torch.float32))
+    quant = F.fp8_quant_act_1x128_pow2 if pow2 else F.fp8_quant_act_1x128
+    quant(x, *outs, rowwise=True, colwise=True)
+    rq, rs = quant(x, rowwise=True, colwise=False)[:2]
+    tq, ts = quant(x.t().contiguous(), rowwise=True, colwise=False)[:2]
+    _same(outs[0], rq, "rows q")
+    _same(outs[1], rs, "rows s")
+    _same(outs[2], tq, "columns qt")
+    _same(outs[3], ts, "columns st")
+    g.check(f"streaming tile quantizer M={M} K={K} pow2={pow2}")
