@@ -23,6 +23,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two fp32 values -> their bf16 bits in one word (lo in bits 0..15), nearest-even: one
+// v_cvt_pk_bf16_f32 on gfx950. For finite values the same bits as f32_to_bf16_bits (checked on
+// the device over every bf16 high half with boundary, tie and subnormal low halves, and 4M
+// random patterns).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 // MXFP8 exponent for a group amax: the smallest integer e with amax <= 448 * 2^e, clamped
 // to [-127, 127]; 0 for amax == 0. For amax = 1.m * 2^F (m the 23-bit field), 448 * 2^(F-8)

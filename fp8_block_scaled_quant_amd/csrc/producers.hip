@@ -103,13 +103,13 @@ __device__ __forceinline__ uint4 swiglu8(uint4 gw, uint4 uw, const uint16_t* lut
         sb[j] = silu_bf16_bits_computed((j & 1) ? bf16_hi(w) : bf16_lo(w));
       }
   }
-  uint32_t h[8];
+  uint32_t h[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w = us[j >> 1];
-    h[j] = f32_to_bf16_bits(__uint_as_float(sb[j] << 16) * ((j & 1) ? bf16_hi(w) : bf16_lo(w)));
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = us[j];
+    h[j] = bf16x2_bits(__uint_as_float(sb[2 * j] << 16) * bf16_lo(w), __uint_as_float(sb[2 * j + 1] << 16) * bf16_hi(w));
   }
-  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  return make_uint4(h[0], h[1], h[2], h[3]);
 }
 
 // SwiGLU of GU[M][2F], presented as h[M][F].
@@ -143,9 +143,8 @@ struct SwigluSrc {
 
 // RMSNorm output for two x values and two gamma values (bf16 pairs in words).
 __device__ __forceinline__ uint32_t rms2(uint32_t xw, uint32_t gw, float r) {
-  const float t0 = __uint_as_float(f32_to_bf16_bits(bf16_lo(xw) * r) << 16);
-  const float t1 = __uint_as_float(f32_to_bf16_bits(bf16_hi(xw) * r) << 16);
-  return f32_to_bf16_bits(bf16_lo(gw) * t0) | (f32_to_bf16_bits(bf16_hi(gw) * t1) << 16);
+  const uint32_t t = bf16x2_bits(bf16_lo(xw) * r, bf16_hi(xw) * r);
+  return bf16x2_bits(bf16_lo(gw) * bf16_lo(t), bf16_hi(gw) * bf16_hi(t));
 }
 __device__ __forceinline__ uint4 rms8(uint4 x, uint4 g, float r) {
   return make_uint4(rms2(x.x, g.x, r), rms2(x.y, g.y, r), rms2(x.z, g.z, r), rms2(x.w, g.w, r));
