@@ -66,17 +66,17 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "5013e189287f549a", "gb": 1.6391},  # read 1.2367 + write 0.4024
-    "gemm_gu_pow2": {"sha": "5013e189287f549a", "gb": 1.6392},  # read 1.2368 + write 0.4024
-    "dgrad": {"sha": "5013e189287f549a", "gb": 1.3247},  # read 1.2576 + write 0.0671
-    "dgrad_pow2": {"sha": "5013e189287f549a", "gb": 1.3195},  # read 1.2524 + write 0.0671
-    "mx_fwd": {"sha": "5013e189287f549a", "gb": 1.6489},  # read 1.2465 + write 0.4024
-    "decode_n24576": {"sha": "02d496c830f423a7", "gb": 0.1221},  # read 0.1095 + write 0.0126 (the GEMM launch of the call)
-    "grouped_gu": {"sha": "5013e189287f549a", "gb": 0.3148},  # read 0.2478 + write 0.0671
-    "grouped_gu_block": {"sha": "5013e189287f549a", "gb": 0.3081},  # read 0.2410 + write 0.0671
-    "install_gu": {"sha": "fefe92b43ebbcbf9", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
-    "swiglu_fp8": {"sha": "4b90bb5d45a62f61", "gb": 0.6222},  # read 0.4035 + write 0.2188
-    "requant_gu": {"sha": "d662e097566beca5", "gb": 0.6041},  # read 0.4026 + write 0.2014
+    "gemm_gu": {"sha": "0916d3ebc8347e05", "gb": 1.6391},  # read 1.2368 + write 0.4023
+    "gemm_gu_pow2": {"sha": "0916d3ebc8347e05", "gb": 1.6391},  # read 1.2368 + write 0.4023
+    "dgrad": {"sha": "0916d3ebc8347e05", "gb": 1.3204},  # read 1.2533 + write 0.0671
+    "dgrad_pow2": {"sha": "0916d3ebc8347e05", "gb": 1.3218},  # read 1.2547 + write 0.0671
+    "mx_fwd": {"sha": "0916d3ebc8347e05", "gb": 1.6487},  # read 1.2464 + write 0.4023
+    "decode_n24576": {"sha": "6d19443449c393bb", "gb": 0.1223},  # read 0.1097 + write 0.0126 (the GEMM launch of the call)
+    "grouped_gu": {"sha": "0916d3ebc8347e05", "gb": 0.3149},  # read 0.2478 + write 0.0671
+    "grouped_gu_block": {"sha": "0916d3ebc8347e05", "gb": 0.3073},  # read 0.2402 + write 0.0671
+    "install_gu": {"sha": "495522813f4a7cae", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
+    "swiglu_fp8": {"sha": "f9a893244725ac88", "gb": 0.6222},  # read 0.4034 + write 0.2188
+    "requant_gu": {"sha": "4c04c29cdeacddd4", "gb": 0.6040},  # read 0.4026 + write 0.2014
 }
 
 
