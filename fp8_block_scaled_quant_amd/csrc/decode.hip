@@ -253,18 +253,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       constexpr int i = decltype(ic)::value;
       sb[i] = ds_read4f<i * 4>(sb_ad);
     });
-    v4i xlo = ds_read16<0>(a_lo), xhi = ds_read16<0>(a_hi);
-    float sx = ds_read4f<0>(sa_ad);
-    lds_wait<0>();
-    v8i bf[FW];
-    static_for<0, FW>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      hold(sb[i]);
-      bf[i] = join(wlo[set][i], whi[set][i]);
+    // Every X fragment of the K block (and its row scale) is requested at once; fragment j
+    // is then awaited alone (LDS reads complete in issue order), so the reads of the later
+    // fragments overlap the MFMAs of the earlier ones.
+    v4i xlo[XF], xhi[XF];
+    float sx[XF];
+    static_for<0, XF>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      xlo[j] = ds_read16<j * 2048>(a_lo);
+      xhi[j] = ds_read16<j * 2048>(a_hi);
+      sx[j] = ds_read4f<j * 64>(sa_ad);
     });
-    hold(xlo);
-    hold(xhi);
-    hold(sx);
+    v8i bf[FW];
     v4f pipe[kDecodeLag + 1];
     float prod[kDecodeLag + 1];
     auto fold = [&](int u) __attribute__((always_inline)) {
@@ -275,31 +275,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     };
     static_for<0, XF>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      v4i nlo, nhi;
-      float nsx = 0.f;
-      if constexpr (j + 1 < XF) {
-        nlo = ds_read16<(j + 1) * 2048>(a_lo);
-        nhi = ds_read16<(j + 1) * 2048>(a_hi);
-        nsx = ds_read4f<(j + 1) * 64>(sa_ad);
+      lds_wait<3 * (XF - 1 - j)>();     // 3 reads per later fragment may still be in flight
+      hold(xlo[j]);
+      hold(xhi[j]);
+      hold(sx[j]);
+      if constexpr (j == 0) {
+        static_for<0, FW>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          hold(sb[i]);
+          bf[i] = join(wlo[set][i], whi[set][i]);
+        });
       }
-      const v8i xf = join(xlo, xhi);
+      const v8i xf = join(xlo[j], xhi[j]);
 #pragma unroll
       for (int i = 0; i < FW; ++i) {
         const int t = j * FW + i;
         pipe[t % (kDecodeLag + 1)] = mfma_fp8(bf[i], xf, v4f{0.f, 0.f, 0.f, 0.f}, 127, 127);
-        prod[t % (kDecodeLag + 1)] = sx * sb[i];
+        prod[t % (kDecodeLag + 1)] = sx[j] * sb[i];
         if (t >= kDecodeLag) fold(t - kDecodeLag);
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (j + 1 < XF) {
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wait<0>();
-        hold(nlo);
-        hold(nhi);
-        hold(nsx);
-        xlo = nlo;
-        xhi = nhi;
-        sx = nsx;
       }
     });
 #pragma unroll
