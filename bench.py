@@ -71,7 +71,7 @@ MEASURED_TRAFFIC = {
     "dgrad": {"sha": "0916d3ebc8347e05", "gb": 1.3204},  # read 1.2533 + write 0.0671
     "dgrad_pow2": {"sha": "0916d3ebc8347e05", "gb": 1.3218},  # read 1.2547 + write 0.0671
     "mx_fwd": {"sha": "0916d3ebc8347e05", "gb": 1.6487},  # read 1.2464 + write 0.4023
-    "decode_n24576": {"sha": "6d19443449c393bb", "gb": 0.1223},  # read 0.1097 + write 0.0126 (the GEMM launch of the call)
+    "decode_n24576": {"sha": "b2d0f8f782049ddb", "gb": 0.1223},  # read 0.1097 + write 0.0126 (the GEMM launch of the call)
     "grouped_gu": {"sha": "0916d3ebc8347e05", "gb": 0.3149},  # read 0.2478 + write 0.0671
     "grouped_gu_block": {"sha": "0916d3ebc8347e05", "gb": 0.3073},  # read 0.2402 + write 0.0671
     "install_gu": {"sha": "495522813f4a7cae", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
