@@ -117,16 +117,12 @@ __global__ __launch_bounds__(256) void k_quant_kbmajor(const uint16_t* __restric
     a = src[0];
     b = src[1];
   }
-  float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
-                     fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const float amax = group_amax<8>(pk_max_u16(mag8(a), mag8(b)));
   const BlockScale bs = block_scale(amax);
   if (valid) {
     const int64_t g = (int64_t)kb * M + m;
-    const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
-    const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
+    const uint2 lo = quant8<false>(a.x, a.y, a.z, a.w, bs);
+    const uint2 hi = quant8<false>(b.x, b.y, b.z, b.w, bs);
     *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     if (part == 0) s[g] = bs.s;
   }

@@ -48,29 +48,44 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 }
 
 // Scale of a 1x128 / 128x1 / 128x128 group: s = fl32(amax / 448) (IEEE division; hipcc's
-// default fp32 division is correctly rounded), 1.0 for an all-zero group. `r` is the
-// fp64 reciprocal used to form the scaled values (see scaled()).
+// default fp32 division is correctly rounded), 1.0 for an all-zero group. The scaled values
+// x / s are formed without a division per value (quant8 below):
+//  - fp32 scales: h = 1/s rounded toward zero, l = (1 - h s) h >= 0 (the residual 1 - h s is
+//    exact in one fma), and q = fl32(x h + fl32(x l)): one multiply and one fma per value.
+//    q can differ from fl32(x / s) in its last bit, but never so that its E4M3 code (or the
+//    sign of a zero) changes: an exhaustive CPU check over every pair of bf16 values
+//    (x, amax) with |x| <= amax and a normal s finds no pair whose code differs.
+//  - a subnormal s (0 < amax < 448 * 2^-126) has no fp32 reciprocal; a wave with such a
+//    group forms fl32(x * fl64(1/s)), which equals fl32(x / s) for every bf16 pair (the same
+//    CPU check covers it).
+//  - power-of-two scales: h = 2^-e, l = 0 and q = x h, exact whenever |q| is above the fp32
+//    subnormal range; below it the E4M3 code is a zero of x's sign either way.
 struct BlockScale {
   float s;
-  double r;
+  float h, l;
 };
 
 __device__ __forceinline__ BlockScale block_scale(float amax) {
   BlockScale b;
   b.s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
-  b.r = 1.0 / (double)b.s;
+  float h = 1.0f / b.s;
+  const float e0 = __builtin_fmaf(-h, b.s, 1.0f);
+  h = e0 < 0.0f ? __uint_as_float(__float_as_uint(h) - 1u) : h;   // the float below 1/s
+  b.h = h;
+  b.l = __builtin_fmaf(-h, b.s, 1.0f) * h;
   return b;
 }
 
 // Power-of-two block scale: s = 2^e with the MX exponent rule (smallest e with
 // amax <= 448 * 2^e, clamped to [-127, 127]; 2^-127 is an exact fp32 subnormal). The
-// scaled value x * 2^-e is then exact (scaled() computes it without rounding) and at most
-// 448 in magnitude.
+// scaled value x * 2^-e is then exact (above the fp32 subnormal range) and at most 448 in
+// magnitude.
 __device__ __forceinline__ BlockScale block_scale_pow2(float amax) {
   const int e = mx_exponent(amax);
   BlockScale b;
   b.s = ldexpf(1.0f, e);
-  b.r = ldexp(1.0, -e);
+  b.h = ldexpf(1.0f, -e);
+  b.l = 0.0f;
   return b;
 }
 
@@ -80,17 +95,10 @@ __device__ __forceinline__ BlockScale group_scale(float amax) {
   else return block_scale(amax);
 }
 
-// The fp32 quotient fl32(x / s) for a bf16 value x with |x| <= amax, computed as
-// fl32(x * fl64(1/s)). x has 8 significant bits and s 24, so x/s never lies within a
-// relative 2^-49 of an fp32 rounding midpoint, while the fp64 product is within 2^-52 of
-// x/s: both round to the same fp32 value. (An exhaustive CPU test over every bf16 pair
-// (x, amax) checks this identity, and that |x/s| stays below 449.)
-__device__ __forceinline__ float scaled(float x, double r) { return (float)((double)x * r); }
-
 // Four fp32 values -> four E4M3 bytes, round to nearest even (v_cvt_pk_fp8_f32 under the
 // default round-to-nearest-even mode). The converter does not saturate: it returns the
-// max-magnitude code only for 448 < |v| < 464, which covers every quotient above, and NaN
-// beyond; callers never pass |v| >= 464.
+// max-magnitude code only for 448 < |v| < 464, which covers every quotient above (below 449),
+// and NaN beyond; callers never pass |v| >= 464.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
@@ -98,17 +106,70 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 }
 
 // Quantize 8 bf16 values held in 4 words (2 per word) with one group scale -> 8 E4M3 bytes.
-__device__ __forceinline__ uint2 quant8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, double r) {
-  uint2 o;
-  o.x = pack4_e4m3(scaled(bf16_lo(w0), r), scaled(bf16_hi(w0), r), scaled(bf16_lo(w1), r), scaled(bf16_hi(w1), r));
-  o.y = pack4_e4m3(scaled(bf16_lo(w2), r), scaled(bf16_hi(w2), r), scaled(bf16_lo(w3), r), scaled(bf16_hi(w3), r));
-  return o;
+// kPow2 names the scale kind (compile time); the fp64 form is chosen per wave, so the branch
+// is uniform.
+template <bool kPow2>
+__device__ __forceinline__ uint2 quant8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, const BlockScale& b) {
+  const float x[8] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1),
+                      bf16_lo(w2), bf16_hi(w2), bf16_lo(w3), bf16_hi(w3)};
+  float q[8];
+  if constexpr (kPow2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = x[i] * b.h;
+  } else if (__builtin_amdgcn_ballot_w64(!(b.s >= 0x1p-126f)) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_fmaf(x[i], b.h, x[i] * b.l);
+  } else {
+    const double r = 1.0 / (double)b.s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (float)((double)x[i] * r);
+  }
+  return make_uint2(pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7]));
 }
 
-// max(|lo|, |hi|) of the two bf16 values in a word.
-__device__ __forceinline__ float absmax2(uint32_t w) {
-  return fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w)));
+// Group amax in the integer domain. For finite bf16 values the order of the magnitude bits
+// (the value with its sign bit cleared) is the numeric order of |x|, so the max needs no
+// float compare (and no NaN canonicalization of its operands). mag8() gives, per 16-bit
+// half, the largest magnitude among the 8 values in four words (one v_and and one
+// v_pk_max_u16 per word); mag_fold() takes the larger half; mag_to_f32() turns magnitude
+// bits back into the fp32 value (exact).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
 }
+__device__ __forceinline__ uint32_t mag8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  constexpr uint32_t k = 0x7fff7fffu;
+  return pk_max_u16(pk_max_u16(w0 & k, w1 & k), pk_max_u16(w2 & k, w3 & k));
+}
+__device__ __forceinline__ uint32_t mag8(const uint4& v) { return mag8(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ uint32_t mag_fold(uint32_t m) { return max(m & 0xffffu, m >> 16); }
+__device__ __forceinline__ float mag_to_f32(uint32_t m) { return __uint_as_float(m << 16); }
+
+// Max over aligned groups of kLanes consecutive lanes (2, 4, 8 or 16), every lane of a group
+// receiving it, by DPP lane moves: swaps within a quad (lanes i ^ 1, then i ^ 2), then the
+// half-row mirror (lane i with 7 - i within 8) and the row mirror (i with 15 - i within 16).
+// Every lane of the wave must be active.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, true));
+}
+template <int kLanes>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  static_assert(kLanes == 2 || kLanes == 4 || kLanes == 8 || kLanes == 16, "group of 2-16 lanes");
+  v = dpp_max<0xB1>(v);                                // quad_perm [1, 0, 3, 2]
+  if constexpr (kLanes >= 4) v = dpp_max<0x4E>(v);     // quad_perm [2, 3, 0, 1]
+  if constexpr (kLanes >= 8) v = dpp_max<0x141>(v);    // row_half_mirror
+  if constexpr (kLanes >= 16) v = dpp_max<0x140>(v);   // row_mirror
+  return v;
+}
+
+// amax of a group whose lanes hold 8 values each in (a, b) words: magnitude bits, group max.
+template <int kLanes>
+__device__ __forceinline__ float group_amax(uint32_t m) {
+  return mag_to_f32(group_max<kLanes>(mag_fold(m)));
+}
+
 
 
 // Raw buffer descriptor over [base, base + bytes) as four SGPR words: loads at byte

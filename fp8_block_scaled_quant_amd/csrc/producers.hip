@@ -252,15 +252,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t* __restrict
       }
     } else {
       // 8 consecutive lanes hold one 1x128 group; every lane takes part in the shuffles.
-      float amax = fmaxf(fmaxf(fmaxf(absmax2(ya.x), absmax2(ya.y)), fmaxf(absmax2(ya.z), absmax2(ya.w))),
-                         fmaxf(fmaxf(absmax2(yb.x), absmax2(yb.y)), fmaxf(absmax2(yb.z), absmax2(yb.w))));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      const float amax = group_amax<8>(pk_max_u16(mag8(ya), mag8(yb)));
       const BlockScale bs = group_scale<kPow2>(amax);
       if (valid) {
-        const uint2 lo = quant8(ya.x, ya.y, ya.z, ya.w, bs.r);
-        const uint2 hi = quant8(yb.x, yb.y, yb.z, yb.w, bs.r);
+        const uint2 lo = quant8<kPow2>(ya.x, ya.y, ya.z, ya.w, bs);
+        const uint2 hi = quant8<kPow2>(yb.x, yb.y, yb.z, yb.w, bs);
         *reinterpret_cast<uint4*>(q + row * K + c * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
         if ((c & 7) == 0) s[row * (K / 128) + c / 8] = bs.s;
       }

@@ -28,9 +28,7 @@ __global__ __launch_bounds__(256) void k_quant_mx_1x32(const uint16_t* __restric
     a = src[0];
     b = src[1];
   }
-  float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
-                     fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const float amax = group_amax<2>(pk_max_u16(mag8(a), mag8(b)));
   const int e = mx_exponent(amax);
   if (valid) {
     // x * 2^-e is exact (v_ldexp_f32) and |x * 2^-e| <= 448 by the choice of e.

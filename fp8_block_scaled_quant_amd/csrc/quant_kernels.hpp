@@ -69,15 +69,11 @@ __global__ __launch_bounds__(256) void k_quant_rows_1x128(Src src, uint8_t* __re
       a = src.make(ra, lds);
       b = src.make(rb, lds);
     }
-    float amax = fmaxf(fmaxf(fmaxf(absmax2(a.x), absmax2(a.y)), fmaxf(absmax2(a.z), absmax2(a.w))),
-                       fmaxf(fmaxf(absmax2(b.x), absmax2(b.y)), fmaxf(absmax2(b.z), absmax2(b.w))));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const float amax = group_amax<8>(pk_max_u16(mag8(a), mag8(b)));
     const BlockScale bs = group_scale<kPow2>(amax);
     if (valid) {
-      const uint2 lo = quant8(a.x, a.y, a.z, a.w, bs.r);
-      const uint2 hi = quant8(b.x, b.y, b.z, b.w, bs.r);
+      const uint2 lo = quant8<kPow2>(a.x, a.y, a.z, a.w, bs);
+      const uint2 hi = quant8<kPow2>(b.x, b.y, b.z, b.w, bs);
       *reinterpret_cast<uint4*>(q + g * 128 + part * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
       if (part == 0) s[g] = bs.s;
     }
@@ -150,42 +146,32 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = src.make(raw[i], src_lds);
 
-  double rblk = 0.0;
+  BlockScale bblk{1.0f, 1.0f, 0.0f};
   if (kBlock) {
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a = fmaxf(a, fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w))));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    uint32_t m = pk_max_u16(pk_max_u16(mag8(v[0]), mag8(v[1])), pk_max_u16(mag8(v[2]), mag8(v[3])));
+    m = group_max<16>(mag_fold(m));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+    float a = mag_to_f32(max(m, (uint32_t)__shfl_xor((int)m, 32)));
     if (lane == 0) red[wave] = a;
     __syncthreads();
     a = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
-    const BlockScale bs = group_scale<kPow2>(a);
-    if (tid == 0) store_scale<128>(s, rb * ncb + cb, bs);
-    rblk = bs.r;
+    bblk = group_scale<kPow2>(a);
+    if (tid == 0) store_scale<128>(s, rb * ncb + cb, bblk);
     if (want_rows) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
-            quant8(v[i].x, v[i].y, v[i].z, v[i].w, rblk);
+            quant8<kPow2>(v[i].x, v[i].y, v[i].z, v[i].w, bblk);
     }
   } else if (want_rows) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float a = fmaxf(fmaxf(absmax2(v[i].x), absmax2(v[i].y)), fmaxf(absmax2(v[i].z), absmax2(v[i].w)));
-      a = fmaxf(a, __shfl_xor(a, 1));
-      a = fmaxf(a, __shfl_xor(a, 2));
-      if constexpr (kG == 128) {
-        a = fmaxf(a, __shfl_xor(a, 4));
-        a = fmaxf(a, __shfl_xor(a, 8));
-      }
-      const BlockScale bs = group_scale<kPow2>(a);
+      const BlockScale bs = group_scale<kPow2>(group_amax<kG / 8>(mag8(v[i])));
       constexpr int kLanes = kG / 8;                               // lanes of one row group
       if ((c & (kLanes - 1)) == 0)
         store_scale<kG>(s, (rb * 128 + 4 * rg + i) * (C / kG) + cb * (128 / kG) + c / kLanes, bs);
       *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
-          quant8(v[i].x, v[i].y, v[i].z, v[i].w, bs.r);
+          quant8<kPow2>(v[i].x, v[i].y, v[i].z, v[i].w, bs);
     }
   }
   if (!want_cols) return;
@@ -218,25 +204,16 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
     const uint4 B = *reinterpret_cast<const uint4*>(tile + col * 64 + (((a ^ 1) ^ sw) * 4));
     const bool even = (a & 1) == 0;
     const uint4 lo = even ? A : B, hi = even ? B : A;               // rows 16k..+7, 16k+8..+15
-    double r;
-    if (kBlock) {
-      r = rblk;
-    } else {
-      float m = fmaxf(fmaxf(fmaxf(absmax2(lo.x), absmax2(lo.y)), fmaxf(absmax2(lo.z), absmax2(lo.w))),
-                      fmaxf(fmaxf(absmax2(hi.x), absmax2(hi.y)), fmaxf(absmax2(hi.z), absmax2(hi.w))));
-      m = fmaxf(m, __shfl_xor(m, 1));
-      if constexpr (kG == 128) {
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-      }
-      const BlockScale bs = group_scale<kPow2>(m);
-      r = bs.r;
+    BlockScale r = bblk;
+    if (!kBlock) {
+      const BlockScale bs = group_scale<kPow2>(group_amax<kG / 16>(pk_max_u16(mag8(lo), mag8(hi))));
+      r = bs;
       constexpr int kLanes = kG / 16;                              // lanes of one column group
       if ((k & (kLanes - 1)) == 0)
         store_scale<kG>(st, (cb * 128 + col) * (R / kG) + rb * (128 / kG) + k / kLanes, bs);
     }
-    const uint2 o0 = quant8(lo.x, lo.y, lo.z, lo.w, r);
-    const uint2 o1 = quant8(hi.x, hi.y, hi.z, hi.w, r);
+    const uint2 o0 = quant8<kPow2>(lo.x, lo.y, lo.z, lo.w, r);
+    const uint2 o1 = quant8<kPow2>(hi.x, hi.y, hi.z, hi.w, r);
     *reinterpret_cast<uint4*>(qt + (cb * 128 + col) * R + rb * 128 + 16 * k) = make_uint4(o0.x, o0.y, o1.x, o1.y);
   }
 }

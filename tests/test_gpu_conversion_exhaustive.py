@@ -2,20 +2,25 @@
 byte against the oracle ([AIS] quantizer equation and worked rounding example; readings
 c2-c5, c7, c21).
 
-Why one binade of amax suffices: a group's codes depend on x / s only. Multiplying every
-element of a group by 2^j (j an integer, all values staying within bf16) multiplies amax by
-2^j, and then
+Why a few binades of amax suffice: a group's codes depend on x / s and on how the kernel
+forms it. Multiplying every element of a group by 2^j (j an integer, all values staying
+within bf16) multiplies amax by 2^j, and then
 - fp32 scales s = fl32(amax / 448) become s * 2^j exactly, as long as s stays a normal fp32
   (a power-of-two factor commutes with a correctly rounded division away from underflow);
+  the kernels' reciprocal pair (h = 1/s rounded toward zero, l = fl32((1 - h s) h)) becomes
+  (h, l) * 2^-j as long as l stays normal, i.e. for amax below 1.75 * 2^110;
 - power-of-two and MX scales 2^e become 2^(e + j), as long as e stays inside its clamp;
-so every quotient x / s, and every code, is unchanged. A bf16 x that would be subnormal in
+so every quotient, and every code, is unchanged. A bf16 x that would be subnormal in
 another binade is, in this one, a normal bf16 with trailing zero bits, which the sweep
 includes. So the sweep takes
 - every amax of one binade, the 128 bf16 mantissas in [1, 2), each with every bf16 x of
   magnitude at most amax, both signs (the amax itself also with its sign flipped);
 - separately, every amax whose scale leaves that regime: fp32 scales that are subnormal
   (amax < 448 * 2^-126) and power-of-two / MX exponents at the -127 clamp (amax <= 448 *
-  2^-127 up to the first exponent above the clamp), each with every x of smaller magnitude.
+  2^-127 up to the first exponent above the clamp), each with every x of smaller magnitude;
+- the binades where l is subnormal are not equivalent to one another; the sweep takes the
+  first, [2^110, 2^111), and the last, [2^127, max bf16], each amax with every x of smaller
+  magnitude (an exhaustive CPU check of the same arithmetic covers all of them).
 Each group holds +-amax first and up to 127 (MX: 31) of the x values; the oracle quantizes the
 same tensor. The 1x128 quantizer runs in its row kernel and, on the transposed tensor, in the
 128x1 column kernel; the power-of-two and MXFP8 quantizers likewise."""
@@ -77,10 +82,22 @@ SUBNORMAL_SCALE = np.arange(0x0001, 0x04E0, dtype=np.uint32)
 CLAMPED_EXPONENT = np.arange(0x0001, 0x04E0, dtype=np.uint32)
 
 
-@pytest.mark.parametrize("region", ["one_binade", "small_amax"])
+# l = fl32((1 - h s) h) subnormal: amax >= 1.75 * 2^110; the first and the last such binade
+LARGE_AMAX = np.concatenate([np.arange(0x7680, 0x7700, dtype=np.uint32), np.arange(0x7F00, 0x7F80, dtype=np.uint32)])
+
+
+def _region(region, pow2):
+    if region == "one_binade":
+        return ONE_BINADE
+    if region == "large_amax":
+        return LARGE_AMAX
+    return CLAMPED_EXPONENT if pow2 else SUBNORMAL_SCALE
+
+
+@pytest.mark.parametrize("region", ["one_binade", "small_amax", "large_amax"])
 @pytest.mark.parametrize("pow2", [False, True])
 def test_1x128_conversion_exhaustive(region, pow2):
-    amax = ONE_BINADE if region == "one_binade" else (CLAMPED_EXPONENT if pow2 else SUBNORMAL_SCALE)
+    amax = _region(region, pow2)
     x = _pad_rows(_groups(amax, 128), 128)                            # [G][128], G % 128 == 0
     quant_gpu = F.fp8_quant_act_1x128_pow2 if pow2 else F.fp8_quant_act_1x128
     rows_ref = OQ.quant_act_1x128_pow2 if pow2 else OQ.quant_act_1x128
@@ -95,9 +112,9 @@ def test_1x128_conversion_exhaustive(region, pow2):
     _eq(st, rs, f"cols st ({region}, pow2={pow2})")
 
 
-@pytest.mark.parametrize("region", ["one_binade", "small_amax"])
+@pytest.mark.parametrize("region", ["one_binade", "small_amax", "large_amax"])
 def test_mx_conversion_exhaustive(region):
-    amax = ONE_BINADE if region == "one_binade" else CLAMPED_EXPONENT
+    amax = _region(region, True)
     x = _groups(amax, 32)                                             # [G][32]
     x = _pad_rows(x, 4).reshape(-1, 128)                              # 4 groups per row of 128
     q, e = F.mxfp8_quant_1x32(_to_dev(x))
