@@ -170,6 +170,33 @@ __device__ __forceinline__ float group_amax(uint32_t m) {
   return mag_to_f32(group_max<kLanes>(mag_fold(m)));
 }
 
+// fp32 group scales from a 1 KB per-workgroup table instead of two divisions per group. For
+// the 128 bf16 mantissas of an amax in [1, 2) the table holds s_m = fl32(a / 448) and h_m =
+// 1/s_m rounded toward zero. For an amax with biased exponent E and a normal s,
+// fl32(amax / 448) = s_m 2^(E-127) and its rounded-down reciprocal is h_m 2^(127-E), exactly
+// (a power-of-two factor commutes with both roundings while the results stay normal), so
+// these scales equal block_scale()'s bit for bit. A subnormal s (amax below 448 * 2^-126,
+// bf16 magnitude bits < 0x04E0) is divided for as in block_scale(); quant8() then takes the
+// fp64 form for the wave.
+__device__ __forceinline__ void fill_scale_table(float2* tab, int tid) {
+  if (tid < 128) {
+    const BlockScale b = block_scale(__uint_as_float(0x3F800000u | ((uint32_t)tid << 16)));
+    tab[tid] = make_float2(b.s, b.h);
+  }
+}
+__device__ __forceinline__ BlockScale table_scale(uint32_t m16, const float2* tab) {
+  const float2 t = tab[m16 & 127u];
+  const int E = (int)(m16 >> 7);
+  BlockScale b;
+  b.s = ldexpf(t.x, E - 127);
+  b.h = ldexpf(t.y, 127 - E);
+  b.l = __builtin_fmaf(-b.h, b.s, 1.0f) * b.h;
+  if (m16 == 0) b = BlockScale{1.0f, 1.0f, 0.0f};
+  const bool tiny = m16 != 0 && m16 < 0x04E0u;
+  if (__builtin_amdgcn_ballot_w64(tiny) != 0 && tiny) b.s = mag_to_f32(m16) / kE4M3Max;
+  return b;
+}
+
 
 
 // Raw buffer descriptor over [base, base + bytes) as four SGPR words: loads at byte

@@ -116,30 +116,38 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
   __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];   // [column][row pair]
   __shared__ float red[8];
   __shared__ __attribute__((aligned(16))) uint8_t src_lds[SrcLds<Src>::kBytes];
+  // fp32 scales of the row and column groups (several per thread) come from a table
+  constexpr bool kTab = !kBlock && !kPow2;
+  __shared__ float2 stab[kTab ? 128 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid & 15, rg = tid >> 4;                               // rg: 0..31
-  const int64_t ncb = C / 128;
+  // The grid has (R/128) (C/128) < 2^32 workgroups, so tile indices fit in 32 bits.
+  const uint32_t ncb = (uint32_t)(C / 128), bid = blockIdx.x;
   // Tile order: the hardware deals consecutive workgroups to the 8 XCDs in turn. When the
   // column blocks split evenly, XCD x takes the column blocks [x w, (x+1) w), w = ncb / 8,
   // row block by row block. The tiles in flight still cover a few whole block rows (the
   // read stream keeps its locality), and each XCD's L2 sees fewer of the lines that
   // several tiles' 4-byte scale stores share.
-  int64_t cb, rb;
+  uint32_t cb, rb;
   if (ncb % 8 == 0) {
-    const int64_t w = ncb / 8, i = blockIdx.x >> 3;
-    cb = (int64_t)(blockIdx.x & 7) * w + i % w;
+    const uint32_t w = ncb / 8, i = bid >> 3;
+    cb = (bid & 7) * w + i % w;
     rb = i / w;
   } else {
-    cb = blockIdx.x % ncb;
-    rb = blockIdx.x / ncb;
+    cb = bid % ncb;
+    rb = bid / ncb;
   }
   const bool want_rows = q != nullptr, want_cols = qt != nullptr;
+  // Element offsets: this thread's first row and column, and (column pass) its first column.
+  const int64_t row0 = (int64_t)rb * 128 + 4 * rg, col0 = (int64_t)cb * 128 + c * 8;
+  const int64_t qoff = row0 * C + col0;
 
   typename Src::Raw raw[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = src.fetch8(rb * 128 + 4 * rg + i, cb * 128 + c * 8);
-  if constexpr (Src::kLdsBytes > 0) {
-    src.prepare(src_lds, tid, 512);
+  for (int i = 0; i < 4; ++i) raw[i] = src.fetch8(row0 + i, col0);
+  if constexpr (Src::kLdsBytes > 0 || kTab) {
+    if constexpr (Src::kLdsBytes > 0) src.prepare(src_lds, tid, 512);
+    if constexpr (kTab) fill_scale_table(stab, tid);
     __syncthreads();
   }
   uint4 v[4];
@@ -160,18 +168,18 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
     if (want_rows) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
-            quant8<kPow2>(v[i].x, v[i].y, v[i].z, v[i].w, bblk);
+        *reinterpret_cast<uint2*>(q + qoff + i * C) = quant8<kPow2>(v[i].x, v[i].y, v[i].z, v[i].w, bblk);
     }
   } else if (want_rows) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const BlockScale bs = group_scale<kPow2>(group_amax<kG / 8>(mag8(v[i])));
+      const uint32_t m16 = group_max<kG / 8>(mag_fold(mag8(v[i])));
+      BlockScale bs;
+      if constexpr (kTab) bs = table_scale(m16, stab);
+      else bs = group_scale<kPow2>(mag_to_f32(m16));
       constexpr int kLanes = kG / 8;                               // lanes of one row group
-      if ((c & (kLanes - 1)) == 0)
-        store_scale<kG>(s, (rb * 128 + 4 * rg + i) * (C / kG) + cb * (128 / kG) + c / kLanes, bs);
-      *reinterpret_cast<uint2*>(q + (rb * 128 + 4 * rg + i) * C + cb * 128 + c * 8) =
-          quant8<kPow2>(v[i].x, v[i].y, v[i].z, v[i].w, bs);
+      if ((c & (kLanes - 1)) == 0) store_scale<kG>(s, (int64_t)((uint64_t)(qoff + i * C) / kG), bs);
+      *reinterpret_cast<uint2*>(q + qoff + i * C) = quant8<kPow2>(v[i].x, v[i].y, v[i].z, v[i].w, bs);
     }
   }
   if (!want_cols) return;
@@ -195,6 +203,8 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
   // The two chunks are read in an order (odd first for half the lanes) that keeps every
   // group of 8 or 16 lanes on distinct banks.
   const int k = lane & 7;
+  // qt [C][R]: this lane's first column is cb 128 + 16 wave + lane / 8, rows rb 128 + 16 k ...
+  const int64_t qtoff = ((int64_t)cb * 128 + 16 * wave + (lane >> 3)) * R + (int64_t)rb * 128 + 16 * k;
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
     const int col = 16 * wave + 8 * rd + (lane >> 3);
@@ -206,15 +216,17 @@ __global__ __launch_bounds__(512) void k_quant_tile(Src src, int64_t R, int64_t 
     const uint4 lo = even ? A : B, hi = even ? B : A;               // rows 16k..+7, 16k+8..+15
     BlockScale r = bblk;
     if (!kBlock) {
-      const BlockScale bs = group_scale<kPow2>(group_amax<kG / 16>(pk_max_u16(mag8(lo), mag8(hi))));
+      const uint32_t m16 = group_max<kG / 16>(mag_fold(pk_max_u16(mag8(lo), mag8(hi))));
+      BlockScale bs;
+      if constexpr (kTab) bs = table_scale(m16, stab);
+      else bs = group_scale<kPow2>(mag_to_f32(m16));
       r = bs;
       constexpr int kLanes = kG / 16;                              // lanes of one column group
-      if ((k & (kLanes - 1)) == 0)
-        store_scale<kG>(st, (cb * 128 + col) * (R / kG) + rb * (128 / kG) + k / kLanes, bs);
+      if ((k & (kLanes - 1)) == 0) store_scale<kG>(st, (int64_t)((uint64_t)(qtoff + 8 * rd * R) / kG), bs);
     }
     const uint2 o0 = quant8<kPow2>(lo.x, lo.y, lo.z, lo.w, r);
     const uint2 o1 = quant8<kPow2>(hi.x, hi.y, hi.z, hi.w, r);
-    *reinterpret_cast<uint4*>(qt + (cb * 128 + col) * R + rb * 128 + 16 * k) = make_uint4(o0.x, o0.y, o1.x, o1.y);
+    *reinterpret_cast<uint4*>(qt + qtoff + 8 * rd * R) = make_uint4(o0.x, o0.y, o1.x, o1.y);
   }
 }
 
