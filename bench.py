@@ -66,17 +66,24 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_quant_amd", "csrc")
 # (factor 0.999). Both count L2 <-> fabric transfers, so lines served by the 256 MB
 # last-level cache are included.
 MEASURED_TRAFFIC = {
-    "gemm_gu": {"sha": "0916d3ebc8347e05", "gb": 1.6391},  # read 1.2368 + write 0.4023
-    "gemm_gu_pow2": {"sha": "0916d3ebc8347e05", "gb": 1.6391},  # read 1.2368 + write 0.4023
-    "dgrad": {"sha": "0916d3ebc8347e05", "gb": 1.3204},  # read 1.2533 + write 0.0671
-    "dgrad_pow2": {"sha": "0916d3ebc8347e05", "gb": 1.3218},  # read 1.2547 + write 0.0671
-    "mx_fwd": {"sha": "0916d3ebc8347e05", "gb": 1.6487},  # read 1.2464 + write 0.4023
-    "decode_n24576": {"sha": "b2d0f8f782049ddb", "gb": 0.1223},  # read 0.1097 + write 0.0126 (the GEMM launch of the call)
-    "grouped_gu": {"sha": "0916d3ebc8347e05", "gb": 0.3149},  # read 0.2478 + write 0.0671
-    "grouped_gu_block": {"sha": "0916d3ebc8347e05", "gb": 0.3073},  # read 0.2402 + write 0.0671
-    "install_gu": {"sha": "495522813f4a7cae", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
-    "swiglu_fp8": {"sha": "f9a893244725ac88", "gb": 0.6222},  # read 0.4034 + write 0.2188
-    "requant_gu": {"sha": "4c04c29cdeacddd4", "gb": 0.6040},  # read 0.4026 + write 0.2014
+    "gemm_gu": {"sha": "d1d74be00594d11b", "gb": 1.6388},  # read 1.2365 + write 0.4024
+    "gemm_gu_pow2": {"sha": "d1d74be00594d11b", "gb": 1.6388},  # read 1.2365 + write 0.4024
+    "dgrad": {"sha": "d1d74be00594d11b", "gb": 1.3244},  # read 1.2574 + write 0.0671
+    "dgrad_pow2": {"sha": "d1d74be00594d11b", "gb": 1.3240},  # read 1.2569 + write 0.0671
+    "mx_fwd": {"sha": "d1d74be00594d11b", "gb": 1.6483},  # read 1.2460 + write 0.4024
+    "decode_n24576": {"sha": "f61860d90a3f3266", "gb": 0.1223},  # read 0.1098 + write 0.0126 (the GEMM launch of the call)
+    "grouped_gu": {"sha": "d1d74be00594d11b", "gb": 0.3147},  # read 0.2476 + write 0.0671
+    "grouped_gu_block": {"sha": "d1d74be00594d11b", "gb": 0.3079},  # read 0.2409 + write 0.0671
+    "install_gu": {"sha": "f3a49985734351c2", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
+    "swiglu_fp8": {"sha": "bd9241e977edc6dd", "gb": 0.6228},  # read 0.4035 + write 0.2193
+    "requant_gu": {"sha": "ff1a9e3db15c1481", "gb": 0.6040},  # read 0.4026 + write 0.2014
+    "quant_x": {"sha": "7c574e55d49538ad", "gb": 0.1377},  # read 0.0672 + write 0.0705
+    "quant_x_pow2": {"sha": "7c574e55d49538ad", "gb": 0.1376},  # read 0.0672 + write 0.0705
+    "quant_dy": {"sha": "7c574e55d49538ad", "gb": 0.8534},  # read 0.4026 + write 0.4507
+    "quant_dy_pow2": {"sha": "7c574e55d49538ad", "gb": 0.8531},  # read 0.4026 + write 0.4506
+    "quant_dy_mx": {"sha": "7c574e55d49538ad", "gb": 0.8523},  # read 0.4026 + write 0.4497
+    "quant_xperm_mx": {"sha": "7c574e55d49538ad", "gb": 0.2033},  # read 0.1342 + write 0.0692
+    "quant_xperm_rows": {"sha": "7c574e55d49538ad", "gb": 0.2034},  # read 0.1342 + write 0.0692
 }
 
 
@@ -100,6 +107,13 @@ KERNEL_SOURCES = {
     "install_gu": ("install.hip", "device.hpp"),
     "swiglu_fp8": ("producers.hip", "quant_kernels.hpp", "device.hpp"),
     "requant_gu": ("fp8_param.hip", "device.hpp"),
+    "quant_x": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
+    "quant_x_pow2": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
+    "quant_dy": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
+    "quant_dy_pow2": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
+    "quant_dy_mx": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
+    "quant_xperm_mx": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
+    "quant_xperm_rows": ("quant.hip", "quant_kernels.hpp", "device.hpp"),
 }
 
 
@@ -210,6 +224,7 @@ def dense_setup(torch, F, W, dev, pow2=False):
                "bf16 read 2 B + row and column E4M3 payloads 1 B each + fp32 scales per element"),
         gemm_keys=("gemm_gu", "gemm_dn"),
         traffic_key="gemm_gu_pow2" if pow2 else "gemm_gu",
+        quant_traffic_key="quant_x_pow2" if pow2 else "quant_x",
     )
     return step, timers, info
 
@@ -368,6 +383,7 @@ def backward_setup(torch, F, W, dev, pow2=False):
                "bf16 read 2 B + row and column E4M3 payloads + fp32 scales per element"),
         gemm_keys=("dgrad", "wgrad"),
         traffic_key="dgrad_pow2" if pow2 else "dgrad",
+        quant_traffic_key="quant_dy_pow2" if pow2 else "quant_dy",
     )
     return step, timers, info
 
@@ -422,6 +438,7 @@ def mx_dense_setup(torch, F, W, dev):
                "bf16 read 2 B + row and column E4M3 payloads + E8M0 scales per element"),
         gemm_keys=("fwd", "dgrad", "wgrad"),
         traffic_key="mx_fwd",
+        quant_traffic_key="quant_dy_mx",
     )
     return step, timers, info
 
@@ -505,6 +522,7 @@ def moe_setup(torch, F, W, dev):
         dominant=("grouped_gu", "mfma", fl_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
                   f"2*T*N*K = {fl_gu:.4g} FLOP per launch"),
         quant=("quant_x", T * K * (2 + 1 + 1 / 32) / 1e9, "bf16 read 2 B + E4M3 1 B + E8M0 1/32 B per element"),
+        quant_traffic_key="quant_xperm_mx",
         gemm_keys=("grouped_gu", "grouped_dn"),
         # X_perm and the expert stack once (E4M3 + E8M0) and Y once (bf16)
         algorithmic_gb=(T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + T * N * 2) / 1e9,
@@ -553,6 +571,7 @@ def moe_block128_setup(torch, F, W, dev):
         dominant=("grouped_gu", "mfma", fl_gu / 1e12, "TFLOP/s", PEAK_FP8_TFLOPS,
                   f"2*T*N*K = {fl_gu:.4g} FLOP per launch"),
         quant=("quant_x", T * K * (2 + 1 + 4 / 128) / 1e9, "bf16 read 2 B + E4M3 1 B + fp32 scale 4/128 B per element"),
+        quant_traffic_key="quant_xperm_rows",
         gemm_keys=("grouped_gu", "grouped_dn"),
         # X_perm once (E4M3 + fp32 1x128 scales), the expert stack once (E4M3 + fp32 128x128
         # block scales) and Y once (bf16)
@@ -838,8 +857,11 @@ def measure(workload, steps, warmup, no_graph, torch, F, W, dev):
     if info["quant"] is not None:
         qname, qgb, qdesc = info["quant"]
         qms = timers[qname].per_launch_ms()
+        qkey = info.get("quant_traffic_key")
+        qtraffic, qsha = _traffic(qkey) if qkey else (None, None)
         rec["quant_roofline"] = {"bound": "hbm", "kernel": qname, "achieved": round(qgb / (qms * 1e-3), 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(qgb / (qms * 1e-3) / PEAK_HBM_GBS, 4),
+                                 "traffic": qtraffic, "traffic_unit": "GB per launch (HBM)", "sources_sha": qsha,
                                  "per_launch": qdesc}
     if "algorithmic_gb" in info:
         # A GEMM whose arithmetic intensity sits below the ridge (flops per HBM byte under
