@@ -79,6 +79,48 @@ def test_quant_act_rows_and_columns(M, K, rows):
         assert q is None and s is None
 
 
+def _mixed_regimes(M, K, seed):
+    """N(0,1) rows scaled so that groups of one wave take different arithmetic: rows times
+    2^-124 (amax near 2^-122: a subnormal fp32 scale, the fp64 form), rows times 2^118 (the
+    reciprocal's low part subnormal), the rest unscaled; one column block holds N(0,1) times
+    2^-125 in every row, so that its 128x1 groups have subnormal scales too."""
+    x = _rand((M, K), seed)
+    r = np.arange(M)
+    x[r % 7 == 3] *= np.float32(2.0 ** -124)
+    x[r % 11 == 5] *= np.float32(2.0 ** 118)
+    x[:, 128:256] = _rand((M, 128), seed + 1) * np.float32(2.0 ** -125)
+    return W.bf16_round(x)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quant_act_mixed_scale_regimes(pow2):
+    """Groups of one wave with tiny, ordinary and huge amax side by side, in the row
+    kernel, the row + column tile kernel and the column-only form."""
+    x = _mixed_regimes(384, 640, 2500)
+    assert np.isfinite(x).all()
+    quant = F.fp8_quant_act_1x128_pow2 if pow2 else F.fp8_quant_act_1x128
+    rows_ref = OQ.quant_act_1x128_pow2 if pow2 else OQ.quant_act_1x128
+    cols_ref = OQ.quant_act_128x1_pow2 if pow2 else OQ.quant_act_128x1
+    rq, rs = rows_ref(x)
+    rqt, rst = cols_ref(x)
+    q, s, _, _ = quant(bf16_dev(x))
+    assert_bytes_equal(q, rq, "rows q")
+    assert_bytes_equal(s, rs, "rows s")
+    q, s, qt, st = quant(bf16_dev(x), rowwise=True, colwise=True)
+    assert_bytes_equal(q, rq, "tile q")
+    assert_bytes_equal(s, rs, "tile s")
+    assert_bytes_equal(qt, rqt, "tile qt")
+    assert_bytes_equal(st, rst, "tile st")
+
+
+def test_mxfp8_quant_mixed_scale_regimes():
+    x = _mixed_regimes(200, 512, 2600)
+    q, e = F.mxfp8_quant_1x32(bf16_dev(x))
+    rq, re = OQ.quant_mx_1x32(x)
+    assert_bytes_equal(q, rq, "q")
+    assert_bytes_equal(e, re, "e8m0")
+
+
 @pytest.mark.parametrize("N,K", [(512, 512), (384, 256), (128, 1024)])
 def test_quant_w_128x128(N, K):
     w = W.tiny_forward()["w"] if (N, K) == (512, 512) else _rand((N, K), 3000 + N, 0.02)
