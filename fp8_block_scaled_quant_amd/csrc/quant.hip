@@ -24,9 +24,9 @@ __global__ __launch_bounds__(256) void k_quant_mx_1x32(const uint16_t* __restric
   const bool valid = g < ngroups;
   uint4 a = make_uint4(0, 0, 0, 0), b = a;
   if (valid) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + g * 32 + part * 16);
-    a = src[0];
-    b = src[1];
+    const uint16_t* src = x + g * 32 + part * 16;
+    a = ntload16(src);
+    b = ntload16(src + 8);
   }
   const float amax = group_amax<2>(pk_max_u16(mag8(a), mag8(b)));
   const int e = mx_exponent(amax);

@@ -18,20 +18,28 @@
 
 namespace fp8rl {
 
-// bf16 matrix [R][C] in memory, row-major.
+// 16-byte non-temporal load (global_load_dwordx4 ... nt).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ntload16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// bf16 matrix [R][C] in memory, row-major. The quantizers read their input once, so the
+// loads are non-temporal: they do not displace lines the last-level cache holds for
+// others, such as the dirty output of the GEMM that ran before (which the loads would
+// otherwise have to evict).
 struct PlainSrc {
   typedef uint4 Raw;
   static constexpr int kLdsBytes = 0;
   const uint16_t* x;
   int64_t C;
-  __device__ __forceinline__ Raw fetch8(int64_t row, int64_t col) const {
-    return *reinterpret_cast<const uint4*>(x + row * C + col);
-  }
+  __device__ __forceinline__ Raw fetch8(int64_t row, int64_t col) const { return ntload16(x + row * C + col); }
   // Groups tile the rows exactly, so group g starts at element g * 128.
   __device__ __forceinline__ void fetch16(int64_t g, int part, Raw& a, Raw& b) const {
-    const uint4* p = reinterpret_cast<const uint4*>(x + g * 128 + part * 16);
-    a = p[0];
-    b = p[1];
+    const uint16_t* p = x + g * 128 + part * 16;
+    a = ntload16(p);
+    b = ntload16(p + 8);
   }
   __device__ __forceinline__ void prepare(void*, int, int) const {}
   __device__ __forceinline__ uint4 make(const Raw& r, const void*) const { return r; }
