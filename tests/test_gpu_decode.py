@@ -162,6 +162,19 @@ _CONFIG_SHAPES = [(1, 128), (1, 16512), (1, 32896), (1, 49280), (65, 8320), (65,
 def test_decode_every_config(M, N, K):
     """Each configuration: row-major and decode-layout weights and both forms of X give the
     same bits, and sampled 128-column blocks match the oracle."""
+    _check_layouts_and_oracle(M, N, K)
+
+
+@pytest.mark.parametrize("M,N", [(1, 384), (130, 4096)])
+@pytest.mark.parametrize("K", [8192, 8320])
+def test_decode_long_k(M, N, K):
+    """K = 8192 (64 K blocks) is the longest K range whose scales the decode kernel loads into
+    LDS before its K loop; K = 8320 (65) takes the kernel that copies the scales per K block.
+    Both weight layouts and both forms of X agree bit for bit and match the oracle."""
+    _check_layouts_and_oracle(M, N, K)
+
+
+def _check_layouts_and_oracle(M, N, K):
     x = W.normal_bf16((M, K), 1.0, 83, M * 3 + N + K)
     w = W.normal_bf16((N, K), 0.02, 84, N + K)
     wq, sw, _ = F.fp8_quant_w_128x128(bf16_dev(w))
