@@ -71,19 +71,19 @@ MEASURED_TRAFFIC = {
     "dgrad": {"sha": "d1d74be00594d11b", "gb": 1.3244},  # read 1.2574 + write 0.0671
     "dgrad_pow2": {"sha": "d1d74be00594d11b", "gb": 1.3240},  # read 1.2569 + write 0.0671
     "mx_fwd": {"sha": "d1d74be00594d11b", "gb": 1.6483},  # read 1.2460 + write 0.4024
-    "decode_n24576": {"sha": "f61860d90a3f3266", "gb": 0.1223},  # read 0.1098 + write 0.0126 (the GEMM launch of the call)
+    "decode_n24576": {"sha": "b58acf680592284a", "gb": 0.1224},  # read 0.1099 + write 0.0126 (the GEMM launch of the call)
     "grouped_gu": {"sha": "d1d74be00594d11b", "gb": 0.3147},  # read 0.2476 + write 0.0671
     "grouped_gu_block": {"sha": "d1d74be00594d11b", "gb": 0.3079},  # read 0.2409 + write 0.0671
     "install_gu": {"sha": "f3a49985734351c2", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
     "swiglu_fp8": {"sha": "bd9241e977edc6dd", "gb": 0.6228},  # read 0.4035 + write 0.2193
     "requant_gu": {"sha": "ff1a9e3db15c1481", "gb": 0.6040},  # read 0.4026 + write 0.2014
-    "quant_x": {"sha": "7c574e55d49538ad", "gb": 0.1377},  # read 0.0672 + write 0.0705
-    "quant_x_pow2": {"sha": "7c574e55d49538ad", "gb": 0.1376},  # read 0.0672 + write 0.0705
-    "quant_dy": {"sha": "7c574e55d49538ad", "gb": 0.8534},  # read 0.4026 + write 0.4507
-    "quant_dy_pow2": {"sha": "7c574e55d49538ad", "gb": 0.8531},  # read 0.4026 + write 0.4506
-    "quant_dy_mx": {"sha": "7c574e55d49538ad", "gb": 0.8523},  # read 0.4026 + write 0.4497
-    "quant_xperm_mx": {"sha": "7c574e55d49538ad", "gb": 0.2033},  # read 0.1342 + write 0.0692
-    "quant_xperm_rows": {"sha": "7c574e55d49538ad", "gb": 0.2034},  # read 0.1342 + write 0.0692
+    "quant_x": {"sha": "df969eae54a17cf5", "gb": 0.1375},  # read 0.0672 + write 0.0703
+    "quant_x_pow2": {"sha": "df969eae54a17cf5", "gb": 0.1374},  # read 0.0672 + write 0.0703
+    "quant_dy": {"sha": "df969eae54a17cf5", "gb": 0.8382},  # read 0.4026 + write 0.4356
+    "quant_dy_pow2": {"sha": "df969eae54a17cf5", "gb": 0.8387},  # read 0.4026 + write 0.4361
+    "quant_dy_mx": {"sha": "df969eae54a17cf5", "gb": 0.8399},  # read 0.4026 + write 0.4373
+    "quant_xperm_mx": {"sha": "df969eae54a17cf5", "gb": 0.2038},  # read 0.1346 + write 0.0692
+    "quant_xperm_rows": {"sha": "df969eae54a17cf5", "gb": 0.2038},  # read 0.1346 + write 0.0692
 }
 
 
