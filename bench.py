@@ -75,7 +75,7 @@ MEASURED_TRAFFIC = {
     "grouped_gu": {"sha": "d1d74be00594d11b", "gb": 0.3147},  # read 0.2476 + write 0.0671
     "grouped_gu_block": {"sha": "d1d74be00594d11b", "gb": 0.3079},  # read 0.2409 + write 0.0671
     "install_gu": {"sha": "f3a49985734351c2", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)
-    "swiglu_fp8": {"sha": "bd9241e977edc6dd", "gb": 0.6228},  # read 0.4035 + write 0.2193
+    "swiglu_fp8": {"sha": "4ad7ed3ca95264b9", "gb": 0.6228},  # read 0.4035 + write 0.2193
     "requant_gu": {"sha": "ff1a9e3db15c1481", "gb": 0.6040},  # read 0.4026 + write 0.2014
     "quant_x": {"sha": "df969eae54a17cf5", "gb": 0.1375},  # read 0.0672 + write 0.0703
     "quant_x_pow2": {"sha": "df969eae54a17cf5", "gb": 0.1374},  # read 0.0672 + write 0.0703
