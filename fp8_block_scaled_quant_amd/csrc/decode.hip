@@ -379,7 +379,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 //   into the same registers.
 // Measured against k_gemm_decode on the rollout decode shapes (M = 256, K = 4096, weights in
 // the decode layout streamed from HBM): 20% faster at N = 4096, 8% at N = 12288, 6% at
-// N = 24576.
+// N = 24576; at N = 24576 the form with two row parts per workgroup and the weights staged in
+// LDS (WL) is another 4% faster.
 constexpr int KPRE = 64;
 
 template <int OFF>
@@ -399,44 +400,59 @@ __device__ __forceinline__ void dma16s(v4i rsrc, uint32_t voff, uint32_t soff, u
                : "memory", "m0");
 }
 
-template <int MT, int NW, int FW, int P>
+// MT rows per wave, NW fragment groups of FW fragments, RP row parts per workgroup: the
+// workgroup's NW RP waves cover MTW = MT RP rows x F = NW FW fragments, wave w taking rows
+// MT (w / NW) .. + MT - 1 and fragment group w % NW. WL (decode layout only): the
+// workgroup's weight tiles are copied into the stage once and every wave reads its fragments
+// from there, instead of each wave loading its fragments into registers (with RP = 2 this
+// halves the weight bytes a CU moves).
+template <int MT, int NW, int FW, int P, int RP = 1, bool WL = false>
 struct PreShape {
-  static constexpr int NT = NW * 64;
+  static constexpr int NWT = NW * RP;                // waves per workgroup
+  static constexpr int NT = NWT * 64;
+  static constexpr int MTW = MT * RP;                // activation rows per workgroup
   static constexpr int F = NW * FW;                  // B fragments per workgroup
   static constexpr int BN = 16 * F;
-  static constexpr int XF = MT / 16;                 // A fragments
+  static constexpr int XF = MT / 16;                 // A fragments per wave
   static constexpr int NS = P + 1;                   // stages / register sets
-  static constexpr int LX = MT * 8 / NT;             // A copies (16 B per lane) per wave and K block
-  static constexpr int STAGE = MT * 128;
-  static constexpr int OFF_ZERO = NS * STAGE;        // MT * 4 zero bytes: the scales of dead K blocks
-  static constexpr int OFF_PA = OFF_ZERO + MT * 4;   // A's row scales [KPRE][MT]
-  static constexpr int OFF_PB = OFF_PA + KPRE * MT * 4;  // B's fragment scales [KPRE][64]
-  static constexpr int LDS = OFF_PB + KPRE * 256;
-  static constexpr int OPS = LX + 2 * FW;            // operations per wave and K block
-  static constexpr int SA_COPIES = MT / 64;          // 64-row scale copies per K block
-  static_assert(MT % 64 == 0 && MT <= 256 && (MT * 8) % NT == 0 && (NT / 8) % 16 == 0, "row part");
-  static_assert(F <= 64, "one B fragment scale per lane");
+  static constexpr int LX = MTW * 8 / NT;            // A copies (16 B per lane) per wave and K block
+  static constexpr int LW = WL ? 2 * F / NWT : 0;    // B copies (1 KB halves of fragment tiles) per wave
+  static constexpr int XS = MTW * 128;               // A bytes per K block
+  static constexpr int STAGE = XS + (WL ? F * 2048 : 0);
+  static constexpr int ZB = MTW * 4 > 256 ? MTW * 4 : 256;
+  static constexpr int OFF_ZERO = NS * STAGE;        // ZB zero bytes: the scales of dead K blocks
+  static constexpr int OFF_PA = OFF_ZERO + ZB;       // A's row scales [KPRE][MTW]
+  static constexpr int SBW = WL ? 16 : 64;           // B fragment scales per K block
+  static constexpr int OFF_PB = OFF_PA + KPRE * MTW * 4;  // B's fragment scales [KPRE][SBW]
+  static constexpr int LDS = OFF_PB + KPRE * SBW * 4;
+  static constexpr int OPS = LX + (WL ? LW : 2 * FW);  // operations per wave and K block
+  static constexpr int SA_COPIES = MTW / 64;         // 64-row scale copies per K block
+  static_assert(MTW % 64 == 0 && MTW <= 256 && (MTW * 8) % NT == 0 && (NT / 8) % 16 == 0, "row part");
+  static_assert(MT % 16 == 0 && F <= SBW && SA_COPIES <= NWT, "fragments");
+  static_assert(!WL || (2 * F) % NWT == 0, "B copies split evenly over the waves");
   static_assert(P >= 1 && (P - 1) * OPS <= 63, "vmcnt range");
-  static_assert(LDS <= 80 * 1024, "two workgroups per CU");
+  static_assert(LDS <= (WL ? 160 : 80) * 1024, "LDS budget (two workgroups per CU without WL)");
 };
 
-template <int MT, int NW, int FW, int P, bool kF32, bool kTiledB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_decode_pre(DecodeParams p) {
-  using S = PreShape<MT, NW, FW, P>;
-  constexpr int NT = S::NT, XF = S::XF, NS = S::NS, LX = S::LX;
+template <int MT, int NW, int FW, int P, int RP, bool WL, bool kF32, bool kTiledB>
+__global__ __launch_bounds__(NW * RP * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_decode_pre(DecodeParams p) {
+  using S = PreShape<MT, NW, FW, P, RP, WL>;
+  constexpr int NT = S::NT, XF = S::XF, NS = S::NS, LX = S::LX, MTW = S::MTW;
+  static_assert(!WL || kTiledB, "weights through LDS need the decode layout");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rp = wave / NW, wf = wave - rp * NW;     // row part, fragment group
   const int M = (int)p.M;
   const int64_t N = p.N, K = p.K;
   const int nkb = (int)(K / 128);
-  const int ms = (M + MT - 1) / MT;
+  const int ms = (M + MTW - 1) / MTW;
   const int q8 = (int)(blockIdx.x >> 3);
   const int mpart = q8 % ms, run = (q8 / ms) * 8 + (int)(blockIdx.x & 7);
   const int64_t n0 = (int64_t)run * S::BN;
-  const int m0 = mpart * MT;
+  const int m0 = mpart * MTW;
   if (n0 >= N) return;                                 // padding workgroup (uniform)
   const int64_t rows_b = (N - n0) < S::BN ? (N - n0) : S::BN;
   const int fvalid = (int)(rows_b / 16);
@@ -452,8 +468,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __syncthreads();
 
   // Scales of the whole K range: A's rows [kb][m] (one copy of 64 rows per K block and 64-row
-  // part) and B's fragment scales [kb][f] (lane f: fragment f's block scale; lanes past the last
-  // valid fragment repeat it), spread over the waves. The K loop's waits bound only the newest
+  // part) and B's fragment scales [kb][f] (lane f < SBW: fragment f's block scale; lanes past the
+  // last valid fragment repeat it), spread over the waves. The K loop's waits bound only the newest
   // operations, so these older copies are complete at its first wait.
   {
     const uint64_t sa_total = (uint64_t)M * (uint64_t)nkb * 4;
@@ -461,17 +477,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int fl = lane < fvalid ? lane : fvalid - 1;
     const uint32_t offSB = (uint32_t)(((n0 + 16 * fl) >> 7) * p.sb_ld_n * 4);
     const int nA = nkb * S::SA_COPIES, ncp = nA + nkb;
-    for (int c = wave; c < ncp; c += NW) {
+    for (int c = wave; c < ncp; c += S::NWT) {
       if (c < nA) {
         const int kb = c / S::SA_COPIES, w = c - kb * S::SA_COPIES;
         const uint64_t used = (uint64_t)((int64_t)kb * p.sa_kb) * 4;
         dma4(make_rsrc(p.sA + (int64_t)kb * p.sa_kb, rng(sa_total, used)),
-             (uint32_t)((int64_t)(m0 + w * 64 + lane) * p.sa_ld * 4), st0 + S::OFF_PA + (uint32_t)((kb * MT + w * 64) * 4));
-      } else {
+             (uint32_t)((int64_t)(m0 + w * 64 + lane) * p.sa_ld * 4), st0 + S::OFF_PA + (uint32_t)((kb * MTW + w * 64) * 4));
+      } else if (lane < S::SBW) {
         const int kb = c - nA;
         const uint64_t used = (uint64_t)((int64_t)kb * p.sb_ld_k) * 4;
         dma4(make_rsrc(p.sB + (int64_t)kb * p.sb_ld_k, rng(sb_total, used)), offSB,
-             st0 + S::OFF_PB + (uint32_t)(kb * 256));
+             st0 + S::OFF_PB + (uint32_t)(kb * S::SBW * 4));
       }
     }
   }
@@ -485,10 +501,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const v4i rB = make_rsrc(Bp, (uint32_t)(rows_b * K));
   const int lr = tid >> 3;
   const uint32_t offA = (uint32_t)((int64_t)(m0 + lr) * p.a_ld) + (uint32_t)(swz(lr, tid & 7) << 4);
-  const uint32_t offB = kTiledB ? (uint32_t)((int64_t)wave * FW * 16 * K + 16 * lane)
-                                : (uint32_t)((int64_t)(wave * FW * 16 + (lane & 15)) * K + 16 * (lane >> 4));
+  const uint32_t offB = kTiledB ? (uint32_t)((int64_t)wf * FW * 16 * K + 16 * lane)
+                                : (uint32_t)((int64_t)(wf * FW * 16 + (lane & 15)) * K + 16 * (lane >> 4));
+  // WL: copy c of wave w moves half h = w + c NWT of the workgroup's fragment tiles (fragment
+  // h / 2, bytes 1024 (h % 2) .. + 1023 of its 2 KB tile) to the same place in the stage.
+  uint32_t offW[S::LW > 0 ? S::LW : 1], ldsW[S::LW > 0 ? S::LW : 1];
+#pragma unroll
+  for (int c = 0; c < S::LW; ++c) {
+    const int h = wave + c * S::NWT;
+    offW[c] = (uint32_t)((int64_t)(h >> 1) * 16 * K) + (uint32_t)((h & 1) * 1024 + 16 * lane);
+    ldsW[c] = (uint32_t)(S::XS + (h >> 1) * 2048 + (h & 1) * 1024);
+  }
 
-  v4i wlo[NS][FW], whi[NS][FW];
+  v4i wlo[WL ? 1 : NS][FW], whi[WL ? 1 : NS][FW];
   // Operation o of K block kb into stage / register set `set`: the LX activation copies, then
   // the FW pairs of weight loads.
   auto issue_op = [&](auto oc, auto setc, int kb) __attribute__((always_inline)) {
@@ -498,6 +523,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const uint32_t soff = live ? (uint32_t)((int64_t)kb * p.a_kb) : 0u;
       dma16s(live ? rA : rZ, offA + (uint32_t)(o * (NT / 8)) * (uint32_t)p.a_ld, soff,
              st0 + set * S::STAGE + (o * NT + wave * 64) * 16);
+    } else if constexpr (WL) {
+      dma16s(live ? rB : rZ, offW[o - LX], live ? (uint32_t)kb * 2048u : 0u, st0 + set * S::STAGE + ldsW[o - LX]);
     } else {
       constexpr int i = (o - LX) / 2;
       const uint32_t soff = live ? (uint32_t)kb * (kTiledB ? 2048u : 128u) : 0u;
@@ -520,18 +547,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto step = [&](auto setc, auto nsetc, int kb) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
     const uint32_t st = st0 + set * S::STAGE;
-    const uint32_t a_lo = st + fa.lo, a_hi = st + fa.hi;
+    const uint32_t a_lo = st + (uint32_t)(rp * MT * 128) + fa.lo, a_hi = st + (uint32_t)(rp * MT * 128) + fa.hi;
     const bool live = kb < nkb;
-    const uint32_t sa_ad = st0 + (live ? S::OFF_PA + (uint32_t)(kb * MT * 4) : S::OFF_ZERO) + (uint32_t)((lane & 15) * 4);
-    const uint32_t sb_ad = st0 + (live ? S::OFF_PB + (uint32_t)(kb * 256) : S::OFF_ZERO) + (uint32_t)(wave * FW * 4);
+    const uint32_t sa_ad = st0 + (live ? S::OFF_PA + (uint32_t)(kb * MTW * 4) : S::OFF_ZERO) + (uint32_t)((rp * MT + (lane & 15)) * 4);
+    const uint32_t sb_ad = st0 + (live ? S::OFF_PB + (uint32_t)(kb * S::SBW * 4) : S::OFF_ZERO) + (uint32_t)(wf * FW * 4);
     float sb[FW];
     static_for<0, FW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       sb[i] = ds_read4f<i * 4>(sb_ad);
     });
+    v4i blo[FW], bhi[FW];                 // WL: the wave's fragment tiles from the stage
+    if constexpr (WL) {
+      const uint32_t w_ad = st + S::XS + (uint32_t)(wf * FW * 2048 + 16 * lane);
+      static_for<0, FW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        blo[i] = ds_read16<i * 2048>(w_ad);
+        bhi[i] = ds_read16<i * 2048 + 1024>(w_ad);
+      });
+    }
     // A fragment j (rows 16 j ..) and its row scales, XD fragments in flight (3 LDS reads
     // each; lgkmcnt counts up to 15).
-    constexpr int XD = (15 - FW) / 3 < XF ? (15 - FW) / 3 : XF;
+    constexpr int XD = (15 - FW - (WL ? 2 * FW : 0)) / 3 < XF ? (15 - FW - (WL ? 2 * FW : 0)) / 3 : XF;
+    static_assert(XD >= 1, "LDS read window");
     v4i xlo[XF], xhi[XF];
     float sx[XF];
     auto read_x = [&](auto jc) __attribute__((always_inline)) {
@@ -563,7 +600,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         static_for<0, FW>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
           hold(sb[i]);
-          bf[i] = join(wlo[set][i], whi[set][i]);
+          if constexpr (WL) {
+            hold(blo[i]);
+            hold(bhi[i]);
+            bf[i] = join(blo[i], bhi[i]);
+          } else {
+            bf[i] = join(wlo[set][i], whi[set][i]);
+          }
         });
       }
       const v8i xf = join(xlo[j], xhi[j]);
@@ -602,20 +645,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // write their registers when they complete. Tying every weight register to this wait keeps
     // the compiler from giving any of them to another value before then.
     wait_vmem();
-    static_for<0, NS>([&](auto sc) {
-      static_for<0, FW>([&](auto ic) {
-        hold(wlo[decltype(sc)::value][decltype(ic)::value]);
-        hold(whi[decltype(sc)::value][decltype(ic)::value]);
+    if constexpr (!WL) {
+      static_for<0, NS>([&](auto sc) {
+        static_for<0, FW>([&](auto ic) {
+          hold(wlo[decltype(sc)::value][decltype(ic)::value]);
+          hold(whi[decltype(sc)::value][decltype(ic)::value]);
+        });
       });
-    });
+    }
 
 #pragma unroll
     for (int j = 0; j < XF; ++j) {
-      const int m = m0 + 16 * j + (lane & 15);
+      const int m = m0 + MT * rp + 16 * j + (lane & 15);
       if (m >= M) continue;
 #pragma unroll
       for (int i = 0; i < FW; ++i) {
-        const int64_t n = n0 + 16 * (wave * FW + i) + 4 * (lane >> 4);
+        const int64_t n = n0 + 16 * (wf * FW + i) + 4 * (lane >> 4);
         if (n >= N) continue;
         if constexpr (kF32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n) =
@@ -675,16 +720,18 @@ static hipError_t launch_decode_cfg(const DecodeParams& p, bool f32, hipStream_t
   return hipGetLastError();
 }
 
-template <int MT, int NW, int FW, int P>
+template <int MT, int NW, int FW, int P, int RP = 1, bool WL = false>
 static hipError_t launch_decode_pre_cfg(const DecodeParams& p, bool f32, hipStream_t stream) {
-  using S = PreShape<MT, NW, FW, P>;
-  const int64_t runs = (p.N + S::BN - 1) / S::BN, ms = (p.M + MT - 1) / MT;
+  using S = PreShape<MT, NW, FW, P, RP, WL>;
+  const int64_t runs = (p.N + S::BN - 1) / S::BN, ms = (p.M + S::MTW - 1) / S::MTW;
   const int64_t blocks = (runs + 7) / 8 * 8 * ms;
   if (blocks > 0x7fffffff || p.M > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 g((unsigned)blocks), b(S::NT);
 #define FP8RL_DECODE_PRE_LAUNCH(F32, TILED) \
-  hipLaunchKernelGGL((k_gemm_decode_pre<MT, NW, FW, P, F32, TILED>), g, b, 0, stream, p)
-  if (f32) {
+  hipLaunchKernelGGL((k_gemm_decode_pre<MT, NW, FW, P, RP, WL, F32, TILED>), g, b, 0, stream, p)
+  if constexpr (WL) {
+    if (f32) FP8RL_DECODE_PRE_LAUNCH(true, true); else FP8RL_DECODE_PRE_LAUNCH(false, true);
+  } else if (f32) {
     if (p.tiled_b) FP8RL_DECODE_PRE_LAUNCH(true, true); else FP8RL_DECODE_PRE_LAUNCH(true, false);
   } else {
     if (p.tiled_b) FP8RL_DECODE_PRE_LAUNCH(false, true); else FP8RL_DECODE_PRE_LAUNCH(false, false);
@@ -724,6 +771,13 @@ static const DecodeCfg kDecodePreCfgs[] = {
 // N = 4096, FW = 3 at N = 12288 and 24576.
 hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t stream) {
   const bool pre = p.K / 128 <= KPRE && (uint64_t)p.M * (uint64_t)p.K <= 0xffffffffull;
+  if (pre && p.tiled_b) {
+    // Decode-layout weights: two row parts per workgroup sharing one LDS copy of the weights,
+    // when that grid still has a workgroup for every CU (the N = 24576 decode shape).
+    using SW = PreShape<64, 4, 3, 2, 2, true>;
+    if ((p.N + SW::BN - 1) / SW::BN * ((p.M + SW::MTW - 1) / SW::MTW) >= 256)
+      return launch_decode_pre_cfg<64, 4, 3, 2, 2, true>(p, f32, stream);
+  }
   const DecodeCfg* cfgs = pre ? kDecodePreCfgs : kDecodeCfgs;
   const int64_t ms = (p.M + 63) / 64;
   for (int i = 0; i < 3; ++i) {

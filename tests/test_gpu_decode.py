@@ -152,9 +152,12 @@ def test_decode_every_k_block(K):
 
 # Shapes that make the launch choose each configuration of the decode kernel (weight
 # fragments per wave 1, 2 and 3; row part 64), with one to three row parts (the last one
-# ragged) and grids of one to a few hundred workgroups.
+# ragged) and grids of one to a few hundred workgroups. (1, 49280), (130, 24576) and
+# (200, 36864) give the grids with a workgroup per CU for two row parts per workgroup, which
+# take the form that stages decode-layout weights in LDS (the last two with a ragged second
+# row part).
 _CONFIG_SHAPES = [(1, 128), (1, 16512), (1, 32896), (1, 49280), (65, 8320), (65, 16512), (65, 32896),
-                  (129, 11008), (129, 16512)]
+                  (129, 11008), (129, 16512), (130, 24576), (200, 36864)]
 
 
 @pytest.mark.parametrize("M,N", _CONFIG_SHAPES)
