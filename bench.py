@@ -71,7 +71,7 @@ MEASURED_TRAFFIC = {
     "dgrad": {"sha": "d1d74be00594d11b", "gb": 1.3244},  # read 1.2574 + write 0.0671
     "dgrad_pow2": {"sha": "d1d74be00594d11b", "gb": 1.3240},  # read 1.2569 + write 0.0671
     "mx_fwd": {"sha": "d1d74be00594d11b", "gb": 1.6483},  # read 1.2460 + write 0.4024
-    "decode_n24576": {"sha": "d65911dd4ae1d1e9", "gb": 0.1220},  # read 0.1094 + write 0.0126 (the GEMM launch of the call)
+    "decode_n24576": {"sha": "c2e3de9b37813cfe", "gb": 0.1221},  # read 0.1095 + write 0.0126 (the GEMM launch of the call)
     "grouped_gu": {"sha": "d1d74be00594d11b", "gb": 0.3147},  # read 0.2476 + write 0.0671
     "grouped_gu_block": {"sha": "d1d74be00594d11b", "gb": 0.3079},  # read 0.2409 + write 0.0671
     "install_gu": {"sha": "f3a49985734351c2", "gb": 0.2014},  # read 0.1007 + write 0.1007 (calibration copy)

@@ -380,7 +380,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // Measured against k_gemm_decode on the rollout decode shapes (M = 256, K = 4096, weights in
 // the decode layout streamed from HBM): 20% faster at N = 4096, 8% at N = 12288, 6% at
 // N = 24576; at N = 24576 the form with two row parts per workgroup and the weights staged in
-// LDS (WL) is another 4% (back-to-back launches) to 10% (kernel trace) faster.
+// LDS (WL) is another 4% (back-to-back launches) to 10% (kernel trace) faster. With the
+// copies moved to two copy waves (NP = 2), which leaves the compute waves nothing to issue
+// but LDS reads and MFMAs, the decode-layout launches were faster again, in three interleaved
+// rounds of back-to-back launches: N = 4096 (one row part, FW = 1) 5% with the weights in
+// the last-level cache and 1.5% streamed from HBM, N = 12288 (one row part, FW = 3) 10% and
+// 4%, N = 24576 (two row parts) 6% and 3%; four copy waves were no faster than two.
 constexpr int KPRE = 64;
 
 template <int OFF>
@@ -405,11 +410,15 @@ __device__ __forceinline__ void dma16s(v4i rsrc, uint32_t voff, uint32_t soff, u
 // MT (w / NW) .. + MT - 1 and fragment group w % NW. WL (decode layout only): the
 // workgroup's weight tiles are copied into the stage once and every wave reads its fragments
 // from there, instead of each wave loading its fragments into registers (with RP = 2 this
-// halves the weight bytes a CU moves).
-template <int MT, int NW, int FW, int P, int RP = 1, bool WL = false>
+// halves the weight bytes a CU moves). NP > 0 (with WL): NP further copy waves issue every
+// copy of the stage and the NW RP compute waves issue none, so that no compute wave stalls
+// on the texture unit's queue between its MFMAs.
+template <int MT, int NW, int FW, int P, int RP = 1, bool WL = false, int NP = 0>
 struct PreShape {
-  static constexpr int NWT = NW * RP;                // waves per workgroup
+  static constexpr int NWT = NW * RP;                // compute waves per workgroup
   static constexpr int NT = NWT * 64;
+  static constexpr int NPT = NP * 64;                // copy-wave threads
+  static constexpr int NTA = NT + NPT;
   static constexpr int MTW = MT * RP;                // activation rows per workgroup
   static constexpr int F = NW * FW;                  // B fragments per workgroup
   static constexpr int BN = 16 * F;
@@ -425,18 +434,22 @@ struct PreShape {
   static constexpr int SBW = WL ? 16 : 64;           // B fragment scales per K block
   static constexpr int OFF_PB = OFF_PA + KPRE * MTW * 4;  // B's fragment scales [KPRE][SBW]
   static constexpr int LDS = OFF_PB + KPRE * SBW * 4;
-  static constexpr int OPS = LX + (WL ? LW : 2 * FW);  // operations per wave and K block
+  static constexpr int OPS = NP ? 0 : LX + (WL ? LW : 2 * FW);  // operations per compute wave and K block
+  static constexpr int LXP = NP ? MTW * 8 / (NP * 64) : 0;   // A copies per copy wave and K block
+  static constexpr int LWP = NP ? 2 * F / NP : 0;            // B copies per copy wave and K block
+  static constexpr int OPSP = LXP + LWP;
   static constexpr int SA_COPIES = MTW / 64;         // 64-row scale copies per K block
   static_assert(MTW % 64 == 0 && MTW <= 256 && (MTW * 8) % NT == 0 && (NT / 8) % 16 == 0, "row part");
   static_assert(MT % 16 == 0 && F <= SBW && SA_COPIES <= NWT, "fragments");
   static_assert(!WL || (2 * F) % NWT == 0, "B copies split evenly over the waves");
-  static_assert(P >= 1 && (P - 1) * OPS <= 63, "vmcnt range");
+  static_assert(P >= 1 && (P - 1) * OPS <= 63 && (P - 1) * OPSP <= 63, "vmcnt range");
+  static_assert(NP == 0 || (WL && NP % 2 == 0 && (MTW * 8) % NPT == 0 && (2 * F) % NP == 0), "copy waves");
   static_assert(LDS <= (WL ? 160 : 80) * 1024, "LDS budget (two workgroups per CU without WL)");
 };
 
-template <int MT, int NW, int FW, int P, int RP, bool WL, bool kF32, bool kTiledB>
-__global__ __launch_bounds__(NW * RP * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_decode_pre(DecodeParams p) {
-  using S = PreShape<MT, NW, FW, P, RP, WL>;
+template <int MT, int NW, int FW, int P, int RP, bool WL, int NP, bool kF32, bool kTiledB>
+__global__ __launch_bounds__((NW * RP + NP) * 64) __attribute__((amdgpu_waves_per_eu(NP ? 3 : 2))) void k_gemm_decode_pre(DecodeParams p) {
+  using S = PreShape<MT, NW, FW, P, RP, WL, NP>;
   constexpr int NT = S::NT, XF = S::XF, NS = S::NS, LX = S::LX, MTW = S::MTW;
   static_assert(!WL || kTiledB, "weights through LDS need the decode layout");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
@@ -464,7 +477,7 @@ __global__ __launch_bounds__(NW * RP * 64) __attribute__((amdgpu_waves_per_eu(2)
   };
 
   // Zero the stages and the dead-block scale slot before any copy writes LDS.
-  for (int o = tid * 16; o < S::OFF_PA; o += NT * 16) *reinterpret_cast<uint4*>(smem + o) = make_uint4(0, 0, 0, 0);
+  for (int o = tid * 16; o < S::OFF_PA; o += S::NTA * 16) *reinterpret_cast<uint4*>(smem + o) = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   // Scales of the whole K range: A's rows [kb][m] (one copy of 64 rows per K block and 64-row
@@ -477,7 +490,7 @@ __global__ __launch_bounds__(NW * RP * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int fl = lane < fvalid ? lane : fvalid - 1;
     const uint32_t offSB = (uint32_t)(((n0 + 16 * fl) >> 7) * p.sb_ld_n * 4);
     const int nA = nkb * S::SA_COPIES, ncp = nA + nkb;
-    for (int c = wave; c < ncp; c += S::NWT) {
+    for (int c = wave; c < ncp; c += S::NWT + NP) {
       if (c < nA) {
         const int kb = c / S::SA_COPIES, w = c - kb * S::SA_COPIES;
         const uint64_t used = (uint64_t)((int64_t)kb * p.sa_kb) * 4;
@@ -511,6 +524,49 @@ __global__ __launch_bounds__(NW * RP * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int h = wave + c * S::NWT;
     offW[c] = (uint32_t)((int64_t)(h >> 1) * 16 * K) + (uint32_t)((h & 1) * 1024 + 16 * lane);
     ldsW[c] = (uint32_t)(S::XS + (h >> 1) * 2048 + (h & 1) * 1024);
+  }
+
+  // Copy waves: copy c of copy wave w moves A copies as the compute waves' copies do, with the
+  // NP copy waves' threads in place of the compute threads, and B halves h = w + c NP. Each
+  // K step: wait for this wave's copies of the current K block, meet the compute waves at the
+  // barrier, issue the copies of K block kb + P into the stage refilled next. Same barriers and
+  // stage protocol as the compute waves, which issue no copies.
+  if constexpr (NP > 0) {
+    if (wave >= S::NWT) {
+      const int pt = tid - NT, pw = wave - S::NWT, plr = pt >> 3;
+      const uint32_t poffA = (uint32_t)((int64_t)(m0 + plr) * p.a_ld) + (uint32_t)(swz(plr, pt & 7) << 4);
+      uint32_t poffW[S::LWP], pldsW[S::LWP];
+#pragma unroll
+      for (int c = 0; c < S::LWP; ++c) {
+        const int h = pw + c * NP;
+        poffW[c] = (uint32_t)((int64_t)(h >> 1) * 16 * K) + (uint32_t)((h & 1) * 1024 + 16 * lane);
+        pldsW[c] = (uint32_t)(S::XS + (h >> 1) * 2048 + (h & 1) * 1024);
+      }
+      auto pissue = [&](auto oc, auto setc, int kb) __attribute__((always_inline)) {
+        constexpr int o = decltype(oc)::value, set = decltype(setc)::value;
+        const bool live = kb < nkb;
+        if constexpr (o < S::LXP) {
+          const uint32_t soff = live ? (uint32_t)((int64_t)kb * p.a_kb) : 0u;
+          dma16s(live ? rA : rZ, poffA + (uint32_t)(o * (S::NPT / 8)) * (uint32_t)p.a_ld, soff,
+                 st0 + set * S::STAGE + (o * S::NPT + pw * 64) * 16);
+        } else {
+          dma16s(live ? rB : rZ, poffW[o - S::LXP], live ? (uint32_t)kb * 2048u : 0u, st0 + set * S::STAGE + pldsW[o - S::LXP]);
+        }
+      };
+      static_for<0, P>([&](auto sc) {
+        static_for<0, S::OPSP>([&](auto oc) { pissue(oc, sc, decltype(sc)::value); });
+      });
+      for (int kb0 = 0; kb0 < nkb; kb0 += NS) {
+        static_for<0, NS>([&](auto sc) {
+          constexpr int c = decltype(sc)::value;
+          wait_vmem_n<(P - 1) * S::OPSP>();
+          barrier_only();
+          static_for<0, S::OPSP>([&](auto oc) { pissue(oc, std::integral_constant<int, (c + P) % NS>{}, kb0 + c + P); });
+        });
+      }
+      wait_vmem();                                   // no LDS write outlives the workgroup
+      return;
+    }
   }
 
   v4i wlo[WL ? 1 : NS][FW], whi[WL ? 1 : NS][FW];
@@ -720,15 +776,15 @@ static hipError_t launch_decode_cfg(const DecodeParams& p, bool f32, hipStream_t
   return hipGetLastError();
 }
 
-template <int MT, int NW, int FW, int P, int RP = 1, bool WL = false>
+template <int MT, int NW, int FW, int P, int RP = 1, bool WL = false, int NP = 0>
 static hipError_t launch_decode_pre_cfg(const DecodeParams& p, bool f32, hipStream_t stream) {
-  using S = PreShape<MT, NW, FW, P, RP, WL>;
+  using S = PreShape<MT, NW, FW, P, RP, WL, NP>;
   const int64_t runs = (p.N + S::BN - 1) / S::BN, ms = (p.M + S::MTW - 1) / S::MTW;
   const int64_t blocks = (runs + 7) / 8 * 8 * ms;
   if (blocks > 0x7fffffff || p.M > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 g((unsigned)blocks), b(S::NT);
+  const dim3 g((unsigned)blocks), b(S::NTA);
 #define FP8RL_DECODE_PRE_LAUNCH(F32, TILED) \
-  hipLaunchKernelGGL((k_gemm_decode_pre<MT, NW, FW, P, RP, WL, F32, TILED>), g, b, 0, stream, p)
+  hipLaunchKernelGGL((k_gemm_decode_pre<MT, NW, FW, P, RP, WL, NP, F32, TILED>), g, b, 0, stream, p)
   if constexpr (WL) {
     if (f32) FP8RL_DECODE_PRE_LAUNCH(true, true); else FP8RL_DECODE_PRE_LAUNCH(false, true);
   } else if (f32) {
@@ -746,21 +802,25 @@ static hipError_t launch_decode_pre_cfg(const DecodeParams& p, bool f32, hipStre
 // k_gemm_decode (P = 3, 2, 2) a row part of 128, four fragments per wave or deeper prefetch
 // were slower or equal, and with more than three fragments per wave (or 128 rows and three)
 // the kernel no longer fits in 256 VGPRs; for k_gemm_decode_pre P = 3, 3, 2, and two K blocks
-// per barrier were no faster. Each configuration fits two workgroups per CU (registers and
-// LDS).
+// per barrier were no faster. Each register-weight configuration fits two workgroups per CU
+// (registers and LDS); the staged forms (decode-layout weights copied into LDS by two copy
+// waves) fit one, so they are used only where the grid is at most one workgroup per CU. For
+// FW = 2 the staged form was slower (its grid starts at 256 workgroups).
+using DecodeLaunch = hipError_t (*)(const DecodeParams&, bool, hipStream_t);
 struct DecodeCfg {
   int fw;
-  hipError_t (*launch)(const DecodeParams&, bool, hipStream_t);
+  DecodeLaunch launch;
+  DecodeLaunch staged;   // decode-layout weights through LDS, or null
 };
 static const DecodeCfg kDecodeCfgs[] = {
-    {3, launch_decode_cfg<64, 4, 3, 2>},
-    {2, launch_decode_cfg<64, 4, 2, 2>},
-    {1, launch_decode_cfg<64, 4, 1, 3>},
+    {3, launch_decode_cfg<64, 4, 3, 2>, nullptr},
+    {2, launch_decode_cfg<64, 4, 2, 2>, nullptr},
+    {1, launch_decode_cfg<64, 4, 1, 3>, nullptr},
 };
 static const DecodeCfg kDecodePreCfgs[] = {
-    {3, launch_decode_pre_cfg<64, 4, 3, 2>},
-    {2, launch_decode_pre_cfg<64, 4, 2, 3>},
-    {1, launch_decode_pre_cfg<64, 4, 1, 3>},
+    {3, launch_decode_pre_cfg<64, 4, 3, 2>, launch_decode_pre_cfg<64, 4, 3, 2, 1, true, 2>},
+    {2, launch_decode_pre_cfg<64, 4, 2, 3>, nullptr},
+    {1, launch_decode_pre_cfg<64, 4, 1, 3>, launch_decode_pre_cfg<64, 4, 1, 3, 1, true, 2>},
 };
 
 // Kernel: k_gemm_decode_pre when its scale tables hold the K range (K / 128 <= KPRE) and the
@@ -773,17 +833,19 @@ hipError_t launch_gemm_decode(const DecodeParams& p, bool f32, hipStream_t strea
   const bool pre = p.K / 128 <= KPRE && (uint64_t)p.M * (uint64_t)p.K <= 0xffffffffull;
   if (pre && p.tiled_b) {
     // Decode-layout weights: two row parts per workgroup sharing one LDS copy of the weights,
-    // when that grid still has a workgroup for every CU (the N = 24576 decode shape).
-    using SW = PreShape<64, 4, 3, 2, 2, true>;
+    // when that grid still has a workgroup for every CU (the N = 24576 decode shape); else one
+    // row part, as below.
+    using SW = PreShape<64, 4, 3, 2, 2, true, 2>;
     if ((p.N + SW::BN - 1) / SW::BN * ((p.M + SW::MTW - 1) / SW::MTW) >= 256)
-      return launch_decode_pre_cfg<64, 4, 3, 2, 2, true>(p, f32, stream);
+      return launch_decode_pre_cfg<64, 4, 3, 2, 2, true, 2>(p, f32, stream);
   }
   const DecodeCfg* cfgs = pre ? kDecodePreCfgs : kDecodeCfgs;
   const int64_t ms = (p.M + 63) / 64;
   for (int i = 0; i < 3; ++i) {
     const DecodeCfg& c = cfgs[i];
     const int64_t runs = (p.N + 64 * c.fw - 1) / (64 * c.fw);
-    if (ms * runs >= 256 || c.fw == 1) return c.launch(p, f32, stream);
+    if (ms * runs >= 256 || c.fw == 1)
+      return (p.tiled_b && c.staged && ms * runs <= 256 ? c.staged : c.launch)(p, f32, stream);
   }
   return hipErrorInvalidValue;   // not reached: the last configuration always applies
 }

@@ -69,7 +69,7 @@ def test_quantizers_guarded(M, K):
     g.check(f"quantizers M={M} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (17, 384, 640), (300, 384, 640), (520, 1024, 256), (130, 24576, 256)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (17, 384, 640), (300, 384, 640), (520, 1024, 256), (130, 24576, 256), (65, 24576, 256)])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_gemms_guarded(M, N, K, dt):
     g = Guarded(M * 7 + N + K)

@@ -155,9 +155,11 @@ def test_decode_every_k_block(K):
 # ragged) and grids of one to a few hundred workgroups. (1, 49280), (130, 24576) and
 # (200, 36864) give the grids with a workgroup per CU for two row parts per workgroup, which
 # take the form that stages decode-layout weights in LDS (the last two with a ragged second
-# row part).
+# row part). (65, 24576) and (256, 12288) give three-fragment grids of exactly one workgroup per
+# CU, which take the staged form with one row part; one-fragment grids of at most 256
+# workgroups take it too.
 _CONFIG_SHAPES = [(1, 128), (1, 16512), (1, 32896), (1, 49280), (65, 8320), (65, 16512), (65, 32896),
-                  (129, 11008), (129, 16512), (130, 24576), (200, 36864)]
+                  (65, 24576), (129, 11008), (129, 16512), (130, 24576), (200, 36864), (256, 12288)]
 
 
 @pytest.mark.parametrize("M,N", _CONFIG_SHAPES)
